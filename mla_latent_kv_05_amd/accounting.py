@@ -1,0 +1,87 @@
+"""Byte and FLOP accounting of one absorbed-MLA decode step.
+
+The per-token figures follow "DeepSeek-MLA-Principle", section 3 ("does
+down/up-projection save memory/compute"): the cache holds d_c + d_h^R values
+per token, the history-dependent work is 2*L*n_h*d_c + L*n_h*d_h^R
+multiplications, and a step reads L*(d_c + d_h^R)*bytes of cache.  Everything
+here is plain counting; no attention arithmetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+FORMAT_BYTES = {"f32": 4, "bf16": 2, "fp16": 2}
+
+
+def cache_values_per_token(d_c: int, d_r: int) -> int:
+    """Values cached per token: the latent plus the shared RoPE key."""
+    return d_c + d_r
+
+
+def mha_values_per_token(n_h: int, d_h: int) -> int:
+    """Values a standard MHA cache holds per token (K and V of every head)."""
+    return 2 * n_h * d_h
+
+
+def cache_bytes_per_token(d_c: int, d_r: int, fmt: str) -> int:
+    """Bytes read per cached token.  'fp8': e4m3 latent + one fp32 scale + bf16 RoPE key."""
+    if fmt == "fp8":
+        return d_c + 4 + 2 * d_r
+    return FORMAT_BYTES[fmt] * (d_c + d_r)
+
+
+def history_multiplications(L: int, n_h: int, d_c: int, d_r: int) -> int:
+    """Multiplications that grow with the history length in one absorbed decode step
+    (content logits + latent weighted sum + RoPE logits)."""
+    return 2 * L * n_h * d_c + L * n_h * d_r
+
+
+def mha_history_multiplications(L: int, n_h: int, d_h: int) -> int:
+    return 2 * L * n_h * d_h
+
+
+def visible_positions(seq_lens, Sq: int) -> int:
+    """Sum over sequences and query rows of the positions each row attends to."""
+    tot = 0
+    for n in seq_lens:
+        n = int(n)
+        for s in range(Sq):
+            tot += max(0, n - Sq + 1 + s)
+    return tot
+
+
+@dataclasses.dataclass
+class StepCost:
+    cache_bytes: int      # latent cache + RoPE keys (+ fp8 scales) of every token read
+    weight_bytes: int     # W_UK + W_UV
+    query_bytes: int      # q_nope + q_rope
+    out_bytes: int        # final per-head output
+    flops: int            # 2 * multiply-adds of the four steps
+    decode_bytes: int     # algorithmic bytes of the split-KV attention kernel alone
+    decode_flops: int
+
+    @property
+    def total_bytes(self) -> int:
+        return self.cache_bytes + self.weight_bytes + self.query_bytes + self.out_bytes
+
+
+def step_cost(B: int, Sq: int, H: int, d_h: int, d_c: int, d_r: int, seq_lens,
+              fmt: str = "bf16", out_fmt: str = "f32") -> StepCost:
+    """Algorithmic bytes/FLOP of absorb + attend + merge + up-projection.
+
+    Intermediates (absorbed query, split partials, merged latent) are excluded:
+    a fully fused design never writes them."""
+    elem = 4 if fmt == "f32" else 2
+    tokens = sum(int(n) for n in seq_lens)
+    cache = tokens * cache_bytes_per_token(d_c, d_r, fmt)
+    weights = 2 * H * d_h * d_c * elem
+    rows = B * Sq * H
+    query = rows * (d_h + d_r) * elem
+    out = rows * d_h * FORMAT_BYTES[out_fmt]
+    vis = visible_positions(seq_lens, Sq)
+    attend_flops = 2 * H * (d_c + d_r + d_c) * vis
+    proj_flops = 2 * 2 * rows * d_h * d_c
+    lat_elem = 4 if fmt == "f32" else 2
+    decode_bytes = cache + rows * (d_c + d_r) * lat_elem
+    return StepCost(cache, weights, query, out, attend_flops + proj_flops,
+                    decode_bytes, attend_flops)
