@@ -1,0 +1,198 @@
+"""Benchmark of one absorbed-MLA decode step on one MI355X.
+
+A step = mla_absorb_q + mla_decode_splitkv + mla_combine_lse + mla_up_v over
+the whole batch (one layer), on synthetic seeded inputs already resident in
+HBM.  Default workload: B=64 sequences, lengths uniform in [1024, 8192],
+DeepSeek-V3 head shapes (H=128, d_h=128, d_c=512, d_r=64), bf16, pages of 64
+tokens in a randomly permuted block table, Sq=1.
+
+The inputs are replicated R times in HBM and the steps rotate over the
+replicas, so the 256 MB last-level cache cannot serve one step from the
+previous one.
+
+Prints one JSON line.  value = latent-cache TB/s = (tokens x 1152 B) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_b64")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a device copy of this size (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_05_amd import accounting as A
+    from mla_latent_kv_05_amd import inputs as I
+    from mla_latent_kv_05_amd import mla
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    wl = I.workload(args.workload)
+    case = I.make_case(wl)
+    lens = case.seq_lens.tolist()
+    fl = mla.F32 if wl.dtype == "f32" else mla.BF16
+    kv = mla.FP8_E4M3 if wl.dtype == "fp8" else fl
+    p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, case.num_pages, case.max_pages,
+                        scale=wl.scale, q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl,
+                        latent_dtype=fl, out_dtype=mla.F32)
+    p = mla.plan_splits(p, max(lens), case.total_tokens, num_cus=props.multi_processor_count,
+                        min_splits=wl.min_splits)
+
+    names = ("q_nope", "q_rope", "c_kv", "k_pe", "kv_scale", "block_table", "seq_lens", "W_UK", "W_UV")
+    base = {k: (None if getattr(case, k) is None else getattr(case, k).to(dev)) for k in names}
+    reps = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
+                     for _ in range(args.replicas - 1)]
+    step = mla.DecodeStep(p, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(r, ev=None):
+        t = reps[r]
+        mla.absorb_q(p, t["q_nope"], t["W_UK"], step.q_abs)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode_splitkv(p, step.q_abs, t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"],
+                           t["block_table"], t["seq_lens"], step.o_part, step.lse_part)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.combine_lse(p, step.o_part, step.lse_part, step.o_latent, step.lse)
+        mla.up_v(p, step.o_latent, t["W_UV"], step.out)
+
+    for i in range(args.warmup):
+        run(i % args.replicas)
+    torch.cuda.synchronize()
+    assert torch.isfinite(step.out).all(), "non-finite output"
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        run(i % args.replicas, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    cost = A.step_cost(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, lens, fmt=wl.dtype, out_fmt="f32")
+    tb_s = cost.cache_bytes / (ms_step * 1e-3) / 1e12
+    achieved_gbs = cost.decode_bytes / (dec_avg_ms * 1e-3) / 1e9
+    roofline_us = max(cost.total_bytes / (HBM_PEAK_GBS * 1e9), cost.flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_budget_s)
+
+    result = {
+        "metric": "MLA absorbed decode µs/step + latent-cache TB/s at B=64, L=4096, bf16",
+        "value": round(tb_s, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype != "f32" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"absorbed MLA decode, B={wl.B}, Sq={wl.Sq}, H={wl.H}, d_h={wl.d_h}, "
+                        f"d_c={wl.d_c}, d_r={wl.d_r}, seq_lens U[{wl.seq_lo},{wl.seq_hi}] "
+                        f"(sum {case.total_tokens}), page 64, permuted pages, {wl.dtype} cache",
+            "name": wl.name, "B": wl.B, "Sq": wl.Sq, "tokens": case.total_tokens,
+            "num_splits": p.num_splits, "split_pages": p.split_pages,
+            "decode_kernel": mla.decode_kernel_name(p), "replicas": args.replicas,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mla_decode_splitkv",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": round(dec_avg_ms * 1e3, 2),
+            "bytes_per_launch": cost.decode_bytes,
+            "mfma_tflops": round(cost.decode_flops / (dec_avg_ms * 1e-3) / 1e12, 1),
+        },
+        "step_roofline": {"bytes": cost.total_bytes, "flops": cost.flops, "t_roof_us": round(roofline_us, 2),
+                          "frac": round(roofline_us / (ms_step * 1e3), 4)},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, budget_s):
+    """The oracle, untuned, on a bounded sample: whole sequences (every head) until
+    about `budget_s` seconds of CPU work; reported in the metric's unit."""
+    import numpy as np
+    from oracle import oracle as O
+
+    wl = case.wl
+    lens = case.seq_lens.numpy()
+    order = np.argsort(lens)[len(lens) // 2:]          # median-length and longer first
+    t_used, toks, seqs = 0.0, 0, []
+    for b in order:
+        rows = np.arange(b * wl.Sq * wl.H, (b + 1) * wl.Sq * wl.H, dtype=np.int64)
+        t0 = time.perf_counter()
+        O.decode(case, rows=rows)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        toks += int(lens[b])
+        seqs.append(int(b))
+        if t_used + dt > budget_s:
+            break
+    value = toks * 1152 / t_used / 1e12
+    return {"value": value, "unit": "TB/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{len(seqs)} whole sequences ({toks} tokens, all {wl.H} heads) of the "
+                      f"same workload, fp64 oracle, {t_used:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

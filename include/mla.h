@@ -1,0 +1,207 @@
+/*
+ * mla.h -- C ABI of libmla.so: weight-absorbed Multi-Head Latent Attention
+ * (MLA) decode over a paged latent KV cache, hand-written HIP kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode step is four stream-ordered calls:
+ *
+ *   mla_absorb_q        q_abs  = q_nope . W_UK            (key absorption)
+ *   mla_decode_splitkv  per split c: scores, softmax, latent sum -> (O_c, lse_c)
+ *   mla_combine_lse     log-sum-exp merge of the splits   -> o_latent (+ lse)
+ *   mla_up_v            out    = o_latent . W_UV^T        (value up-projection)
+ *
+ * Sources ("the pages"): "MLA 矩阵吸收 & 吸收分离 原理详解" (MLA Matrix
+ * Absorption), sections 2.1, 4.1, 4.2; "DeepSeek-MLA-Principle", section 2
+ * (score scale, softmax, eq. (10)) and section 3, matrix absorption 3) (key
+ * absorption and value absorption) and "does down/up-projection save..." 3.
+ * (FlashMLA: no K/V materialisation, tiling with online softmax and split-KV,
+ * paged cache with a block table); "DeepSeek MLA 架构详解" section 3 and its
+ * PyTorch decode module (tensor layouts [n_heads, d_head, d_latent]).
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, contiguous, in DEVICE memory owned by the
+ *     caller.  The library never allocates, frees or synchronises; it only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns an error status and launches nothing.  A launch
+ *     failure returns MLA_ERR_HIP.  mla_last_error() gives a message for the
+ *     calling thread's most recent failure.
+ *   - Contents of seq_lens and block_table are NOT checked (they live on the
+ *     device): every referenced page id must lie in [0, num_pages) and
+ *     0 <= seq_lens[b] <= max_pages * page_size.  Violations are undefined.
+ *   - Calls on different streams share no state and may run concurrently.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_F32 = 0,
+    MLA_BF16 = 1,
+    MLA_FP8_E4M3 = 2   /* OCP E4M3 (bias 7, max 448, no infinities); c_kv only */
+} mla_dtype_t;
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MLA_ERR_SHAPE = 2,       /* a dimension is out of range */
+    MLA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
+    MLA_ERR_SPLITS = 4,      /* num_splits * split_pages cannot cover max_pages */
+    MLA_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+    MLA_ERR_UNSUPPORTED = 6  /* a valid request no kernel here implements */
+} mla_status_t;
+
+/* Flags (mla_params_t.flags). */
+#define MLA_FLAG_GENERIC 1u  /* use the fp32 VALU kernels even where MFMA kernels apply */
+
+/*
+ * Problem description shared by the four calls.
+ *
+ *   B           sequences in the batch                          >= 1
+ *   Sq          new query tokens per sequence (causal among them) 1..16
+ *   H           attention heads n_h (DeepSeek-V3: 128)           >= 1
+ *   d_h         per-head non-RoPE query/key dim = value dim (128)  1..256
+ *   d_c         latent dim kv_lora_rank (512)                    1..1024
+ *   d_r         decoupled RoPE dim d_h^R (64)                    0..256
+ *   page_size   tokens per cache page; must be 64
+ *   num_pages   physical pages in c_kv / k_pe / kv_scale          >= 1
+ *   max_pages   row stride of block_table                         >= 1
+ *   num_splits  S: split slots per sequence (stride of o_part / lse_part) >= 1
+ *   split_pages pages per split; split c of sequence b covers its pages
+ *               [c*split_pages, (c+1)*split_pages).  Requires
+ *               num_splits * split_pages >= max_pages.
+ *   scale       softmax scale, 1/sqrt(d_h + d_r) ("DeepSeek-MLA-Principle"
+ *               sec. 2; the decode module's self.scale)
+ *   q_dtype     q_nope, q_rope            F32 | BF16
+ *   w_dtype     W_UK, W_UV                F32 | BF16
+ *   kv_dtype    c_kv                      F32 | BF16 | FP8_E4M3
+ *   pe_dtype    k_pe                      F32 | BF16
+ *   latent_dtype q_abs and o_latent       F32 | BF16
+ *   out_dtype   out                       F32 | BF16
+ *   flags       MLA_FLAG_* bits
+ */
+typedef struct {
+    int32_t B, Sq, H, d_h, d_c, d_r;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages;
+    int32_t num_splits;
+    int32_t split_pages;
+    float scale;
+    int32_t q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype;
+    uint32_t flags;
+} mla_params_t;
+
+/*
+ * mla_absorb_q -- key absorption ("DeepSeek-MLA-Principle", matrix absorption
+ * 3) (1); "MLA Matrix Absorption" sec. 2.1, Q' = Q x W_UK^T):
+ *
+ *   q_abs[b,s,h,m] = sum_{d < d_h} q_nope[b,s,h,d] * W_UK[h,d,m]
+ *
+ *   q_nope [B,Sq,H,d_h]  q_dtype       (in)
+ *   W_UK   [H,d_h,d_c]   w_dtype       (in)
+ *   q_abs  [B,Sq,H,d_c]  latent_dtype  (out)
+ * Accumulates in fp32; rounds once to latent_dtype.
+ */
+mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void *W_UK,
+                          void *q_abs, void *stream);
+
+/*
+ * mla_decode_splitkv -- attention over the paged latent cache, one partial
+ * per split ("MLA Matrix Absorption" sec. 4.1-4.2: score = Q'_nope c^T +
+ * Q_rope k_pe^T; "DeepSeek-MLA-Principle" sec. 2 scale and softmax, value
+ * absorption m = sum alpha c; FlashMLA's tiling / online softmax / split-KV /
+ * paged cache).  For row (b,s,h) and split c, with
+ *   n = seq_lens[b] - Sq + 1 + s          (causal: position t visible iff t < n)
+ *   T = positions t < n on the sequence's pages [c*split_pages, (c+1)*split_pages)
+ *   z_t = scale * (q_abs[b,s,h,:] . C_t + q_rope[b,s,h,:] . k_pe_t)
+ * where token t lives at page block_table[b, t/64], slot t%64, and
+ * C_t = c_kv row (fp8: decoded code * kv_scale of that token):
+ *   lse_part[b,s,h,c]  = ln sum_{t in T} exp(z_t)          (-inf if T empty)
+ *   o_part[b,s,h,c,:]  = sum_{t in T} exp(z_t - lse) C_t   (normalised; left
+ *                        unwritten when T is empty)
+ *
+ *   q_abs     [B,Sq,H,d_c]          latent_dtype (in)
+ *   q_rope    [B,Sq,H,d_r]          q_dtype      (in)
+ *   c_kv      [num_pages,64,d_c]    kv_dtype     (in)
+ *   k_pe      [num_pages,64,d_r]    pe_dtype     (in, already rotated)
+ *   kv_scale  [num_pages,64] fp32   (in; required iff kv_dtype == FP8_E4M3, else ignored)
+ *   block_table [B,max_pages] int32 (in; entries past a sequence's last page unread)
+ *   seq_lens  [B] int32             (in; tokens per sequence incl. the Sq new ones)
+ *   o_part    [B,Sq,H,num_splits,d_c] fp32 (out)
+ *   lse_part  [B,Sq,H,num_splits]     fp32 (out)
+ * Cache slots at or beyond seq_lens[b] in a sequence's last page are read but
+ * contribute exactly zero, whatever they hold (non-finite values included).
+ */
+mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const void *q_rope,
+                                const void *c_kv, const void *k_pe, const float *kv_scale,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                float *o_part, float *lse_part, void *stream);
+
+/*
+ * mla_combine_lse -- log-sum-exp merge of split partials (the merge that
+ * split-KV implies; the pages only name split-KV):
+ *   M = max_c lse_c,  lse = M + ln sum_c exp(lse_c - M),
+ *   o_latent = sum_c exp(lse_c - lse) * o_part_c
+ * Splits with lse_c = -inf carry no weight and their o_part is not read.  A
+ * row whose splits are all empty gets o_latent = 0 and lse = -inf.
+ *
+ *   o_part   [B,Sq,H,num_splits,d_c] fp32 (in)
+ *   lse_part [B,Sq,H,num_splits]     fp32 (in)
+ *   o_latent [B,Sq,H,d_c]  latent_dtype  (out)
+ *   lse_out  [B,Sq,H] fp32 (out; may be NULL)
+ */
+mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const float *lse_part,
+                             void *o_latent, float *lse_out, void *stream);
+
+/*
+ * mla_up_v -- value up-projection after the latent-space sum
+ * ("DeepSeek-MLA-Principle", matrix absorption 3) (2): o = W_i^UV m;
+ * "MLA Matrix Absorption" sec. 2.1, O = O' x W_UV):
+ *
+ *   out[b,s,h,d] = sum_{m < d_c} o_latent[b,s,h,m] * W_UV[h,d,m]
+ *
+ *   o_latent [B,Sq,H,d_c]  latent_dtype (in)
+ *   W_UV     [H,d_h,d_c]   w_dtype      (in)
+ *   out      [B,Sq,H,d_h]  out_dtype    (out)
+ */
+mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W_UV,
+                      void *out, void *stream);
+
+/* Host-only validation of *p (no GPU needed).  Returns MLA_OK or the first error. */
+mla_status_t mla_check_params(const mla_params_t *p);
+
+/*
+ * Host-only split planner.  Given the longest sequence (tokens), the total
+ * tokens of the batch and the number of compute units to fill, sets
+ * p->split_pages and p->num_splits (enough slots for max_pages) so that the
+ * attention kernel has work for every compute unit in chunks of whole pages,
+ * with at least `min_splits` splits for a sequence of max_seq_len tokens.
+ * Reads B, Sq, H, max_pages, kv_dtype and flags.  Returns MLA_OK or an error.
+ */
+mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total_tokens,
+                             int32_t num_cus, int32_t min_splits);
+
+/* Name of the kernel family mla_decode_splitkv would use for *p:
+ * "mfma_bf16", "mfma_fp8" or "generic_f32" (host-only). */
+const char *mla_decode_kernel_name(const mla_params_t *p);
+
+/* Static string for a status code. */
+const char *mla_status_string(mla_status_t s);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char *mla_last_error(void);
+
+/* ABI version: bumped when mla_params_t or a signature changes. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,186 @@
+// C ABI of libmla.so: host-side validation and kernel dispatch.
+// Validation is pure host code (no HIP call), so it can be exercised on a
+// machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kMaxSplits = 4096;   // the merge kernel keeps one weight per split in LDS
+
+mla_status_t fail(mla_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status_t fail(mla_status_t s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+mla_status_t check(const mla_params_t *p) {
+    if (!p) return fail(MLA_ERR_NULL, "params is NULL");
+    if (p->B < 1 || p->Sq < 1 || p->Sq > 16 || p->H < 1)
+        return fail(MLA_ERR_SHAPE, "need B >= 1, 1 <= Sq <= 16, H >= 1 (got B=%d Sq=%d H=%d)", p->B, p->Sq, p->H);
+    if (p->d_h < 1 || p->d_h > 256 || p->d_c < 1 || p->d_c > 1024 || p->d_r < 0 || p->d_r > 256)
+        return fail(MLA_ERR_SHAPE, "need 1<=d_h<=256, 1<=d_c<=1024, 0<=d_r<=256 (got %d, %d, %d)", p->d_h, p->d_c, p->d_r);
+    if (p->page_size != 64) return fail(MLA_ERR_SHAPE, "page_size must be 64 (got %d)", p->page_size);
+    if (p->num_pages < 1 || p->max_pages < 1)
+        return fail(MLA_ERR_SHAPE, "num_pages and max_pages must be >= 1 (got %d, %d)", p->num_pages, p->max_pages);
+    if ((int64_t)p->B * p->Sq * p->H > (1ll << 28))
+        return fail(MLA_ERR_SHAPE, "B*Sq*H too large");
+    if (p->num_splits < 1 || p->num_splits > kMaxSplits)
+        return fail(MLA_ERR_SPLITS, "num_splits must be in [1, %d] (got %d)", kMaxSplits, p->num_splits);
+    if (p->split_pages < 1) return fail(MLA_ERR_SPLITS, "split_pages must be >= 1 (got %d)", p->split_pages);
+    if ((int64_t)p->num_splits * p->split_pages < p->max_pages)
+        return fail(MLA_ERR_SPLITS, "num_splits*split_pages = %lld < max_pages = %d",
+                    (long long)p->num_splits * p->split_pages, p->max_pages);
+    if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(MLA_ERR_SHAPE, "scale must be finite and > 0");
+    if (!is_float_dtype(p->q_dtype)) return fail(MLA_ERR_DTYPE, "q_dtype must be F32 or BF16");
+    if (!is_float_dtype(p->w_dtype)) return fail(MLA_ERR_DTYPE, "w_dtype must be F32 or BF16");
+    if (!is_float_dtype(p->kv_dtype) && p->kv_dtype != MLA_FP8_E4M3)
+        return fail(MLA_ERR_DTYPE, "kv_dtype must be F32, BF16 or FP8_E4M3");
+    if (!is_float_dtype(p->pe_dtype)) return fail(MLA_ERR_DTYPE, "pe_dtype must be F32 or BF16");
+    if (!is_float_dtype(p->latent_dtype)) return fail(MLA_ERR_DTYPE, "latent_dtype must be F32 or BF16");
+    if (!is_float_dtype(p->out_dtype)) return fail(MLA_ERR_DTYPE, "out_dtype must be F32 or BF16");
+    if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC)) return fail(MLA_ERR_SHAPE, "unknown flag bits 0x%x", p->flags);
+    return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return MLA_OK;
+    return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return 1; }
+
+const char *mla_status_string(mla_status_t s) {
+    switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE";
+    case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    }
+    return "MLA_ERR_UNKNOWN";
+}
+
+const char *mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status_t mla_check_params(const mla_params_t *p) { return check(p); }
+
+const char *mla_decode_kernel_name(const mla_params_t *p) {
+    if (!p || check(p) != MLA_OK) return "invalid";
+    if (mla::decode_mfma_supported(*p)) return p->kv_dtype == MLA_FP8_E4M3 ? "mfma_fp8" : "mfma_bf16";
+    return "generic_f32";
+}
+
+mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total_tokens,
+                             int32_t num_cus, int32_t min_splits) {
+    if (!p) return fail(MLA_ERR_NULL, "params is NULL");
+    if (max_seq_len < 0 || total_tokens < 0 || num_cus < 1 || min_splits < 1)
+        return fail(MLA_ERR_SHAPE, "need max_seq_len >= 0, total_tokens >= 0, num_cus >= 1, min_splits >= 1");
+    if (p->max_pages < 1) return fail(MLA_ERR_SHAPE, "max_pages must be >= 1");
+    const int64_t page = 64;
+    const int64_t max_pages_seq = std::max<int64_t>(1, (max_seq_len + page - 1) / page);
+    const int64_t total_pages = std::max<int64_t>(1, (total_tokens + page - 1) / page);
+    int64_t split_pages;
+    if (p->B >= 1 && p->H >= 1 && p->Sq >= 1) {
+        // Workgroups per split: one per 64 query rows on the MFMA path, one per row otherwise.
+        const bool mfma = mla::decode_mfma_supported(*p);
+        const int64_t rows = (int64_t)p->Sq * p->H;
+        const int64_t wg_per_split = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
+        // Aim for about two rounds of equal-sized chunks over the compute units, but keep
+        // chunks long enough that the fp32 partials (d_c*4 bytes per row) stay small next
+        // to the cache they summarise.
+        const int64_t target_wgs = 2ll * num_cus;
+        const int64_t chunks = std::max<int64_t>(1, (target_wgs + wg_per_split - 1) / wg_per_split);
+        split_pages = std::max<int64_t>(1, (total_pages + chunks - 1) / chunks);
+        const int64_t min_chunk = mfma ? 8 : 1;
+        split_pages = std::max(split_pages, min_chunk);
+    } else {
+        split_pages = 1;
+    }
+    // at least min_splits splits for the longest sequence
+    split_pages = std::min(split_pages, std::max<int64_t>(1, max_pages_seq / min_splits));
+    int64_t num_splits = (p->max_pages + split_pages - 1) / split_pages;
+    if (num_splits > kMaxSplits) {
+        split_pages = (p->max_pages + kMaxSplits - 1) / kMaxSplits;
+        num_splits = (p->max_pages + split_pages - 1) / split_pages;
+    }
+    p->split_pages = (int32_t)split_pages;
+    p->num_splits = (int32_t)std::max<int64_t>(1, num_splits);
+    return MLA_OK;
+}
+
+mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void *W_UK, void *q_abs,
+                          void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!q_nope || !W_UK || !q_abs) return fail(MLA_ERR_NULL, "mla_absorb_q: NULL tensor pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mla::absorb_mfma_supported(*p))
+        return hip_status(mla::launch_absorb_mfma(*p, q_nope, W_UK, q_abs, st), "mla_absorb_q launch");
+    return hip_status(mla::launch_absorb_generic(*p, q_nope, W_UK, q_abs, st), "mla_absorb_q launch");
+}
+
+mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const void *q_rope,
+                                const void *c_kv, const void *k_pe, const float *kv_scale,
+                                const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                                float *lse_part, void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!q_abs || !c_kv || !block_table || !seq_lens || !o_part || !lse_part)
+        return fail(MLA_ERR_NULL, "mla_decode_splitkv: NULL tensor pointer");
+    if (p->d_r > 0 && (!q_rope || !k_pe)) return fail(MLA_ERR_NULL, "mla_decode_splitkv: NULL q_rope/k_pe with d_r > 0");
+    if (p->kv_dtype == MLA_FP8_E4M3 && !kv_scale)
+        return fail(MLA_ERR_NULL, "mla_decode_splitkv: kv_scale is required for an FP8_E4M3 cache");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mla::decode_mfma_supported(*p))
+        return hip_status(mla::launch_decode_mfma(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table,
+                                                  seq_lens, o_part, lse_part, st),
+                          "mla_decode_splitkv launch");
+    return hip_status(mla::launch_decode_generic(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table,
+                                                 seq_lens, o_part, lse_part, st),
+                      "mla_decode_splitkv launch");
+}
+
+mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const float *lse_part,
+                             void *o_latent, float *lse_out, void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!o_part || !lse_part || !o_latent) return fail(MLA_ERR_NULL, "mla_combine_lse: NULL tensor pointer");
+    return hip_status(mla::launch_combine(*p, o_part, lse_part, o_latent, lse_out, static_cast<hipStream_t>(stream)),
+                      "mla_combine_lse launch");
+}
+
+mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W_UV, void *out,
+                      void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!o_latent || !W_UV || !out) return fail(MLA_ERR_NULL, "mla_up_v: NULL tensor pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mla::up_v_mfma_supported(*p))
+        return hip_status(mla::launch_up_v_mfma(*p, o_latent, W_UV, out, st), "mla_up_v launch");
+    return hip_status(mla::launch_up_v_generic(*p, o_latent, W_UV, out, st), "mla_up_v launch");
+}
+
+}  // extern "C"

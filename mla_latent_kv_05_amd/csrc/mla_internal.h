@@ -1,0 +1,41 @@
+// Internal launcher interface between the C ABI (mla_api.cpp) and the HIP
+// kernel translation units.  Every launcher enqueues on `stream` and returns
+// the launch status; arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// fp32 VALU kernels for any supported shape / dtype (kernels_generic.hip)
+hipError_t launch_absorb_generic(const mla_params_t &p, const void *q_nope, const void *W_UK,
+                                 void *q_abs, hipStream_t stream);
+hipError_t launch_decode_generic(const mla_params_t &p, const void *q_abs, const void *q_rope,
+                                 const void *c_kv, const void *k_pe, const float *kv_scale,
+                                 const int32_t *block_table, const int32_t *seq_lens,
+                                 float *o_part, float *lse_part, hipStream_t stream);
+hipError_t launch_up_v_generic(const mla_params_t &p, const void *o_latent, const void *W_UV,
+                               void *out, hipStream_t stream);
+hipError_t launch_combine(const mla_params_t &p, const float *o_part, const float *lse_part,
+                          void *o_latent, float *lse_out, hipStream_t stream);
+
+// bf16 MFMA kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip)
+bool decode_mfma_supported(const mla_params_t &p);
+hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const void *q_rope,
+                              const void *c_kv, const void *k_pe, const float *kv_scale,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              float *o_part, float *lse_part, hipStream_t stream);
+bool absorb_mfma_supported(const mla_params_t &p);
+hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
+                              void *q_abs, hipStream_t stream);
+bool up_v_mfma_supported(const mla_params_t &p);
+hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,
+                            void *out, hipStream_t stream);
+
+// Heads x query rows handled by one attention workgroup of the MFMA kernel.
+constexpr int kDecodeRowsPerBlock = 64;
+
+}  // namespace mla

@@ -1,0 +1,235 @@
+"""ctypes binding of libmla.so (include/mla.h), same entry-point names.
+
+Argument marshalling only: tensors must already be on the GPU, contiguous and
+in the dtypes the parameters declare; every step of the computation runs in
+the library's HIP kernels.  Torch provides device memory and the stream.
+There is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+FLAG_GENERIC = 1
+PAGE = 64
+
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",
+          4: "MLA_ERR_SPLITS", 5: "MLA_ERR_HIP", 6: "MLA_ERR_UNSUPPORTED"}
+
+# every symbol include/mla.h declares
+EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v",
+           "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
+           "mla_status_string", "mla_last_error", "mla_abi_version")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    """mirror of mla_params_t"""
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d_h", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("split_pages", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("pe_dtype", ctypes.c_int32),
+                ("latent_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+    def copy(self) -> "Params":
+        q = Params()
+        ctypes.pointer(q)[0] = self
+        return q
+
+    def __repr__(self):
+        return "Params(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def lib():
+    """Load libmla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m mla_latent_kv_05_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(Params)
+        st = ctypes.c_int
+        for name, args in (
+            ("mla_absorb_q", [PP, P, P, P, P]),
+            ("mla_decode_splitkv", [PP, P, P, P, P, P, P, P, P, P, P]),
+            ("mla_combine_lse", [PP, P, P, P, P, P]),
+            ("mla_up_v", [PP, P, P, P, P]),
+            ("mla_check_params", [PP]),
+            ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+        ):
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = st
+        L.mla_decode_kernel_name.argtypes = [PP]
+        L.mla_decode_kernel_name.restype = ctypes.c_char_p
+        L.mla_status_string.argtypes = [st]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_last_error.argtypes = []
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_abi_version.argtypes = []
+        L.mla_abi_version.restype = ctypes.c_int32
+        if L.mla_abi_version() != 1:
+            raise RuntimeError("libmla.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MLAError(status, lib().mla_last_error().decode())
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_params(B: int, Sq: int, H: int, d_h: int, d_c: int, d_r: int, num_pages: int,
+                max_pages: int, num_splits: int = 1, split_pages: Optional[int] = None,
+                scale: Optional[float] = None, q_dtype: int = BF16, w_dtype: int = BF16,
+                kv_dtype: int = BF16, pe_dtype: int = BF16, latent_dtype: int = BF16,
+                out_dtype: int = F32, flags: int = 0) -> Params:
+    if split_pages is None:
+        split_pages = -(-max_pages // num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h + d_r)
+    return Params(B, Sq, H, d_h, d_c, d_r, PAGE, num_pages, max_pages, num_splits, split_pages,
+                  scale, q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype, flags)
+
+
+def check_params(p: Params) -> None:
+    _check(lib().mla_check_params(ctypes.byref(p)))
+
+
+def plan_splits(p: Params, max_seq_len: int, total_tokens: int, num_cus: int = 256,
+                min_splits: int = 1) -> Params:
+    """Fill num_splits / split_pages with the library's planner (host only)."""
+    q = p.copy()
+    _check(lib().mla_plan_splits(ctypes.byref(q), max_seq_len, total_tokens, num_cus, min_splits))
+    return q
+
+
+def decode_kernel_name(p: Params) -> str:
+    return lib().mla_decode_kernel_name(ctypes.byref(p)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor], what: str, shape=None, dtype: Optional[int] = None):
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if dtype is not None and dtype_code(t.dtype) != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype} does not match the parameters")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def absorb_q(p: Params, q_nope, W_UK, q_abs, stream=None) -> None:
+    rows = (p.B, p.Sq, p.H)
+    _check(lib().mla_absorb_q(ctypes.byref(p),
+                              _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
+                              _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
+                              _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype),
+                              _stream(stream)))
+
+
+def decode_splitkv(p: Params, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
+                   o_part, lse_part, stream=None) -> None:
+    rows = (p.B, p.Sq, p.H)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    _check(lib().mla_decode_splitkv(
+        ctypes.byref(p),
+        _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype),
+        _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+        _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+        _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+        _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
+        _stream(stream)))
+
+
+def combine_lse(p: Params, o_part, lse_part, o_latent, lse_out=None, stream=None) -> None:
+    rows = (p.B, p.Sq, p.H)
+    _check(lib().mla_combine_lse(ctypes.byref(p),
+                                 _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                 _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
+                                 _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
+                                 _ptr(lse_out, "lse_out", rows, F32),
+                                 _stream(stream)))
+
+
+def up_v(p: Params, o_latent, W_UV, out, stream=None) -> None:
+    rows = (p.B, p.Sq, p.H)
+    _check(lib().mla_up_v(ctypes.byref(p),
+                          _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
+                          _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+                          _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
+                          _stream(stream)))
+
+
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class DecodeStep:
+    """Owns the intermediates of one decode step (allocated once with torch) and
+    runs the four library calls on the current stream."""
+
+    def __init__(self, p: Params, device="cuda"):
+        self.p = p
+        rows = (p.B, p.Sq, p.H)
+        self.q_abs = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
+        self.o_part = torch.empty(rows + (p.num_splits, p.d_c), dtype=torch.float32, device=device)
+        self.lse_part = torch.empty(rows + (p.num_splits,), dtype=torch.float32, device=device)
+        self.o_latent = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
+        self.lse = torch.empty(rows, dtype=torch.float32, device=device)
+        self.out = torch.empty(rows + (p.d_h,), dtype=_TORCH[p.out_dtype], device=device)
+
+    def __call__(self, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
+                 stream=None):
+        p = self.p
+        absorb_q(p, q_nope, W_UK, self.q_abs, stream)
+        decode_splitkv(p, self.q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
+                       self.o_part, self.lse_part, stream)
+        combine_lse(p, self.o_part, self.lse_part, self.o_latent, self.lse, stream)
+        up_v(p, self.o_latent, W_UV, self.out, stream)
+        return self.out

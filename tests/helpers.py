@@ -1,0 +1,83 @@
+"""Shared plumbing for the test suite: parameter structs for a generated case,
+copying a case to the GPU, the error metric, and row sampling."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from mla_latent_kv_05_amd import inputs as I
+from mla_latent_kv_05_amd import mla
+
+# max|gpu - oracle| / RMS(oracle): fp32 inputs, bf16 inputs, fp8 latent cache
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def err_rms(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(got - ref))) / rms
+
+
+def assert_bf16_rounding(got, ref, acc_rel=1e-3):
+    """Every element is within half a bf16 ulp (at most 2^-8 relative) of the exact
+    value, plus an accumulation allowance of acc_rel * RMS(ref)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bound = np.abs(ref) * 2.0 ** -8 + acc_rel * rms
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{int(bad.sum())} elements beyond bf16 rounding, worst excess " \
+        f"{float(np.max(np.abs(got - ref) - bound)):.3e}"
+
+
+def params_for(case: I.Case, num_splits=None, split_pages=None, flags=0, out_dtype=None,
+               plan=False, num_cus=256) -> mla.Params:
+    wl = case.wl
+    f32 = wl.dtype == "f32"
+    fl = mla.F32 if f32 else mla.BF16
+    kv = mla.FP8_E4M3 if wl.dtype == "fp8" else fl
+    if num_splits is None and split_pages is None:
+        num_splits = 1
+    if num_splits is None:
+        num_splits = -(-case.max_pages // split_pages)
+    p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, case.num_pages, case.max_pages,
+                        num_splits=num_splits, split_pages=split_pages, scale=wl.scale,
+                        q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl, latent_dtype=fl,
+                        out_dtype=mla.F32 if out_dtype is None else out_dtype, flags=flags)
+    if plan:
+        p = mla.plan_splits(p, int(case.seq_lens.max()), case.total_tokens, num_cus=num_cus,
+                            min_splits=wl.min_splits)
+    return p
+
+
+class DeviceCase:
+    """The tensors of a Case on the GPU (storage formats unchanged)."""
+
+    def __init__(self, case: I.Case, device="cuda"):
+        self.case = case
+        for f in ("seq_lens", "block_table", "c_kv", "k_pe", "q_nope", "q_rope", "W_UK", "W_UV"):
+            setattr(self, f, getattr(case, f).to(device).contiguous())
+        self.kv_scale = None if case.kv_scale is None else case.kv_scale.to(device).contiguous()
+
+    def step(self, p: mla.Params) -> mla.DecodeStep:
+        st = mla.DecodeStep(p)
+        st(self.q_nope, self.q_rope, self.c_kv, self.k_pe, self.kv_scale, self.block_table,
+           self.seq_lens, self.W_UK, self.W_UV)
+        return st
+
+
+def sample_rows(case: I.Case, n_seq: int, heads_per_seq: int, seed: int = 0) -> np.ndarray:
+    """Flat (b,s,h) rows: the shortest and longest sequences plus random ones, every
+    query row s, a spread of heads (first, last, random)."""
+    wl = case.wl
+    rng = np.random.default_rng(seed)
+    lens = case.seq_lens.numpy()
+    seqs = {int(lens.argmin()), int(lens.argmax())}
+    while len(seqs) < min(n_seq, wl.B):
+        seqs.add(int(rng.integers(wl.B)))
+    heads = {0, wl.H - 1}
+    while len(heads) < min(heads_per_seq, wl.H):
+        heads.add(int(rng.integers(wl.H)))
+    rows = [(b * wl.Sq + s) * wl.H + h for b in sorted(seqs) for s in range(wl.Sq) for h in sorted(heads)]
+    return np.array(rows, dtype=np.int64)

@@ -1,0 +1,334 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Error metric: max |gpu - oracle| / RMS(oracle) over the compared outputs.
+Bounds: 1e-4 with fp32 inputs, 2e-2 with bf16 inputs, 6e-2 with an fp8 cache.
+Small cases compare every output; the full-size workloads run in the launch
+configuration the bench uses and compare sampled rows the oracle computes
+one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_05_amd import inputs as I
+from mla_latent_kv_05_amd import mla
+from oracle import oracle as O
+from tests.helpers import TOL, DeviceCase, assert_bf16_rounding, err_rms, params_for, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def validate(case: I.Case):
+    """Host-side check that the block table and lengths respect the ABI preconditions."""
+    lens = case.seq_lens.to(torch.int64)
+    assert int(lens.min()) >= 0 and int(lens.max()) <= case.max_pages * 64
+    for b in range(case.wl.B):
+        n = -(-int(lens[b]) // 64)
+        ids = case.block_table[b, :n]
+        assert int(ids.min(initial=0) if n == 0 else ids.min()) >= 0
+        assert n == 0 or int(ids.max()) < case.num_pages
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tol_of(wl):
+    return TOL[wl.dtype]
+
+
+# ------------------------------------------------------------------ one entry point at a time
+
+@pytest.mark.parametrize("wl_name,R,flags", [
+    ("v3_b1", 1, 0), ("v3_b64", 64, 0), ("v3_b64", 70, 0), ("v3_sq4_fp8", 9, 0),
+    ("v3_b64", 70, mla.FLAG_GENERIC), ("tiny", 3, 0),
+])
+def test_absorb_q(wl_name, R, flags):
+    wl = I.workload(wl_name, B=R, Sq=1)
+    case = I.make_case(wl, seq_lens=[64] * wl.B)
+    p = params_for(case, flags=flags)
+    note(f"absorb_q {wl_name} R={R} flags={flags}")
+    qa = torch.empty((wl.B, wl.Sq, wl.H, wl.d_c), dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16,
+                     device="cuda")
+    mla.absorb_q(p, case.q_nope.cuda(), case.W_UK.cuda(), qa)
+    torch.cuda.synchronize()
+    ref = O.absorb_q(O.dims_of(case), case.q_nope, case.W_UK)
+    e = err_rms(qa.float().cpu().numpy(), ref)
+    note(f"  err {e:.3e}")
+    if wl.dtype == "f32":
+        assert e <= 1e-5
+    else:
+        assert e <= TOL["bf16"]
+        assert_bf16_rounding(qa.float().cpu().numpy(), ref)
+
+
+def run_decode(case, p):
+    dc = DeviceCase(case)
+    q_abs = I.random_q_abs(case.wl, seed=123)
+    S = p.num_splits
+    rows = (case.wl.B, case.wl.Sq, case.wl.H)
+    o_part = torch.full(rows + (S, case.wl.d_c), float("nan"), device="cuda")
+    lse_part = torch.full(rows + (S,), float("nan"), device="cuda")
+    mla.decode_splitkv(p, q_abs.cuda(), dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table,
+                       dc.seq_lens, o_part, lse_part)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.decode_splitkv(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
+                                    case.k_pe, case.block_table, case.seq_lens, S, p.split_pages)
+    return o_part.cpu().numpy(), lse_part.cpu().numpy(), ref_o, ref_l
+
+
+@pytest.mark.parametrize("wl_name,lens,split_pages,flags", [
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 1, 0),
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 3, 0),
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 100, 0),
+    ("v3_b64", [130, 5, 1000], 2, mla.FLAG_GENERIC),
+    ("v3_sq4_fp8", [1, 2, 3, 4, 5, 66, 67, 500], 2, 0),
+    ("v3_sq4_fp8", [4, 129, 700], 100, 0),
+    ("v3_b64", [3, 64, 190], 1, 0),
+    ("tiny", [128], 1, 0),
+    ("tiny", [5, 77], 1, 0),
+])
+def test_decode_splitkv(wl_name, lens, split_pages, flags):
+    wl = I.workload(wl_name, B=len(lens))
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, split_pages=split_pages, flags=flags)
+    note(f"decode_splitkv {wl_name} lens={lens} sp={split_pages} S={p.num_splits} "
+         f"kernel={mla.decode_kernel_name(p)}")
+    o, l, ref_o, ref_l = run_decode(case, p)
+    empty = ref_l == -np.inf
+    assert np.array_equal(l == -np.inf, empty), "empty splits differ"
+    full = ~empty
+    assert np.abs(l[full] - ref_l[full]).max() <= (1e-5 if wl.dtype == "f32" else 2e-3)
+    e = err_rms(o[full], ref_o[full])
+    note(f"  o_part err {e:.3e}")
+    assert e <= tol_of(wl)
+
+
+@pytest.mark.parametrize("wl_name,S", [("v3_b64", 7), ("tiny", 3), ("v3_sq4_fp8", 40)])
+def test_combine_lse(wl_name, S):
+    wl = I.workload(wl_name, B=3)
+    o, l = I.random_partials(wl, S, seed=9)
+    D = O.dims(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, S, wl.scale)
+    ref_o, ref_l = O.combine_lse(D, o, l)
+    latent = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, 1, S, num_splits=S,
+                        split_pages=1, latent_dtype=mla.dtype_code(latent))
+    ol = torch.empty((wl.B, wl.Sq, wl.H, wl.d_c), dtype=latent, device="cuda")
+    lse = torch.empty((wl.B, wl.Sq, wl.H), device="cuda")
+    note(f"combine {wl_name} S={S}")
+    mla.combine_lse(p, o.cuda(), l.cuda(), ol, lse)
+    torch.cuda.synchronize()
+    e = err_rms(ol.float().cpu().numpy(), ref_o)
+    if wl.dtype == "f32":
+        assert e <= 1e-5
+    else:
+        assert e <= TOL["bf16"]
+        assert_bf16_rounding(ol.float().cpu().numpy(), ref_o)
+    assert np.abs(lse.cpu().numpy() - ref_l).max() <= 1e-4
+
+
+@pytest.mark.parametrize("wl_name,R,out_dtype,flags", [
+    ("v3_b64", 64, mla.F32, 0), ("v3_b64", 70, mla.BF16, 0), ("v3_b1", 1, mla.F32, 0),
+    ("v3_b64", 5, mla.F32, mla.FLAG_GENERIC), ("tiny", 4, mla.F32, 0),
+])
+def test_up_v(wl_name, R, out_dtype, flags):
+    wl = I.workload(wl_name, B=R, Sq=1)
+    case = I.make_case(wl, seq_lens=[64] * R)
+    ol = I.random_o_latent(wl, seed=5)
+    p = params_for(case, flags=flags, out_dtype=out_dtype)
+    out = torch.empty((wl.B, 1, wl.H, wl.d_h), dtype=torch.float32 if out_dtype == mla.F32 else torch.bfloat16,
+                      device="cuda")
+    note(f"up_v {wl_name} R={R} out={out_dtype} flags={flags}")
+    mla.up_v(p, ol.cuda(), case.W_UV.cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.up_v(O.dims_of(case), ol, case.W_UV)
+    e = err_rms(out.float().cpu().numpy(), ref)
+    note(f"  err {e:.3e}")
+    if wl.dtype == "f32" or out_dtype == mla.F32:
+        assert e <= 1e-4
+    else:
+        assert e <= TOL["bf16"]
+        assert_bf16_rounding(out.float().cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ the whole step, every output
+
+SMALL = [
+    ("tiny", {}, None),                                        # full size: B=1, L=128, fp32
+    ("v3_b1", {}, None),                                       # full size: B=1, L=4096
+    ("v3_b64", {"B": 6}, None),
+    ("v3_long", {"B": 2, "seq_lo": 8192, "seq_hi": 8192}, None),
+    ("v3_sq4_fp8", {"B": 4, "seq_lo": 300, "seq_hi": 2000}, None),
+    ("v3_sq4_fp8", {"B": 3}, [4, 3, 66]),
+]
+
+
+@pytest.mark.parametrize("wl_name,over,lens", SMALL)
+def test_step_matches_oracle(wl_name, over, lens):
+    wl = I.workload(wl_name, **over)
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, plan=True)
+    note(f"step {wl_name} {over} lens={case.seq_lens.tolist()[:8]} S={p.num_splits} sp={p.split_pages}")
+    st = DeviceCase(case).step(p)
+    torch.cuda.synchronize()
+    out, ol, lse = O.decode(case)
+    e = err_rms(st.out.float().cpu().numpy(), out)
+    note(f"  out err {e:.3e}")
+    assert e <= tol_of(wl)
+    vis = lse > -np.inf
+    assert np.abs(st.lse.cpu().numpy()[vis] - lse[vis]).max() <= (1e-5 if wl.dtype == "f32" else 2e-3)
+    assert np.all(st.lse.cpu().numpy()[~vis] == -np.inf)
+
+
+def test_generic_path_matches_oracle_at_v3_shapes():
+    wl = I.workload("v3_b64", B=3, Sq=2)
+    case = I.make_case(wl, seq_lens=[70, 2, 300])
+    p = params_for(case, split_pages=2, flags=mla.FLAG_GENERIC)
+    st = DeviceCase(case).step(p)
+    torch.cuda.synchronize()
+    out, _, _ = O.decode(case)
+    assert err_rms(st.out.float().cpu().numpy(), out) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ invariances and edge cases
+
+def test_split_count_invariance():
+    wl = I.workload("v3_b64", B=2, seq_lo=4096, seq_hi=4096)
+    case = I.make_case(wl)
+    dc = DeviceCase(case)
+    outs = []
+    for S in (1, 2, 8, 32, 64):
+        p = params_for(case, num_splits=S)
+        note(f"split invariance S={S} sp={p.split_pages}")
+        outs.append(dc.step(p).out.cpu().numpy())
+    torch.cuda.synchronize()
+    ref, _, _ = O.decode(case)
+    for o in outs:
+        assert err_rms(o, ref) <= TOL["bf16"]
+    for o in outs[1:]:
+        assert err_rms(o, outs[0]) <= TOL["bf16"]
+
+
+def test_physical_page_order_and_padding_contents_do_not_matter():
+    """Permuting physical pages (with the block table) gives bitwise-identical output,
+    and NaN in the unused slots of last pages changes nothing."""
+    for name in ("v3_b64", "v3_sq4_fp8"):
+        wl = I.workload(name, B=3)
+        case = I.make_case(wl, seq_lens=[100, 4, 250])
+        p = params_for(case, split_pages=2)
+        a = DeviceCase(case).step(p).out.cpu()
+        perm = torch.randperm(case.num_pages, generator=torch.Generator().manual_seed(2))
+        inv = torch.argsort(perm).int()
+        case2 = I.Case(**{**case.__dict__})
+        case2.c_kv = case.c_kv[perm].contiguous()
+        case2.k_pe = case.k_pe[perm].contiguous()
+        if case.kv_scale is not None:
+            case2.kv_scale = case.kv_scale[perm].contiguous()
+        case2.block_table = torch.where(case.block_table >= 0, inv[case.block_table.clamp(min=0)],
+                                        case.block_table).contiguous()
+        b = DeviceCase(case2).step(p).out.cpu()
+        assert torch.equal(a, b), name
+        # poison every slot past the end of each sequence
+        case3 = I.Case(**{**case.__dict__})
+        case3.c_kv = case.c_kv.clone()
+        case3.k_pe = case.k_pe.clone()
+        case3.kv_scale = None if case.kv_scale is None else case.kv_scale.clone()
+        for bb, n in enumerate(case.seq_lens.tolist()):
+            if n % 64:
+                pg = int(case.block_table[bb, n // 64])
+                if case.kv_scale is None:
+                    case3.c_kv[pg, n % 64:] = float("nan")
+                else:
+                    case3.c_kv[pg, n % 64:] = 0x7F             # e4m3 NaN code
+                    case3.kv_scale[pg, n % 64:] = float("nan")
+                case3.k_pe[pg, n % 64:] = float("nan")
+        c = DeviceCase(case3).step(p).out.cpu()
+        assert torch.equal(a, c), name
+
+
+def test_causal_row_equals_shorter_single_row_run():
+    wl4 = I.workload("v3_sq4_fp8", B=2)
+    case = I.make_case(wl4, seq_lens=[300, 70])
+    p4 = params_for(case, split_pages=2)
+    out4 = DeviceCase(case).step(p4).out.cpu().numpy()
+    for s in range(4):
+        wl1 = I.workload("v3_sq4_fp8", B=2, Sq=1)
+        c1 = I.Case(**{**case.__dict__, "wl": wl1, "seq_lens": (case.seq_lens - 3 + s).contiguous(),
+                       "q_nope": case.q_nope[:, s:s + 1].contiguous(),
+                       "q_rope": case.q_rope[:, s:s + 1].contiguous()})
+        p1 = params_for(c1, split_pages=2)
+        out1 = DeviceCase(c1).step(p1).out.cpu().numpy()
+        assert err_rms(out4[:, s], out1[:, 0]) <= 1e-3
+
+
+def test_degenerate_lengths():
+    """seq_len < Sq leaves leading query rows with nothing visible: zero output, lse -inf."""
+    wl = I.workload("v3_sq4_fp8", B=3)
+    case = I.make_case(wl, seq_lens=[1, 2, 64])
+    p = params_for(case, split_pages=1)
+    st = DeviceCase(case).step(p)
+    torch.cuda.synchronize()
+    out, _, lse = O.decode(case)
+    got_l = st.lse.cpu().numpy()
+    assert np.array_equal(got_l == -np.inf, lse == -np.inf)
+    assert np.all(st.out.cpu().numpy()[lse == -np.inf] == 0)
+    assert err_rms(st.out.cpu().numpy(), out) <= TOL["fp8"]
+
+
+def test_wide_block_table_and_unreferenced_pages():
+    wl = I.workload("v3_b64", B=2)
+    case = I.make_case(wl, seq_lens=[65, 130], max_pages=40, extra_pages=5)
+    validate(case)
+    p = params_for(case, split_pages=3)
+    st = DeviceCase(case).step(p)
+    torch.cuda.synchronize()
+    out, _, _ = O.decode(case)
+    assert err_rms(st.out.cpu().numpy(), out) <= TOL["bf16"]
+
+
+def test_repeatable_bitwise():
+    wl = I.workload("v3_b64", B=4)
+    case = I.make_case(wl)
+    p = params_for(case, plan=True)
+    dc = DeviceCase(case)
+    a = dc.step(p).out.cpu()
+    b = dc.step(p).out.cpu()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+FULL = [
+    ("v3_b64", 6, 24),       # B=64, L ~ U[1024, 8192], permuted pages
+    ("v3_long", 2, 12),      # B=4, L = 131072, >= 32 splits
+    ("v3_sq4_fp8", 4, 12),   # B=128, Sq=4, L ~ U[4096, 16384], e4m3 cache
+]
+
+
+@pytest.mark.parametrize("wl_name,n_seq,n_heads", FULL)
+def test_full_size_sampled(wl_name, n_seq, n_heads):
+    wl = I.workload(wl_name)
+    note(f"full {wl_name}: generating")
+    case = I.make_case(wl)
+    validate(case)
+    p = params_for(case, plan=True)
+    note(f"full {wl_name}: tokens={case.total_tokens} pages={case.num_pages} S={p.num_splits} "
+         f"sp={p.split_pages} kernel={mla.decode_kernel_name(p)}")
+    st = DeviceCase(case).step(p)
+    torch.cuda.synchronize()
+    got = st.out.float().cpu().numpy().reshape(-1, wl.d_h)
+    got_l = st.lse.cpu().numpy().reshape(-1)
+    assert np.isfinite(got).all()
+    rows = sample_rows(case, n_seq, n_heads)
+    note(f"full {wl_name}: oracle on {len(rows)} rows")
+    out, _, lse = O.decode(case, rows=rows)
+    e = err_rms(got[rows], out)
+    note(f"  sampled out err {e:.3e}")
+    assert e <= tol_of(wl)
+    assert np.abs(got_l[rows] - lse).max() <= 2e-3
