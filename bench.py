@@ -145,7 +145,7 @@ def main():
                         f"d_c={wl.d_c}, d_r={wl.d_r}, seq_lens U[{wl.seq_lo},{wl.seq_hi}] "
                         f"(sum {case.total_tokens}), page 64, permuted pages, {wl.dtype} cache",
             "name": wl.name, "B": wl.B, "Sq": wl.Sq, "tokens": case.total_tokens,
-            "num_splits": p.num_splits, "split_pages": p.split_pages,
+            "num_splits": p.num_splits, "num_parts": p.num_parts,
             "decode_kernel": mla.decode_kernel_name(p), "replicas": args.replicas,
         },
         "roofline": {

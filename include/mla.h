@@ -51,7 +51,7 @@ typedef enum {
     MLA_ERR_NULL = 1,        /* a required pointer is NULL */
     MLA_ERR_SHAPE = 2,       /* a dimension is out of range */
     MLA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
-    MLA_ERR_SPLITS = 4,      /* num_splits * split_pages cannot cover max_pages */
+    MLA_ERR_SPLITS = 4,      /* split plan out of range (see num_splits / split_pages / num_parts) */
     MLA_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
     MLA_ERR_UNSUPPORTED = 6  /* a valid request no kernel here implements */
 } mla_status_t;
@@ -72,9 +72,21 @@ typedef enum {
  *   num_pages   physical pages in c_kv / k_pe / kv_scale          >= 1
  *   max_pages   row stride of block_table                         >= 1
  *   num_splits  S: split slots per sequence (stride of o_part / lse_part) >= 1
- *   split_pages pages per split; split c of sequence b covers its pages
- *               [c*split_pages, (c+1)*split_pages).  Requires
- *               num_splits * split_pages >= max_pages.
+ *   split_pages fixed splits (num_parts == 0): pages per split; split c of
+ *               sequence b covers its pages [c*split_pages, (c+1)*split_pages).
+ *               Requires num_splits * split_pages >= max_pages.
+ *   num_parts   0 for fixed splits; P >= 1 for balanced splits, which give
+ *               every part of the work the same number of pages whatever the
+ *               length mix.  With n_b = ceil(seq_lens[b] / 64) pages for
+ *               sequence b, off_b = n_0 + ... + n_{b-1} and T = sum_b n_b, the
+ *               batch's pages taken in order are cut into P parts, part j
+ *               holding pages [floor(j*T/P), floor((j+1)*T/P)).  Split c of
+ *               sequence b is its pages in part j0(b) + c, where j0(b) is the
+ *               part holding its first page (a sequence touches one part per
+ *               split, consecutively).  split_pages is ignored.  Requires
+ *               num_splits >= the largest number of parts any sequence touches,
+ *               which mla_plan_splits guarantees; a split index at or past
+ *               num_splits is not computed.
  *   scale       softmax scale, 1/sqrt(d_h + d_r) ("DeepSeek-MLA-Principle"
  *               sec. 2; the decode module's self.scale)
  *   q_dtype     q_nope, q_rope            F32 | BF16
@@ -95,6 +107,7 @@ typedef struct {
     float scale;
     int32_t q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype;
     uint32_t flags;
+    int32_t num_parts;
 } mla_params_t;
 
 /*
@@ -125,6 +138,9 @@ mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void 
  *   lse_part[b,s,h,c]  = ln sum_{t in T} exp(z_t)          (-inf if T empty)
  *   o_part[b,s,h,c,:]  = sum_{t in T} exp(z_t - lse) C_t   (normalised; left
  *                        unwritten when T is empty)
+ * With balanced splits, "the sequence's pages" of split c are those given
+ * under num_parts above.  In both modes every lse_part slot c < num_splits of
+ * every row is written.
  *
  *   q_abs     [B,Sq,H,d_c]          latent_dtype (in)
  *   q_rope    [B,Sq,H,d_r]          q_dtype      (in)
@@ -178,11 +194,12 @@ mla_status_t mla_check_params(const mla_params_t *p);
 
 /*
  * Host-only split planner.  Given the longest sequence (tokens), the total
- * tokens of the batch and the number of compute units to fill, sets
- * p->split_pages and p->num_splits (enough slots for max_pages) so that the
- * attention kernel has work for every compute unit in chunks of whole pages,
- * with at least `min_splits` splits for a sequence of max_seq_len tokens.
- * Reads B, Sq, H, max_pages, kv_dtype and flags.  Returns MLA_OK or an error.
+ * tokens of the batch and the number of compute units to fill, chooses
+ * balanced splits: sets p->num_parts (one workgroup per compute unit, parts of
+ * at least 8 pages, at least `min_splits` parts when the batch has that many
+ * pages) and p->num_splits, the bound on the parts one sequence can touch.
+ * max_seq_len must not be below, and total_tokens not above, the true values.
+ * Reads B, Sq, H, max_pages, the dtypes and flags.  Returns MLA_OK or an error.
  */
 mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total_tokens,
                              int32_t num_cus, int32_t min_splits);

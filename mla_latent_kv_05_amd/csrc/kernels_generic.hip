@@ -41,6 +41,50 @@ __device__ __forceinline__ float block_reduce_sum(float v, float *red) {
     return r;
 }
 
+__device__ __forceinline__ int64_t block_reduce_sum_i64(int64_t v, int64_t *red) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    int64_t r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r += red[i];
+    return r;
+}
+
+// Pages [*pa, *pb) of sequence b that split c covers (empty when *pa >= *pb).
+// Fixed splits: [c*split_pages, (c+1)*split_pages).  Balanced splits: the
+// batch's pages in sequence order are cut into num_parts parts, part j holding
+// flattened pages [floor(j*T/P), floor((j+1)*T/P)); split c of b is its pages
+// in part j0 + c, j0 being the part that holds b's first page.
+__device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict__ seq_lens, int b, int c,
+                               int64_t *pa, int64_t *pb, int64_t *red) {
+    const int64_t pages = (seq_lens[b] + p.page_size - 1) / p.page_size;
+    if (p.num_parts == 0) {
+        *pa = static_cast<int64_t>(c) * p.split_pages;
+        *pb = *pa + p.split_pages;
+        if (*pb > pages) *pb = pages;
+        return;
+    }
+    int64_t tot = 0, before = 0;
+    for (int i = threadIdx.x; i < p.B; i += kThreads) {
+        const int64_t n = (seq_lens[i] + p.page_size - 1) / p.page_size;
+        tot += n;
+        if (i < b) before += n;
+    }
+    const int64_t T = block_reduce_sum_i64(tot, red);
+    const int64_t off = block_reduce_sum_i64(before, red);
+    *pa = 0;
+    *pb = 0;
+    if (pages == 0) return;
+    const int64_t P = p.num_parts;
+    const int64_t j = ((off + 1) * P - 1) / T + c;      // part holding b's first page, plus c
+    if (j >= P) return;
+    const int64_t lo = j * T / P - off, hi = (j + 1) * T / P - off;
+    *pa = lo > 0 ? lo : 0;
+    *pb = hi < pages ? hi : pages;
+}
+
 // q_abs[row, m] = sum_d q_nope[row, d] * W_UK[h, d, m]; one block per (b,s,h) row.
 __global__ __launch_bounds__(kThreads) void absorb_generic_kernel(
     mla_params_t p, const void *__restrict__ q_nope, const void *__restrict__ W_UK,
@@ -73,6 +117,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
     __shared__ float pw[kThreads];
     __shared__ int64_t prow[kThreads];
     __shared__ float red[kThreads / 64];
+    __shared__ int64_t red64[kThreads / 64];
 
     const int S = p.num_splits;
     const int64_t row = blockIdx.x / S;
@@ -80,8 +125,10 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
     const int b = static_cast<int>(row / (static_cast<int64_t>(p.Sq) * p.H));
     const int s = static_cast<int>((row / p.H) % p.Sq);
     const int64_t n = static_cast<int64_t>(seq_lens[b]) - p.Sq + 1 + s;   // visible positions
-    const int64_t t0 = static_cast<int64_t>(c) * p.split_pages * p.page_size;
-    int64_t t1 = t0 + static_cast<int64_t>(p.split_pages) * p.page_size;
+    int64_t pa, pb;
+    split_pages_of(p, seq_lens, b, c, &pa, &pb, red64);
+    const int64_t t0 = pa * p.page_size;
+    int64_t t1 = pb * p.page_size;
     if (t1 > n) t1 = n;
     const int64_t out_idx = row * S + c;
     if (t1 <= t0) {

@@ -16,6 +16,7 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr int kMaxSplits = 4096;   // the merge kernel keeps one weight per split in LDS
+constexpr int kMaxParts = 1 << 20;
 
 mla_status_t fail(mla_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 mla_status_t fail(mla_status_t s, const char *fmt, ...) {
@@ -43,10 +44,16 @@ mla_status_t check(const mla_params_t *p) {
         return fail(MLA_ERR_SHAPE, "B*Sq*H too large");
     if (p->num_splits < 1 || p->num_splits > kMaxSplits)
         return fail(MLA_ERR_SPLITS, "num_splits must be in [1, %d] (got %d)", kMaxSplits, p->num_splits);
-    if (p->split_pages < 1) return fail(MLA_ERR_SPLITS, "split_pages must be >= 1 (got %d)", p->split_pages);
-    if ((int64_t)p->num_splits * p->split_pages < p->max_pages)
-        return fail(MLA_ERR_SPLITS, "num_splits*split_pages = %lld < max_pages = %d",
-                    (long long)p->num_splits * p->split_pages, p->max_pages);
+    if (p->num_parts < 0 || p->num_parts > kMaxParts)
+        return fail(MLA_ERR_SPLITS, "num_parts must be in [0, %d] (got %d)", kMaxParts, p->num_parts);
+    if (p->num_parts == 0) {
+        if (p->split_pages < 1) return fail(MLA_ERR_SPLITS, "split_pages must be >= 1 (got %d)", p->split_pages);
+        if ((int64_t)p->num_splits * p->split_pages < p->max_pages)
+            return fail(MLA_ERR_SPLITS, "num_splits*split_pages = %lld < max_pages = %d",
+                        (long long)p->num_splits * p->split_pages, p->max_pages);
+        if ((int64_t)p->B * p->num_splits > (1ll << 31) / 64)
+            return fail(MLA_ERR_SPLITS, "B*num_splits too large");
+    }
     if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(MLA_ERR_SHAPE, "scale must be finite and > 0");
     if (!is_float_dtype(p->q_dtype)) return fail(MLA_ERR_DTYPE, "q_dtype must be F32 or BF16");
     if (!is_float_dtype(p->w_dtype)) return fail(MLA_ERR_DTYPE, "w_dtype must be F32 or BF16");
@@ -68,7 +75,7 @@ mla_status_t hip_status(hipError_t e, const char *what) {
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 1; }
+int32_t mla_abi_version(void) { return 2; }
 
 const char *mla_status_string(mla_status_t s) {
     switch (s) {
@@ -98,36 +105,33 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     if (!p) return fail(MLA_ERR_NULL, "params is NULL");
     if (max_seq_len < 0 || total_tokens < 0 || num_cus < 1 || min_splits < 1)
         return fail(MLA_ERR_SHAPE, "need max_seq_len >= 0, total_tokens >= 0, num_cus >= 1, min_splits >= 1");
-    if (p->max_pages < 1) return fail(MLA_ERR_SHAPE, "max_pages must be >= 1");
+    if (p->B < 1 || p->H < 1 || p->Sq < 1) return fail(MLA_ERR_SHAPE, "need B, Sq, H >= 1");
     const int64_t page = 64;
     const int64_t max_pages_seq = std::max<int64_t>(1, (max_seq_len + page - 1) / page);
-    const int64_t total_pages = std::max<int64_t>(1, (total_tokens + page - 1) / page);
-    int64_t split_pages;
-    if (p->B >= 1 && p->H >= 1 && p->Sq >= 1) {
-        // Workgroups per split: one per 64 query rows on the MFMA path, one per row otherwise.
-        const bool mfma = mla::decode_mfma_supported(*p);
-        const int64_t rows = (int64_t)p->Sq * p->H;
-        const int64_t wg_per_split = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
-        // Aim for about two rounds of equal-sized chunks over the compute units, but keep
-        // chunks long enough that the fp32 partials (d_c*4 bytes per row) stay small next
-        // to the cache they summarise.
-        const int64_t target_wgs = 2ll * num_cus;
-        const int64_t chunks = std::max<int64_t>(1, (target_wgs + wg_per_split - 1) / wg_per_split);
-        split_pages = std::max<int64_t>(1, (total_pages + chunks - 1) / chunks);
-        const int64_t min_chunk = mfma ? 8 : 1;
-        split_pages = std::max(split_pages, min_chunk);
-    } else {
-        split_pages = 1;
-    }
-    // at least min_splits splits for the longest sequence
-    split_pages = std::min(split_pages, std::max<int64_t>(1, max_pages_seq / min_splits));
-    int64_t num_splits = (p->max_pages + split_pages - 1) / split_pages;
-    if (num_splits > kMaxSplits) {
-        split_pages = (p->max_pages + kMaxSplits - 1) / kMaxSplits;
-        num_splits = (p->max_pages + split_pages - 1) / split_pages;
-    }
-    p->split_pages = (int32_t)split_pages;
-    p->num_splits = (int32_t)std::max<int64_t>(1, num_splits);
+    const int64_t pages_lo = (total_tokens + page - 1) / page;   // <= the batch's true page count
+    // one workgroup per compute unit: each part is processed by Sq*H/64 workgroups
+    // on the MFMA path (one per (row, split) on the generic path)
+    const bool mfma = mla::decode_mfma_supported(*p);
+    const int64_t rows = (int64_t)p->Sq * p->H;
+    const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
+    int64_t P = std::max<int64_t>(1, num_cus / wg_per_part);
+    if (!mfma) P = std::max<int64_t>(1, 2ll * num_cus / wg_per_part);
+    // parts of at least 8 pages keep the fp32 partials (d_c*4 bytes per row) small next
+    // to the cache they summarise
+    P = std::min(P, std::max<int64_t>(1, pages_lo / 8));
+    P = std::max(P, std::min<int64_t>(min_splits, std::max<int64_t>(1, pages_lo)));
+    P = std::min<int64_t>(P, kMaxParts);
+    // a sequence of n pages touches at most ceil(n / q) + 1 parts of >= q pages, and
+    // at most n parts
+    const int64_t q_lo = pages_lo / P;
+    int64_t S = q_lo >= 1 ? (max_pages_seq + q_lo - 1) / q_lo + 1 : max_pages_seq;
+    S = std::min(S, max_pages_seq);
+    S = std::min(S, P);
+    S = std::max<int64_t>(S, 1);
+    if (S > kMaxSplits) return fail(MLA_ERR_SPLITS, "planned num_splits %lld exceeds %d", (long long)S, kMaxSplits);
+    p->num_parts = (int32_t)P;
+    p->num_splits = (int32_t)S;
+    if (p->split_pages < 1) p->split_pages = 1;   // unused with balanced splits
     return MLA_OK;
 }
 
@@ -154,6 +158,12 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
     if (p->kv_dtype == MLA_FP8_E4M3 && !kv_scale)
         return fail(MLA_ERR_NULL, "mla_decode_splitkv: kv_scale is required for an FP8_E4M3 cache");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t rows = (int64_t)p->B * p->Sq * p->H;
+    const int64_t parts = p->num_parts > 0 ? p->num_parts : (int64_t)p->B * p->num_splits;
+    const int64_t grid = mla::decode_mfma_supported(*p)
+                             ? (parts + 7) / 8 * 8 * (rows / p->B / mla::kDecodeRowsPerBlock)
+                             : rows * p->num_splits;
+    if (grid > 0x7fffffffll) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: grid of %lld workgroups too large", (long long)grid);
     if (mla::decode_mfma_supported(*p))
         return hip_status(mla::launch_decode_mfma(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table,
                                                   seq_lens, o_part, lse_part, st),

@@ -46,7 +46,7 @@ class Params(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("pe_dtype", ctypes.c_int32),
                 ("latent_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("num_parts", ctypes.c_int32)]
 
     def copy(self) -> "Params":
         q = Params()
@@ -90,7 +90,7 @@ def lib():
         L.mla_last_error.restype = ctypes.c_char_p
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = ctypes.c_int32
-        if L.mla_abi_version() != 1:
+        if L.mla_abi_version() != 2:
             raise RuntimeError("libmla.so ABI version mismatch")
         _lib = L
     return _lib
@@ -115,13 +115,13 @@ def make_params(B: int, Sq: int, H: int, d_h: int, d_c: int, d_r: int, num_pages
                 max_pages: int, num_splits: int = 1, split_pages: Optional[int] = None,
                 scale: Optional[float] = None, q_dtype: int = BF16, w_dtype: int = BF16,
                 kv_dtype: int = BF16, pe_dtype: int = BF16, latent_dtype: int = BF16,
-                out_dtype: int = F32, flags: int = 0) -> Params:
+                out_dtype: int = F32, flags: int = 0, num_parts: int = 0) -> Params:
     if split_pages is None:
         split_pages = -(-max_pages // num_splits)
     if scale is None:
         scale = 1.0 / math.sqrt(d_h + d_r)
     return Params(B, Sq, H, d_h, d_c, d_r, PAGE, num_pages, max_pages, num_splits, split_pages,
-                  scale, q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype, flags)
+                  scale, q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype, flags, num_parts)
 
 
 def check_params(p: Params) -> None:
@@ -130,7 +130,8 @@ def check_params(p: Params) -> None:
 
 def plan_splits(p: Params, max_seq_len: int, total_tokens: int, num_cus: int = 256,
                 min_splits: int = 1) -> Params:
-    """Fill num_splits / split_pages with the library's planner (host only)."""
+    """Balanced split plan from the library's planner (host only): fills num_parts
+    and num_splits."""
     q = p.copy()
     _check(lib().mla_plan_splits(ctypes.byref(q), max_seq_len, total_tokens, num_cus, min_splits))
     return q

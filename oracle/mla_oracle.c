@@ -223,6 +223,47 @@ void orc_decode_splitkv(const orc_dims *D, const void *q_abs, int qa_dt,
     }
 }
 
+/* ---- split partials over explicit page ranges ------------------------------
+ * Split c of sequence b covers the sequence's pages [page_begin[b*S+c],
+ * page_end[b*S+c]) (empty when begin >= end); within it, positions below the
+ * row's visible count.  Same arithmetic as orc_decode_splitkv, for a split
+ * plan given as data.  o_part [B,Sq,H,S,d_c], lse_part [B,Sq,H,S]. */
+void orc_decode_page_ranges(const orc_dims *D, const void *q_abs, int qa_dt,
+                            const void *q_rope, int qr_dt,
+                            const void *c_kv, int kv_dt, const float *kv_scale,
+                            const void *k_pe, int pe_dt,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int num_splits, const int32_t *page_begin, const int32_t *page_end,
+                            double *o_part, double *lse_part)
+{
+    cache_t C = {D, c_kv, kv_dt, kv_scale, k_pe, pe_dt, block_table};
+    int64_t rows = (int64_t)D->B * D->Sq * D->H;
+    int64_t maxlen = 0;
+    for (int b = 0; b < D->B; ++b) if (seq_lens[b] > maxlen) maxlen = seq_lens[b];
+#pragma omp parallel
+    {
+        double *qa = malloc(sizeof(double) * (D->d_c + 1));
+        double *qr = malloc(sizeof(double) * (D->d_r + 1));
+        double *z = malloc(sizeof(double) * (maxlen + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t row = 0; row < rows; ++row) {
+            int b = (int)(row / ((int64_t)D->Sq * D->H));
+            int s = (int)((row / D->H) % D->Sq);
+            load_row(q_abs, qa_dt, row, D->d_c, qa);
+            load_row(q_rope, qr_dt, row, D->d_r, qr);
+            int64_t n = visible(D, seq_lens, b, s);
+            for (int c = 0; c < num_splits; ++c) {
+                int64_t t0 = (int64_t)page_begin[b * num_splits + c] * D->page_size;
+                int64_t t1 = (int64_t)page_end[b * num_splits + c] * D->page_size;
+                if (t1 > n) t1 = n;
+                lse_part[row * num_splits + c] =
+                    attend(&C, b, qa, qr, t0, t1, z, o_part + (row * num_splits + c) * D->d_c);
+            }
+        }
+        free(qa); free(qr); free(z);
+    }
+}
+
 /* ---- log-sum-exp merge of split partials ---------------------------------
  * lse = M + ln sum_c exp(lse_c - M), o = sum_c exp(lse_c - lse) o_c with
  * M = max_c lse_c.  Splits with lse_c = -inf carry no weight and their o_c is

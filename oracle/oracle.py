@@ -58,6 +58,7 @@ def lib():
         L.orc_decode_array.argtypes = [P, I, I64, P]
         L.orc_absorb_q.argtypes = [D, P, I, P, I, P]
         L.orc_decode_splitkv.argtypes = [D, P, I, P, I, P, I, P, P, I, P, P, I, I, P, P]
+        L.orc_decode_page_ranges.argtypes = [D, P, I, P, I, P, I, P, P, I, P, P, I, P, P, P, P]
         L.orc_combine_lse.argtypes = [D, I, P, I, P, P, P]
         L.orc_up_v.argtypes = [D, P, I, P, I, P]
         L.orc_decode.argtypes = [D, P, P, I, P, I, P, P, I, P, P, I, P, P, I64, P, P, P, P]
@@ -137,6 +138,26 @@ def decode_splitkv(D: Dims, q_abs, q_rope, c_kv, kv_scale, k_pe, block_table, se
                              _p(c_kv), _dt(c_kv), _p(ks), _p(k_pe), _dt(k_pe),
                              _p(block_table), _p(seq_lens), num_splits, split_pages,
                              _np_ptr(o), _np_ptr(lse))
+    return o, lse
+
+
+def decode_page_ranges(D: Dims, q_abs, q_rope, c_kv, kv_scale, k_pe, block_table, seq_lens,
+                       page_begin: np.ndarray, page_end: np.ndarray):
+    """Split partials for a split plan given as data: split c of sequence b covers
+    its pages [page_begin[b, c], page_end[b, c]).  Returns (o_part, lse_part) in
+    float64, shaped as decode_splitkv's."""
+    q_abs = q_abs.contiguous()
+    pb = np.ascontiguousarray(page_begin, dtype=np.int32)
+    pe = np.ascontiguousarray(page_end, dtype=np.int32)
+    assert pb.shape == pe.shape and pb.shape[0] == D.B
+    S = pb.shape[1]
+    o = np.empty((D.B, D.Sq, D.H, S, D.d_c), dtype=np.float64)
+    lse = np.empty((D.B, D.Sq, D.H, S), dtype=np.float64)
+    ks = None if kv_scale is None else kv_scale.contiguous()
+    lib().orc_decode_page_ranges(ctypes.byref(D), _p(q_abs), _dt(q_abs), _p(q_rope), _dt(q_rope),
+                                 _p(c_kv), _dt(c_kv), _p(ks), _p(k_pe), _dt(k_pe),
+                                 _p(block_table), _p(seq_lens), S, _np_ptr(pb), _np_ptr(pe),
+                                 _np_ptr(o), _np_ptr(lse))
     return o, lse
 
 

@@ -2,6 +2,8 @@
 copying a case to the GPU, the error metric, and row sampling."""
 from __future__ import annotations
 
+import bisect
+
 import numpy as np
 import torch
 
@@ -31,20 +33,61 @@ def assert_bf16_rounding(got, ref, acc_rel=1e-3):
         f"{float(np.max(np.abs(got - ref) - bound)):.3e}"
 
 
+def split_page_ranges(seq_lens, p: mla.Params):
+    """Pages [begin, end) of sequence b that split slot c covers under p's split plan,
+    as two [B, num_splits] int32 arrays (end <= begin: empty).  Written from the
+    plan's definition in the C header, independently of the kernels: fixed splits
+    cover [c*split_pages, (c+1)*split_pages); balanced splits cut the batch's pages,
+    taken in sequence order, into num_parts parts at floor(j*T/P), and slot c of
+    sequence b is its share of the (c+1)-th part it touches."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    n = (lens + 63) // 64
+    B, S = len(lens), p.num_splits
+    beg = np.zeros((B, S), np.int64)
+    end = np.zeros((B, S), np.int64)
+    if p.num_parts == 0:
+        for b in range(B):
+            for c in range(S):
+                beg[b, c] = c * p.split_pages
+                end[b, c] = min((c + 1) * p.split_pages, n[b])
+        return beg.astype(np.int32), np.maximum(end, beg).astype(np.int32)
+    P, T = p.num_parts, int(n.sum())
+    starts = [j * T // P for j in range(P + 1)]
+    off = 0
+    for b in range(B):
+        if n[b] > 0:
+            # the parts holding the sequence's first and last pages
+            j0 = bisect.bisect_right(starts[:P], off) - 1
+            jl = bisect.bisect_right(starts[:P], off + n[b] - 1) - 1
+            for j in range(j0, jl + 1):
+                c = j - j0
+                assert c < S, f"sequence {b} touches more than num_splits={S} parts"
+                beg[b, c] = max(starts[j] - off, 0)
+                end[b, c] = min(starts[j + 1] - off, n[b])
+        off += n[b]
+    return beg.astype(np.int32), np.maximum(end, beg).astype(np.int32)
+
+
 def params_for(case: I.Case, num_splits=None, split_pages=None, flags=0, out_dtype=None,
-               plan=False, num_cus=256) -> mla.Params:
+               plan=False, num_cus=256, num_parts=0) -> mla.Params:
     wl = case.wl
     f32 = wl.dtype == "f32"
     fl = mla.F32 if f32 else mla.BF16
     kv = mla.FP8_E4M3 if wl.dtype == "fp8" else fl
-    if num_splits is None and split_pages is None:
+    if num_parts:
+        # balanced splits with exactly as many slots as the plan needs (+ extra_slots)
+        num_splits, split_pages = 1, 1
+    elif num_splits is None and split_pages is None:
         num_splits = 1
     if num_splits is None:
         num_splits = -(-case.max_pages // split_pages)
     p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, case.num_pages, case.max_pages,
                         num_splits=num_splits, split_pages=split_pages, scale=wl.scale,
                         q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl, latent_dtype=fl,
-                        out_dtype=mla.F32 if out_dtype is None else out_dtype, flags=flags)
+                        out_dtype=mla.F32 if out_dtype is None else out_dtype, flags=flags,
+                        num_parts=num_parts)
+    if num_parts:
+        p.num_splits = max(1, int(touched_parts(case.seq_lens, num_parts).max()))
     if plan:
         p = mla.plan_splits(p, int(case.seq_lens.max()), case.total_tokens, num_cus=num_cus,
                             min_splits=wl.min_splits)
@@ -81,3 +124,17 @@ def sample_rows(case: I.Case, n_seq: int, heads_per_seq: int, seed: int = 0) -> 
         heads.add(int(rng.integers(wl.H)))
     rows = [(b * wl.Sq + s) * wl.H + h for b in sorted(seqs) for s in range(wl.Sq) for h in sorted(heads)]
     return np.array(rows, dtype=np.int64)
+
+
+def touched_parts(seq_lens, num_parts: int) -> np.ndarray:
+    """Number of balanced-split parts each sequence touches (0 for an empty one)."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    n = (lens + 63) // 64
+    T, P = int(n.sum()), num_parts
+    starts = [j * T // P for j in range(P)]
+    off = np.concatenate([[0], np.cumsum(n)[:-1]])
+    out = np.zeros(len(n), np.int64)
+    for b in range(len(n)):
+        if n[b]:
+            out[b] = (bisect.bisect_right(starts, off[b] + n[b] - 1) - bisect.bisect_right(starts, off[b])) + 1
+    return out

@@ -5,9 +5,11 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from mla_latent_kv_05_amd import mla
+from tests.helpers import split_page_ranges, touched_parts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -32,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_layout_matches_header():
-    # 18 int32/float fields + one uint32 flags field, no padding
-    assert ctypes.sizeof(mla.Params) == 19 * 4
+    # 18 int32/float fields, one uint32 flags field, num_parts; no padding
+    assert ctypes.sizeof(mla.Params) == 20 * 4
 
 
 def v3(**kw):
@@ -59,6 +61,7 @@ def test_valid_params_pass():
     ("num_splits", 0, 4), ("num_splits", 5000, 4), ("split_pages", 0, 4), ("scale", 0.0, 2),
     ("scale", float("inf"), 2), ("q_dtype", 2, 3), ("w_dtype", 7, 3), ("kv_dtype", 3, 3),
     ("pe_dtype", 2, 3), ("latent_dtype", 2, 3), ("out_dtype", -1, 3), ("flags", 4, 2),
+    ("num_parts", -1, 4), ("num_parts", 1 << 21, 4),
 ])
 def test_invalid_params_rejected(field, value, status):
     p = v3()
@@ -112,17 +115,46 @@ def test_kernel_dispatch_names():
     assert mla.decode_kernel_name(v3(H=8)) == "generic_f32"       # 8 heads: not a multiple of 16
 
 
-@pytest.mark.parametrize("B,lens_max,total,min_splits", [
-    (64, 8192, 294912, 1), (4, 131072, 524288, 32), (1, 4096, 4096, 1), (128, 16384, 1310720, 1),
-    (3, 70, 150, 1),
+@pytest.mark.parametrize("B,lo,hi,Sq,min_splits,seed", [
+    (64, 1024, 8192, 1, 1, 1),        # the B=64 decode workload's length mix
+    (4, 131072, 131072, 1, 32, 2),    # four long sequences, >= 32 splits each
+    (1, 4096, 4096, 1, 1, 3),
+    (128, 4096, 16384, 4, 1, 4),      # Sq = 4: eight row groups per part
+    (3, 1, 70, 1, 1, 5),
+    (200, 0, 300, 1, 1, 6),           # many short sequences, some empty
+    (7, 0, 0, 1, 1, 7),               # nothing to attend to
 ])
-def test_planner_covers_every_page(B, lens_max, total, min_splits):
-    max_pages = -(-lens_max // 64)
-    p = mla.make_params(B, 1, 128, 128, 512, 64, num_pages=max(1, -(-total // 64)), max_pages=max_pages)
-    q = mla.plan_splits(p, lens_max, total, num_cus=256, min_splits=min_splits)
-    assert q.num_splits * q.split_pages >= max_pages
-    assert -(-max_pages // q.split_pages) >= min(min_splits, max_pages)
+def test_balanced_plan(B, lo, hi, Sq, min_splits, seed):
+    """The planner's balanced split plan: every sequence fits its slots, its splits
+    tile its pages in order, parts differ by at most one page, and one round of
+    workgroups fills the compute units."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, size=B, endpoint=True)
+    n = (lens + 63) // 64
+    max_pages = max(1, int(n.max()))
+    p = mla.make_params(B, Sq, 128, 128, 512, 64, num_pages=max(1, int(n.sum())), max_pages=max_pages)
+    q = mla.plan_splits(p, int(lens.max()), int(lens.sum()), num_cus=256, min_splits=min_splits)
     assert status_of(q) == 0
+    assert q.num_parts >= 1
+    n_rg = Sq * 128 // 64                           # workgroups per part
+    assert q.num_parts * n_rg <= 256 or q.num_parts <= min_splits
+    assert max(1, int(touched_parts(lens, q.num_parts).max())) <= q.num_splits
+    beg, end = split_page_ranges(lens, q)          # asserts the slot bound as it goes
+    sizes = {}
+    T = int(n.sum())
+    for b in range(B):
+        covered = 0
+        for c in range(q.num_splits):
+            if end[b, c] > beg[b, c]:
+                assert beg[b, c] == covered, "splits of a sequence must tile its pages in order"
+                covered = int(end[b, c])
+        assert covered == n[b]
+    parts = [(j + 1) * T // q.num_parts - j * T // q.num_parts for j in range(q.num_parts)]
+    assert max(parts) - min(parts) <= 1
+    if T >= 8:
+        assert min(parts) >= 1
+    if min_splits > 1:
+        assert (touched_parts(lens, q.num_parts) >= min_splits).all()
 
 
 def test_generic_split_count_invariance_of_checks():

@@ -16,7 +16,8 @@ import torch
 from mla_latent_kv_05_amd import inputs as I
 from mla_latent_kv_05_amd import mla
 from oracle import oracle as O
-from tests.helpers import TOL, DeviceCase, assert_bf16_rounding, err_rms, params_for, sample_rows
+from tests.helpers import (TOL, DeviceCase, assert_bf16_rounding, err_rms, params_for, sample_rows,
+                           split_page_ranges)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +28,10 @@ def validate(case: I.Case):
     assert int(lens.min()) >= 0 and int(lens.max()) <= case.max_pages * 64
     for b in range(case.wl.B):
         n = -(-int(lens[b]) // 64)
+        if n == 0:
+            continue
         ids = case.block_table[b, :n]
-        assert int(ids.min(initial=0) if n == 0 else ids.min()) >= 0
-        assert n == 0 or int(ids.max()) < case.num_pages
+        assert int(ids.min()) >= 0 and int(ids.max()) < case.num_pages
 
 
 def note(msg):
@@ -76,9 +78,22 @@ def run_decode(case, p):
     mla.decode_splitkv(p, q_abs.cuda(), dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table,
                        dc.seq_lens, o_part, lse_part)
     torch.cuda.synchronize()
-    ref_o, ref_l = O.decode_splitkv(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
-                                    case.k_pe, case.block_table, case.seq_lens, S, p.split_pages)
+    beg, end = split_page_ranges(case.seq_lens.numpy(), p)
+    ref_o, ref_l = O.decode_page_ranges(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
+                                        case.k_pe, case.block_table, case.seq_lens, beg, end)
     return o_part.cpu().numpy(), lse_part.cpu().numpy(), ref_o, ref_l
+
+
+def check_partials(wl, o, l, ref_o, ref_l):
+    empty = ref_l == -np.inf
+    assert not np.isnan(l).any(), "an lse_part slot was left unwritten"
+    assert np.array_equal(l == -np.inf, empty), "empty splits differ"
+    full = ~empty
+    if full.any():
+        assert np.abs(l[full] - ref_l[full]).max() <= (1e-5 if wl.dtype == "f32" else 2e-3)
+        e = err_rms(o[full], ref_o[full])
+        note(f"  o_part err {e:.3e}")
+        assert e <= tol_of(wl)
 
 
 @pytest.mark.parametrize("wl_name,lens,split_pages,flags", [
@@ -100,13 +115,30 @@ def test_decode_splitkv(wl_name, lens, split_pages, flags):
     note(f"decode_splitkv {wl_name} lens={lens} sp={split_pages} S={p.num_splits} "
          f"kernel={mla.decode_kernel_name(p)}")
     o, l, ref_o, ref_l = run_decode(case, p)
-    empty = ref_l == -np.inf
-    assert np.array_equal(l == -np.inf, empty), "empty splits differ"
-    full = ~empty
-    assert np.abs(l[full] - ref_l[full]).max() <= (1e-5 if wl.dtype == "f32" else 2e-3)
-    e = err_rms(o[full], ref_o[full])
-    note(f"  o_part err {e:.3e}")
-    assert e <= tol_of(wl)
+    check_partials(wl, o, l, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("wl_name,lens,num_parts,extra_slots,flags", [
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 1, 0, 0),          # one part: every sequence whole
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 3, 0, 0),
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 7, 2, 0),          # spare slots must read -inf
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 40, 0, 0),         # more parts than pages: empty parts
+    ("v3_b64", [0, 130, 0, 64, 0], 3, 1, 0),                 # empty sequences
+    ("v3_b64", [5000, 3, 2, 4100], 16, 0, 0),                # long sequences over many parts
+    ("v3_b64", [1, 63, 64, 65, 200, 700], 5, 0, mla.FLAG_GENERIC),
+    ("v3_sq4_fp8", [1, 2, 3, 4, 5, 66, 67, 500], 5, 0, 0),
+    ("v3_sq4_fp8", [4, 129, 700, 0], 3, 1, 0),
+    ("tiny", [5, 77, 128], 2, 0, 0),
+])
+def test_decode_balanced_splits(wl_name, lens, num_parts, extra_slots, flags):
+    wl = I.workload(wl_name, B=len(lens))
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, num_parts=num_parts, flags=flags)
+    p.num_splits += extra_slots
+    note(f"balanced {wl_name} lens={lens} P={num_parts} S={p.num_splits} kernel={mla.decode_kernel_name(p)}")
+    o, l, ref_o, ref_l = run_decode(case, p)
+    check_partials(wl, o, l, ref_o, ref_l)
 
 
 @pytest.mark.parametrize("wl_name,S", [("v3_b64", 7), ("tiny", 3), ("v3_sq4_fp8", 40)])
