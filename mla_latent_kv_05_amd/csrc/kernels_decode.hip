@@ -415,16 +415,16 @@ __device__ __forceinline__ void attend_segment(
     const int S = p.num_splits;
 
     seq_len = __builtin_amdgcn_readfirstlane(seq_len);              // wave-uniform scalars
-    const int t_begin = seg.pa * kPage;                            // page aligned
-    const int t_end = min(seg.pb * kPage, seq_len);                // one past the last stored token
+    const int t_begin = __builtin_amdgcn_readfirstlane(seg.pa * kPage);                 // page aligned
+    const int t_end = __builtin_amdgcn_readfirstlane(min(seg.pb * kPage, seq_len));     // past the last stored token
     const int row0 = rg * kRows + (wave >> 1) * 32;    // first (s,h) row of this wave pair
     const int s = row0 / p.H;
     const int h = row0 % p.H + t32;                    // this lane's head
     const int64_t qrow = (static_cast<int64_t>(seg.b) * p.Sq + s) * p.H + h;
     const int n_vis = __builtin_amdgcn_readfirstlane(seq_len - p.Sq + 1 + s);   // positions these rows may see
     const int64_t out_row = qrow * S + seg.c;
-    const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;          // >= 1
-    const int last_valid = t_end - (t_begin + (n_tiles - 1) * kTile);   // stored rows of the last tile
+    const int n_tiles = __builtin_amdgcn_readfirstlane((t_end - t_begin + kTile - 1) / kTile);   // >= 1
+    const int last_valid = __builtin_amdgcn_readfirstlane(t_end - (t_begin + (n_tiles - 1) * kTile));  // rows of the last tile
     // earlier stores (a previous segment's partials) complete before the counted
     // waits on this segment's copies begin
     wait_vmcnt<0>();
@@ -440,9 +440,10 @@ __device__ __forceinline__ void attend_segment(
         qreg[ks] = *reinterpret_cast<const bf16x8 *>(src);
     }
     // the segment's pages, one per lane (refilled every 64 pages)
-    const int n_pages = seg.pb - seg.pa;
+    const int n_pages = __builtin_amdgcn_readfirstlane(seg.pb - seg.pa);
+    const int32_t *seg_bt = bt + __builtin_amdgcn_readfirstlane(seg.pa);
     int pl_base = 0;
-    int plist = lane < n_pages ? bt[seg.pa + lane] : 0;
+    int plist = seg_bt[min(lane, n_pages - 1)];
     // Consume the loads here: otherwise the compiler places their vmcnt
     // waits at the first use inside the tile loop, where (re-executed every
     // iteration) they would also wait for the tile copies in flight.
@@ -488,9 +489,13 @@ __device__ __forceinline__ void attend_segment(
     // physical page of tile t (pages are listed from the segment's first page)
     auto page_of = [&](int t) -> int64_t {
         const int k = t >> 1;
-        if (k - pl_base >= 64) {                       // next 64 pages (segments over 4096 tokens)
+        if (k - pl_base >= 64) {
+            // the next 64 pages (segments of more than 4096 tokens): a load and its
+            // wait in one statement, so that no wait for it lands on the common path
+            // (the wait also drains the copies in flight; this is rare)
             pl_base = k & ~63;
-            plist = pl_base + lane < n_pages ? bt[seg.pa + pl_base + lane] : 0;
+            const int32_t *src = seg_bt + min(pl_base + lane, n_pages - 1);
+            asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(plist) : "v"(src) : "memory");
         }
         return __builtin_amdgcn_readlane(plist, k - pl_base);
     };

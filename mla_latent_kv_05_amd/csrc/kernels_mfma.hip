@@ -1,9 +1,10 @@
-// bf16 MFMA kernels for the two per-head projections of absorbed-MLA decode at
-// the DeepSeek-V3 head shapes (d_h = 128, d_c = 512), gfx950 / CDNA4:
-// mla_absorb_q (q_abs = q_nope . W_UK) and mla_up_v (out = o_latent . W_UV^T).
-// Both are per-head batched GEMMs with a small row count (B*Sq), bound by
-// reading the weights; each wave streams a slice of one head's weight matrix
-// once and applies it to up to 64 rows on v_mfma_f32_16x16x32_bf16.
+// Kernels around the attention at the DeepSeek-V3 head shapes (d_h = 128,
+// d_c = 512), gfx950 / CDNA4: the two per-head projections mla_absorb_q
+// (q_abs = q_nope . W_UK) and mla_up_v (out = o_latent . W_UV^T), bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16), and the split merge mla_combine_lse.  The
+// projections are per-head batched GEMMs with a small row count (B*Sq), bound
+// by reading the weights: each wave reads a slice of one head's weight matrix
+// once, with all its loads in flight together, and applies it to every row.
 #include <hip/hip_runtime.h>
 
 #include "gfx950.h"
@@ -20,73 +21,93 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return cvt_p
 
 // ---------------------------------------------------------------------------
 // mla_absorb_q: q_abs[r, h, m] = sum_d q_nope[r, h, d] W_UK[h, d, m]
-// One wave per (head, 64-row chunk, 128-column quarter of d_c).
+// One wave per (head, 128-column quarter of d_c): the wave reads its 128 x 128
+// slice of W_UK[h] once, all loads in flight together, keeps it in registers
+// as MFMA operands and applies it to the rows 64 at a time.
 // D^T[m, r] = W^T[m, d] . q^T[d, r]: W rows are read 8 at a time (16 bytes
-// each) and transposed in registers into 8 A operands covering 128 columns.
+// each) and transposed in registers into 8 A operands; MFMA i of a k-step
+// covers columns col0 + i of the 16 lanes' column groups.
 // ---------------------------------------------------------------------------
 template <int kDh>
 __global__ __launch_bounds__(64) void absorb_mfma_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_nope, const uint16_t *__restrict__ W_UK,
     uint16_t *__restrict__ q_abs) {
+    constexpr int kKs = kDh / 32;                 // 32-deep k-steps
     const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
     const int R = p.B * p.Sq;
-    const int h = blockIdx.x % p.H;
-    const int rest = blockIdx.x / p.H;
-    const int cq = rest & 3;                      // 128-column quarter of d_c
-    const int r0 = (rest >> 2) * 64;              // first row of the chunk
-    const int col0 = cq * 128 + r16 * 8;          // this lane's 8 columns in A
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int h = blockIdx.x >> 2;
+    const int cq = blockIdx.x & 3;                // 128-column quarter of d_c
+    const int col0 = cq * 128 + r16 * 8;          // this lane's 8 columns
     const uint16_t *W = W_UK + static_cast<int64_t>(h) * kDh * kDc;
-#pragma unroll 1
-    for (int ks = 0; ks < kDh / 32; ++ks) {
-        u32x4 rows[8];
+    u32x4 rows[kKs][8];
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            rows[e] = *reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(ks * 32 + g * 8 + e) * kDc + col0);
-        bf16x8 bq[4];
+            rows[ks][e] = *reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(ks * 32 + g * 8 + e) * kDc + col0);
+    // the first row chunk's query loads go out with the weight loads
+    auto load_q = [&](int r0, bf16x8 (&bq)[kKs][4]) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int r = r0 + rt * 16 + r16;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (r < R) v = *reinterpret_cast<const u32x4 *>(q_nope + (static_cast<int64_t>(r) * p.H + h) * kDh + ks * 32 + g * 8);
-            bq[rt] = as_bf16x8(v);
+            const uint16_t *src = q_nope + (static_cast<int64_t>(r < R ? r : 0) * p.H + h) * kDh + g * 8;
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+                u32x4 v = *reinterpret_cast<const u32x4 *>(src + ks * 32);
+                if (r >= R) v = u32x4{0u, 0u, 0u, 0u};
+                bq[ks][rt] = as_bf16x8(v);
+            }
         }
+    };
+    bf16x8 bq[kKs][4];
+    load_q(0, bq);
+    bf16x8 a[kKs][8];
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            u32x4 a;
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2)
-                a[k2] = (i & 1) ? pack_hi(rows[2 * k2][i >> 1], rows[2 * k2 + 1][i >> 1])
-                                : pack_lo(rows[2 * k2][i >> 1], rows[2 * k2 + 1][i >> 1]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[i][rt] = mfma16(as_bf16x8(a), bq[rt], acc[i][rt]);
-        }
-    }
-    // acc[i][rt][j]: row r0 + rt*16 + r16, column cq*128 + 8*(4g + j) + i
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int r = r0 + rt * 16 + r16;
-        if (r >= R) continue;
-        uint16_t *dst = q_abs + (static_cast<int64_t>(r) * p.H + h) * kDc + cq * 128;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
             u32x4 v;
 #pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) v[k2] = pack_bf16x2(acc[2 * k2][rt][j], acc[2 * k2 + 1][rt][j]);
-            *reinterpret_cast<u32x4 *>(dst + (g * 4 + j) * 8) = v;
+            for (int k2 = 0; k2 < 4; ++k2)
+                v[k2] = (i & 1) ? pack_hi(rows[ks][2 * k2][i >> 1], rows[ks][2 * k2 + 1][i >> 1])
+                                : pack_lo(rows[ks][2 * k2][i >> 1], rows[ks][2 * k2 + 1][i >> 1]);
+            a[ks][i] = as_bf16x8(v);
+        }
+    for (int r0 = 0; r0 < R; r0 += 64) {
+        f32x4 acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) acc[i][rt] = mfma16(a[ks][i], bq[ks][rt], acc[i][rt]);
+        if (r0 + 64 < R) load_q(r0 + 64, bq);          // next chunk, in flight under the stores
+        // acc[i][rt][j]: row r0 + rt*16 + r16, column cq*128 + 8*(4g + j) + i
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int r = r0 + rt * 16 + r16;
+            if (r >= R) continue;
+            uint16_t *dst = q_abs + (static_cast<int64_t>(r) * p.H + h) * kDc + cq * 128;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x4 v;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) v[k2] = pack_bf16x2(acc[2 * k2][rt][j], acc[2 * k2 + 1][rt][j]);
+                *reinterpret_cast<u32x4 *>(dst + (g * 4 + j) * 8) = v;
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // mla_up_v: out[r, h, d] = sum_m o_latent[r, h, m] W_UV[h, d, m]
-// One wave per (head, 64-row chunk, 32-row quarter of d_h... generalised to
-// d_h/4 rows): D^T[d, r] = W_UV[d, m] . o^T[m, r]; both operands are
-// contiguous along m, so no transpose is needed.
+// One wave per (head, 64-row chunk, quarter of the d_h output rows):
+// D^T[d, r] = W_UV[d, m] . o^T[m, r]; both operands are contiguous along m,
+// so no transpose is needed.
 // ---------------------------------------------------------------------------
 template <int kDh, bool kOutBf16>
 __global__ __launch_bounds__(64) void up_v_mfma_kernel(
@@ -149,6 +170,73 @@ __global__ __launch_bounds__(64) void up_v_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// mla_combine_lse at d_c = 512: one wave per (b,s,h) row, 8 latent columns per
+// lane, four rows per workgroup.  The lanes read the row's split log-sum-exps
+// 64 at a time; the weighted sum visits only the splits with weight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void combine_kernel_512(
+    const mla_params_t p, const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    void *__restrict__ o_latent, float *__restrict__ lse_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Sq * p.H;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int S = p.num_splits;
+    const float *l = lse_part + row * S;
+    float mx = -INFINITY;
+    for (int c0 = 0; c0 < S; c0 += 64) mx = fmaxf(mx, c0 + lane < S ? l[c0 + lane] : -INFINITY);
+    mx = wave_max_f(mx);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float sum = 0.f;
+    if (mx != -INFINITY) {
+        const float *op = o_part + row * static_cast<int64_t>(S) * kDc + lane * 8;
+        for (int c0 = 0; c0 < S; c0 += 64) {
+            const float lc = c0 + lane < S ? l[c0 + lane] : -INFINITY;
+            const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);
+            sum += w;
+            uint64_t live = __builtin_amdgcn_ballot_w64(w != 0.f);
+            while (live) {
+                const int k = __builtin_ctzll(live);
+                live &= live - 1;
+                const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), k));
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(op + static_cast<int64_t>(c0 + k) * kDc);
+                const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[j] += wk * v0[j];
+                    acc[4 + j] += wk * v1[j];
+                }
+            }
+        }
+        sum = wave_sum_f(sum);
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    if constexpr (kBf16Out) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[2 * k] * inv, acc[2 * k + 1] * inv);
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(o_latent) + row * kDc + lane * 8) = o;
+    } else {
+        f32x4 *dst = reinterpret_cast<f32x4 *>(static_cast<float *>(o_latent) + row * kDc + lane * 8);
+        dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]} * inv;
+        dst[1] = f32x4{acc[4], acc[5], acc[6], acc[7]} * inv;
+    }
+    if (lse_out && lane == 0) lse_out[row] = mx == -INFINITY ? -INFINITY : mx + __logf(sum);
+}
+
 }  // namespace
 
 bool absorb_mfma_supported(const mla_params_t &p) {
@@ -159,8 +247,7 @@ bool absorb_mfma_supported(const mla_params_t &p) {
 
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
                               void *q_abs, hipStream_t stream) {
-    const int64_t R = static_cast<int64_t>(p.B) * p.Sq;
-    const int64_t blocks = static_cast<int64_t>(p.H) * 4 * ((R + 63) / 64);
+    const int64_t blocks = static_cast<int64_t>(p.H) * 4;
     hipLaunchKernelGGL(absorb_mfma_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, p,
                        static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(W_UK),
                        static_cast<uint16_t *>(q_abs));
@@ -184,6 +271,24 @@ hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const v
     else
         hipLaunchKernelGGL((up_v_mfma_kernel<128, false>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
                            p, ol, w, out);
+    return hipGetLastError();
+}
+
+bool combine_fast_supported(const mla_params_t &p) {
+    if (p.flags & MLA_FLAG_GENERIC) return false;
+    return p.d_c == kDc && (p.latent_dtype == MLA_BF16 || p.latent_dtype == MLA_F32);
+}
+
+hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,
+                               void *o_latent, float *lse_out, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(p.B) * p.Sq * p.H;
+    const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
+    if (p.latent_dtype == MLA_BF16)
+        hipLaunchKernelGGL(combine_kernel_512<true>, dim3(blocks), dim3(256), 0, stream, p, o_part, lse_part,
+                           o_latent, lse_out);
+    else
+        hipLaunchKernelGGL(combine_kernel_512<false>, dim3(blocks), dim3(256), 0, stream, p, o_part, lse_part,
+                           o_latent, lse_out);
     return hipGetLastError();
 }
 

@@ -178,8 +178,10 @@ mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const f
     mla_status_t s = check(p);
     if (s != MLA_OK) return s;
     if (!o_part || !lse_part || !o_latent) return fail(MLA_ERR_NULL, "mla_combine_lse: NULL tensor pointer");
-    return hip_status(mla::launch_combine(*p, o_part, lse_part, o_latent, lse_out, static_cast<hipStream_t>(stream)),
-                      "mla_combine_lse launch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mla::combine_fast_supported(*p))
+        return hip_status(mla::launch_combine_fast(*p, o_part, lse_part, o_latent, lse_out, st), "mla_combine_lse launch");
+    return hip_status(mla::launch_combine(*p, o_part, lse_part, o_latent, lse_out, st), "mla_combine_lse launch");
 }
 
 mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W_UV, void *out,

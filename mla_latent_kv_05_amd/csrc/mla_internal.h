@@ -22,7 +22,7 @@ hipError_t launch_up_v_generic(const mla_params_t &p, const void *o_latent, cons
 hipError_t launch_combine(const mla_params_t &p, const float *o_part, const float *lse_part,
                           void *o_latent, float *lse_out, hipStream_t stream);
 
-// bf16 MFMA kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip)
+// kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip, kernels_decode.hip)
 bool decode_mfma_supported(const mla_params_t &p);
 hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const void *q_rope,
                               const void *c_kv, const void *k_pe, const float *kv_scale,
@@ -32,6 +32,9 @@ bool absorb_mfma_supported(const mla_params_t &p);
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
                               void *q_abs, hipStream_t stream);
 bool up_v_mfma_supported(const mla_params_t &p);
+bool combine_fast_supported(const mla_params_t &p);
+hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,
+                               void *o_latent, float *lse_out, hipStream_t stream);
 hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,
                             void *out, hipStream_t stream);
 
