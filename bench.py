@@ -25,6 +25,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+# rocprofv3 counter summary of the attention kernel on this workload (FETCH_SIZE /
+# WRITE_SIZE in KiB per dispatch) and the hash of the kernel source it was taken on
+COUNTERS = os.path.join(ROOT, "profiles", "decode_mfma_bf16_v3_b64_counters.txt")
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc", "kernels_decode.hip")
+FETCH_SCALE = 2.0              # FETCH_SIZE reads as half the bytes of a 256 MiB device copy
+WRITE_SCALE = 1.0              # WRITE_SIZE reads exactly
 
 
 def parse():
@@ -155,7 +161,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "launch_us": round(dec_avg_ms * 1e3, 2),
             "bytes_per_launch": cost.decode_bytes,
             "mfma_tflops": round(cost.decode_flops / (dec_avg_ms * 1e-3) / 1e12, 1),
@@ -166,6 +172,23 @@ def main():
         "wall_s": round(wall, 3),
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, scaled by
+    the copy-kernel calibration; None when the summary is missing, for another
+    workload, or was taken on a different version of the kernel source."""
+    import hashlib
+    try:
+        kv = dict(l.split("=", 1) for l in open(COUNTERS).read().split("\n") if "=" in l and not l.startswith("#"))
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256", "").strip() != src or kv.get("workload", "").strip() != workload:
+        return None
+    fetch = float(kv["fetch_size_kib"]) * 1024 * FETCH_SCALE
+    write = float(kv["write_size_kib"]) * 1024 * WRITE_SCALE
+    return round(fetch + write)
 
 
 def cpu_baseline(case, budget_s):
