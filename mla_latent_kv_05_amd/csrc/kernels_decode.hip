@@ -34,7 +34,7 @@
 //               tile i while the partner's partial scores of tile i+1 land in
 //               LDS.  Tiles are copied global->LDS by buffer_load ... lds (no
 //               VGPR staging) into a ring (bf16: 4 stages, copies issued 3
-//               tiles ahead, spread over the score MFMAs).  The 16-byte chunks
+//               tiles ahead, one instruction per odd score MFMA).  The 16-byte chunks
 //               of each latent row are XOR-swizzled with (row % 16), which
 //               keeps both the K-operand reads (16 rows, one column) and the
 //               transposing V reads (4 rows x 64 bytes per 16 lanes) free of
@@ -263,8 +263,8 @@ __device__ __forceinline__ u32x4 k_operand(const uint32_t *kb, const uint32_t *k
 }
 
 // Partial scores of one tile over this wave's half of the 576 dims (one MFMA
-// chain of 18 steps; K operands read 8 steps ahead), with copy(part) for a
-// later tile after steps 1, 5, 9 and fill(k) after every MFMA.
+// chain of 18 steps; K operands read 8 steps ahead), with copy(part) of a
+// later tile's part (k-1)/2 after every odd step k and fill(k) after every MFMA.
 //   tsc (fp8): per-D-element token scales, multiplied in before the RoPE term
 template <int KH, bool kFp8, typename Copy, typename Fill>
 __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t *kp, const bf16x8 *qreg,
@@ -287,7 +287,7 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
         }                                                                              \
         acc = mfma32(as_bf16x8(a[k]), qreg[k], acc);                                   \
         if constexpr ((k) + kReadAhead < kSteps) a[(k) + kReadAhead] = k_operand<KH, (k) + kReadAhead>(kb, kp); \
-        if constexpr ((k) == 1 || (k) == 5 || (k) == 9) copy((k) / 4);                  \
+        if constexpr ((k) & 1) copy((k) >> 1);                                         \
         fill(k);                                                                       \
         pin();                                                                         \
     }
@@ -301,6 +301,105 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
         for (int j = 0; j < 16; ++j) acc[j] *= tsc[j];
     }
     return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Steady-state phases with reads issued one phase ahead (cross-phase pipeline).
+// Per tile, a wave's LDS operations are issued in this order:
+//   score phase: K reads R0..R17 (8 ahead); in slots 10..17 also the transposing
+//                reads T0..T15 of the first latent k-step (two per slot)
+//   exchange writes W0..W3
+//   first latent k-step: slot b waits for T(2b, 2b+1) and issues U(2b, 2b+1), the
+//                reads of the second k-step
+//   barrier (after W3 completed), exchange reads X0..X3
+//   second latent k-step: waits for U, then X
+// LDS operations complete in issue order, so each counted wait below is the
+// number of younger operations issued before it (capped at 15, which only
+// makes the wait stricter).
+// ---------------------------------------------------------------------------
+// transposing reads of column block blk (halves lo / hi) of k-step kq
+#define MLA_TR_PAIR(kq, blk, lo, hi, base, vx)                                                         \
+    lo = lds_read_tr16<(kq) * 16 * kCkvRow + ((blk) >> 2) * 256>((base) + (vx)[(blk) & 3]);            \
+    hi = lds_read_tr16<(kq) * 16 * kCkvRow + ((blk) >> 2) * 256>((base) + (vx)[4 + ((blk) & 3)]);
+
+__device__ __forceinline__ bf16x8 tr_operand(const v4i16 &lo, const v4i16 &hi) {
+    return __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// Score phase with the first latent k-step's reads (of the tile at vbase) in slots 10..17.
+template <int KH, bool kFp8, typename Copy, typename Fill>
+__device__ __forceinline__ f32x16 score_tile_ahead(const uint32_t *kb, const uint32_t *kp, const bf16x8 *qreg,
+                                                   const float *tsc, Copy &&copy, Fill &&fill, uint32_t vbase,
+                                                   const uint32_t *vx, v4i16 *tlo, v4i16 *thi) {
+    constexpr int kContent = KH == 0 ? kSteps : 14;
+    u32x4 a[kSteps];
+    f32x16 acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#define MLA_KREAD(k) a[k] = k_operand<KH, k>(kb, kp);
+    MLA_KREAD(0) MLA_KREAD(1) MLA_KREAD(2) MLA_KREAD(3) MLA_KREAD(4) MLA_KREAD(5) MLA_KREAD(6) MLA_KREAD(7)
+    pin();
+    // slot k waits for R(k): younger are R(k+1..min(k+7,17)) and the T pairs of slots 10..k-1
+#define MLA_KSTEP(k)                                                                   \
+    {                                                                                  \
+        constexpr int younger = (k) <= 10 ? 7 : (k) - 3;                               \
+        wait_lgkm_tied<younger>(a[k]);                                                 \
+        if constexpr (kFp8 && (k) == kContent) {                                       \
+            for (int j = 0; j < 16; ++j) acc[j] *= tsc[j];                              \
+        }                                                                              \
+        acc = mfma32(as_bf16x8(a[k]), qreg[k], acc);                                   \
+        if constexpr ((k) + kReadAhead < kSteps) a[(k) + kReadAhead] = k_operand<KH, (k) + kReadAhead>(kb, kp); \
+        if constexpr ((k) >= 10) { MLA_TR_PAIR(0, (k) - 10, tlo[(k) - 10], thi[(k) - 10], vbase, vx) } \
+        if constexpr ((k) & 1) copy((k) >> 1);                                         \
+        fill(k);                                                                       \
+        pin();                                                                         \
+    }
+    MLA_KSTEP(0) MLA_KSTEP(1) MLA_KSTEP(2) MLA_KSTEP(3) MLA_KSTEP(4) MLA_KSTEP(5)
+    MLA_KSTEP(6) MLA_KSTEP(7) MLA_KSTEP(8) MLA_KSTEP(9) MLA_KSTEP(10) MLA_KSTEP(11)
+    MLA_KSTEP(12) MLA_KSTEP(13) MLA_KSTEP(14) MLA_KSTEP(15) MLA_KSTEP(16) MLA_KSTEP(17)
+#undef MLA_KSTEP
+#undef MLA_KREAD
+    if constexpr (kFp8 && KH == 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] *= tsc[j];
+    }
+    return acc;
+}
+
+// First latent k-step on the reads T issued in the score phase (the four exchange
+// writes follow them); slot b issues the reads U of the second k-step.  Each slot
+// has 18 younger operations (T after the pair, W, U so far): lgkmcnt(15).
+__device__ __forceinline__ void latent_first(const v4i16 *tlo, const v4i16 *thi, bf16x8 pb, f32x16 *oacc,
+                                             uint32_t vbase, const uint32_t *vx, v4i16 *ulo, v4i16 *uhi) {
+#define MLA_B1(blk)                                                                    \
+    {                                                                                  \
+        v4i16 lo = tlo[blk], hi = thi[blk];                                            \
+        wait_lgkm_tied2<15>(lo, hi);                                                   \
+        oacc[blk] = mfma32(tr_operand(lo, hi), pb, oacc[blk]);                         \
+        MLA_TR_PAIR(1, blk, ulo[blk], uhi[blk], vbase, vx)                             \
+        pin();                                                                         \
+    }
+    MLA_B1(0) MLA_B1(1) MLA_B1(2) MLA_B1(3) MLA_B1(4) MLA_B1(5) MLA_B1(6) MLA_B1(7)
+#undef MLA_B1
+}
+
+// Second latent k-step on the reads U, with the exchange reads X0..X3 issued after
+// them: slots 0..3 wait for their U pair (younger: later U pairs and X), slot 4
+// waits for everything (then X has landed too); fill(b) runs after MFMA b.
+template <typename Fill>
+__device__ __forceinline__ void latent_second(const v4i16 *ulo, const v4i16 *uhi, bf16x8 pb, f32x16 *oacc,
+                                              u32x4 *xr, Fill &&fill) {
+#define MLA_B2(blk, n)                                                                 \
+    {                                                                                  \
+        v4i16 lo = ulo[blk], hi = uhi[blk];                                            \
+        wait_lgkm_tied2<n>(lo, hi);                                                    \
+        if constexpr ((blk) == 4) wait_lgkm_tied4<0>(xr[0], xr[1], xr[2], xr[3]);      \
+        oacc[blk] = mfma32(tr_operand(lo, hi), pb, oacc[blk]);                         \
+        fill(blk);                                                                     \
+        pin();                                                                         \
+    }
+    MLA_B2(0, 15) MLA_B2(1, 15) MLA_B2(2, 14) MLA_B2(3, 12) MLA_B2(4, 0) MLA_B2(5, 0) MLA_B2(6, 0) MLA_B2(7, 0)
+#undef MLA_B2
 }
 
 // ---------------------------------------------------------------------------
@@ -509,31 +608,31 @@ __device__ __forceinline__ void attend_segment(
         const uint32_t base = stage_of(t);
         const uint32_t live = real ? ~0u : 0u;
         if constexpr (!kFp8) {
-            const char *src = static_cast<const char *>(c_kv) + crow0 * kCkvRow;
-            const uint32_t l0 = base + wave * 8 * kCkvRow, s0 = wave * 8 * kCkvRow;
-            if (part == 0) dma_rows3(src, kTileCkv & live, l0, s0, vd[0], vd[1], vd[2]);
-            else if (part == 1) dma_rows3(src, kTileCkv & live, l0 + 3 * kCkvRow, s0 + 3 * kCkvRow, vd[3], vd[4], vd[5]);
-            else {
-                dma_rows2(src, kTileCkv & live, l0 + 6 * kCkvRow, s0 + 6 * kCkvRow, vd[6], vd[7]);
+            // parts 0..7: latent row wave*8 + part; part 8: the wave's 8 RoPE-key rows
+            if (part < 8) {
+                const uint32_t r = wave * 8 + part;
+                dma_x4(static_cast<const char *>(c_kv) + crow0 * kCkvRow, kTileCkv & live, base + r * kCkvRow,
+                       r * kCkvRow, vd[part]);
+            } else {
                 dma_x4(k_pe + crow0 * kDr, kTileKpe & live, base + kTileCkv + wave * 1024, 0, voff_kpe);
             }
         } else {
-            const char *src = static_cast<const char *>(c_kv) + crow0 * kDc;
-            if (part == 0) dma_kib2(src, kRawCkv & live, base + wave * 4096, wave * 4096, lane * 16);
-            else if (part == 1) dma_kib2(src, kRawCkv & live, base + wave * 4096 + 2048, wave * 4096 + 2048, lane * 16);
-            else {
+            // parts 0..3: one KiB of the wave's 4 KiB of codes; 4: RoPE keys; 5: scales
+            if (part < 4) {
+                const uint32_t o = wave * 4096 + part * 1024;
+                dma_x4(static_cast<const char *>(c_kv) + crow0 * kDc, kRawCkv & live, base + o, o, lane * 16);
+            } else if (part == 4) {
                 dma_x4(k_pe + crow0 * kDr, kTileKpe & live, base + kRawCkv + wave * 1024, 0, voff_kpe);
-                if (lane < 8)
-                    dma_x1(kv_scale + crow0, (kTile * 4) & live, base + kRawCkv + kTileKpe + wave * 32, wave * 32, lane * 4);
+            } else if (lane < 8) {
+                dma_x1(kv_scale + crow0, (kTile * 4) & live, base + kRawCkv + kTileKpe + wave * 32, wave * 32, lane * 4);
             }
         }
     };
     auto issue_tile = [&](int t) {
         const bool real = t < n_tiles;
         const int64_t phys = real ? page_of(t) : 0;
-        copy_part(t, phys, 0, real);
-        copy_part(t, phys, 1, real);
-        copy_part(t, phys, 2, real);
+#pragma unroll
+        for (int part = 0; part < kLoads; ++part) copy_part(t, phys, part, real);
     };
 
     // make tile t (just landed) ready for the MFMAs: fp8 -> bf16 conversion, or (bf16)
@@ -592,6 +691,16 @@ __device__ __forceinline__ void attend_segment(
 #pragma unroll
         for (int r = 0; r < 4; ++r) kp[r] = kpe + kpx[r];
         return score_tile<KH, kFp8>(kb, kp, qreg, tsc, copy, fill);
+    };
+    auto partial_scores_ahead = [&](int t, const float *tsc, auto &&copy, auto &&fill, uint32_t vbase,
+                                    v4i16 *tlo, v4i16 *thi) -> f32x16 {
+        uint32_t kb[8], kp[4];
+        const uint32_t ckv = ckv_of(t), kpe = kpe_of(t);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kb[u] = ckv + kx[u];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kp[r] = kpe + kpx[r];
+        return score_tile_ahead<KH, kFp8>(kb, kp, qreg, tsc, copy, fill, vbase, vx, tlo, thi);
     };
 
     // partial scores are swapped with the other wave of the pair through LDS: four
@@ -730,25 +839,32 @@ __device__ __forceinline__ void attend_segment(
         const int t_copy = i + kAhead;
         const bool copy_real = t_copy < n_tiles;
         const int64_t phys = copy_real ? page_of(t_copy) : 0;
-        auto copy = [&](int part) { copy_part(t_copy, phys, part, copy_real); };
-        // score MFMAs of tile i+1, with the weights of tile i under them
+        auto copy = [&](int part) {
+            if (part < kLoads) copy_part(t_copy, phys, part, copy_real);
+        };
+        // score MFMAs of tile i+1, with the weights of tile i under them and the
+        // first latent k-step's reads of tile i in the last slots
         float pw[16];
         uint32_t pk[8];
         const float m_cur = m_use;
-        own = partial_scores(i + 1, tsc_next, copy, [&](int k) {
-            if (k < 16) weight_piece(k, m_cur, tsc_cur, pw, pk);
-        });
-        exchange_write(own);
-        // latent MFMAs of tile i: first k-step
         const uint32_t vbase = ckv_of(i);
-        latent_step<0>(vbase, vx, as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]}), oacc, no_fill);
-        barrier_lds();                                 // partner's partial scores of tile i+1 written
+        v4i16 tlo[8], thi[8], ulo[8], uhi[8];
+        own = partial_scores_ahead(i + 1, tsc_next, copy, [&](int k) {
+            if (k < 16) weight_piece(k, m_cur, tsc_cur, pw, pk);
+        }, vbase, tlo, thi);
+        exchange_write(own);
+        // latent MFMAs of tile i, first k-step (issuing the second k-step's reads)
+        latent_first(tlo, thi, as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]}), oacc, vbase, vx, ulo, uhi);
+        // the exchange writes have completed (15 younger reads at most): partner may read
+        asm volatile("s_waitcnt lgkmcnt(15)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         exchange_read();
-        // second k-step, with the full scores and maximum of tile i+1 under it (the
-        // four exchange reads precede the 16 transposing reads: lgkmcnt(14) covers them)
-        latent_step<1>(vbase, vx, as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]}), oacc, [&](int blk) {
-            if (blk == 0) wait_lgkm_tied4<14>(xr[0], xr[1], xr[2], xr[3]);
-            if (blk < 5) max_piece(i + 1, own, blk);
+        // second k-step, with the full scores and maximum of tile i+1 under its last MFMAs
+        latent_second(ulo, uhi, as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]}), oacc, xr, [&](int blk) {
+            if (blk == 4) { max_piece(i + 1, own, 0); max_piece(i + 1, own, 1); }
+            if (blk == 5) { max_piece(i + 1, own, 2); max_piece(i + 1, own, 3); }
+            if (blk == 6) max_piece(i + 1, own, 4);
         });
         m_use = max_finish();
         if (i + 2 < n_tiles) {                         // tile i+2 landed; later copies in flight
