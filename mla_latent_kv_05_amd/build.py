@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["mla_api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip"]
+SOURCES = ["mla_api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
+           "kernels_decode8.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -66,24 +66,19 @@ __device__ __forceinline__ uint32_t hi32(const void *p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) >> 32));
 }
 
-// three / two rows of 1 KiB: global soff, soff+1024, ...; LDS l, l+1024, ...; row j's lane offset v<j>
-__device__ __forceinline__ void dma_rows3(const void *base, uint32_t bytes, uint32_t l, uint32_t soff,
-                                          uint32_t v0, uint32_t v1, uint32_t v2) {
-    asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v0) MLA_DMA_STEP(1024, 1024) MLA_DMA_X4(v1) MLA_DMA_STEP(1024, 1024)
-                 MLA_DMA_X4(v2)
-                 :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2)
-                 : MLA_DMA_CLOBBERS);
-}
+// two / four rows of 1 KiB: global soff, soff+1024, ...; LDS l, l+1024, ...; row j's lane offset v<j>
 __device__ __forceinline__ void dma_rows2(const void *base, uint32_t bytes, uint32_t l, uint32_t soff,
                                           uint32_t v0, uint32_t v1) {
     asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v0) MLA_DMA_STEP(1024, 1024) MLA_DMA_X4(v1)
                  :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1)
                  : MLA_DMA_CLOBBERS);
 }
-// 4 / 2 consecutive KiB with the same lane offsets
-__device__ __forceinline__ void dma_kib2(const void *base, uint32_t bytes, uint32_t l, uint32_t soff, uint32_t v) {
-    asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v) MLA_DMA_STEP(1024, 1024) MLA_DMA_X4(v)
-                 :: MLA_DMA_BASE(base, bytes, l, soff), [v] "v"(v)
+// four rows of 1 KiB
+__device__ __forceinline__ void dma_rows4(const void *base, uint32_t bytes, uint32_t l, uint32_t soff,
+                                          uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+    asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v0) MLA_DMA_STEP(1024, 1024) MLA_DMA_X4(v1) MLA_DMA_STEP(1024, 1024)
+                 MLA_DMA_X4(v2) MLA_DMA_STEP(1024, 1024) MLA_DMA_X4(v3)
+                 :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3)
                  : MLA_DMA_CLOBBERS);
 }
 // one 16-byte-per-lane copy

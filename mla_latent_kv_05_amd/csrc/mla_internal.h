@@ -22,12 +22,18 @@ hipError_t launch_up_v_generic(const mla_params_t &p, const void *o_latent, cons
 hipError_t launch_combine(const mla_params_t &p, const float *o_part, const float *lse_part,
                           void *o_latent, float *lse_out, hipStream_t stream);
 
-// kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip, kernels_decode.hip)
+// kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip, kernels_decode.hip: both cache
+// dtypes)
 bool decode_mfma_supported(const mla_params_t &p);
 hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const void *q_rope,
                               const void *c_kv, const void *k_pe, const float *kv_scale,
                               const int32_t *block_table, const int32_t *seq_lens,
                               float *o_part, float *lse_part, hipStream_t stream);
+// bf16 cache: eight-wave attention kernel (kernels_decode8.hip)
+bool decode8_supported(const mla_params_t &p);
+hipError_t launch_decode8(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
+                          const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                          float *lse_part, hipStream_t stream);
 bool absorb_mfma_supported(const mla_params_t &p);
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
                               void *q_abs, hipStream_t stream);
