@@ -81,6 +81,15 @@ __device__ __forceinline__ void dma_rows4(const void *base, uint32_t bytes, uint
                  :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3)
                  : MLA_DMA_CLOBBERS);
 }
+// four 1 KiB pieces to consecutive LDS KiB from global offsets soff, soff+4096, ...
+// (four rows of 256 bytes each, of a tile whose rows are 1 KiB apart)
+__device__ __forceinline__ void dma_blk4(const void *base, uint32_t bytes, uint32_t l, uint32_t soff,
+                                         uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+    asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v0) MLA_DMA_STEP(1024, 4096) MLA_DMA_X4(v1) MLA_DMA_STEP(1024, 4096)
+                 MLA_DMA_X4(v2) MLA_DMA_STEP(1024, 4096) MLA_DMA_X4(v3)
+                 :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3)
+                 : MLA_DMA_CLOBBERS);
+}
 // one 16-byte-per-lane copy
 __device__ __forceinline__ void dma_x4(const void *base, uint32_t bytes, uint32_t l, uint32_t soff, uint32_t v) {
     asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v)

@@ -43,10 +43,14 @@ using namespace dec;
 
 constexpr int kThreads = 512;
 constexpr int kRows = kDecodeRowsPerBlock;              // 64 query rows: two head blocks of 32
+// LDS: the latent rows of tile t in stage t % 3, column-blocked: physical chunk p of
+// row r at (p / 16) * 8192 + r * 256 + (p % 16) * 16, so that latent wave v reads (as
+// V), and refills, block v alone; the RoPE rows of tile t in slot t % 3
 constexpr int kStages = 3;
-constexpr int kStage = kTileCkv + kTileKpe;             // 36864: latent rows, then RoPE rows
+constexpr int kBlock = kTile * 256;                     // one column block (16 chunks) of a tile
+constexpr int kOffRope = kStages * kTileCkv;            // 98304
 constexpr int kPartWave = 64 * 16 * 4;                  // one score wave's partial scores (fp32)
-constexpr int kOffPart = kStages * kStage;              // 110592
+constexpr int kOffPart = kOffRope + kStages * kTileKpe; // 110592
 constexpr int kOffP = kOffPart + 4 * kPartWave;         // 126976
 constexpr int kPBuf = 2 * 2 * 2 * 32 * 16;              // bf16 weights: [hb][k-step][g2][head] x 16 B
 constexpr int kOffAlpha = kOffP + 2 * kPBuf;            // 135168: rescale factors [buf][head][hb]
@@ -71,7 +75,7 @@ __device__ __forceinline__ u32x4 k_operand(const uint32_t *kb, const uint32_t *k
         return lds_read_b128<0>(kp[k - 14]);
     } else {
         constexpr int chunk = 2 * k + 36 * KH;
-        return lds_read_b128<(chunk & ~15) << 4>(kb[(chunk >> 1) & 7]);
+        return lds_read_b128<(chunk >> 4) * kBlock>(kb[(chunk >> 1) & 7]);
     }
 }
 
@@ -185,13 +189,14 @@ __device__ __forceinline__ void score_role(char *smem, const mla_params_t &p, co
     for (int ks = 0; ks < kSSteps; ++ks) asm volatile("" : "+v"(qreg[ks]));
 
     const uint32_t sm = lds_addr(smem);
-    // K operand: row perm_tok(t32); chunk column u holds logical chunk (2u + g2) ^ (row % 16)
+    // K operand: row perm_tok(t32); in each column block, chunk column u holds logical
+    // chunk (2u + g2) ^ (row % 16)
     const int krow = perm_tok(t32);
     uint32_t kx[8], kpx[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) kx[u] = krow * kCkvRow + ((((2 * u + g2) & 15) ^ (krow & 15)) << 4);
+    for (int u = 0; u < 8; ++u) kx[u] = krow * 256 + ((((2 * u + g2) & 15) ^ (krow & 15)) << 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kpx[r] = kTileCkv + krow * kKpeRow + (((2 * r + g2) ^ ((krow >> 1) & 7)) << 4);
+    for (int r = 0; r < 4; ++r) kpx[r] = krow * kKpeRow + (((2 * r + g2) ^ ((krow >> 1) & 7)) << 4);
     // partial scores: chunk q of lane l (D rows 8q + 4(l/32) ..) in slot
     // q*64 + (l & ~15) + ((l + 4(l/32) + 8(q/2)) % 16) of the wave's area
     auto pslot = [](int l, int q) -> uint32_t {
@@ -220,11 +225,12 @@ __device__ __forceinline__ void score_role(char *smem, const mla_params_t &p, co
     auto score_and_weights = [&](int t) {
         gen += 1;
         uint32_t kb[8], kp[4];
-        const uint32_t st = sm + (t % kStages) * kStage;
+        const uint32_t lst = sm + (t % kStages) * kTileCkv;
+        const uint32_t rst = sm + kOffRope + (t % kStages) * kTileKpe;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kb[u] = st + kx[u];
+        for (int u = 0; u < 8; ++u) kb[u] = lst + kx[u];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) kp[r] = st + kpx[r];
+        for (int r = 0; r < 4; ++r) kp[r] = rst + kpx[r];
         const f32x16 acc = score_tile<KH>(kb, kp, qreg);
         // publish the partial: plain stores (the compiler keeps the wait states an MFMA
         // result needs before a store reads it), then the flag once they completed
@@ -324,10 +330,16 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
     asm volatile("" : "+v"(plist));
 
     const uint32_t sm = lds_addr(smem);
-    // copies: latent rows 8v + r (logical chunk lane ^ (row % 16) lands in physical chunk lane),
+    // copies of block v: instruction m covers rows 4m .. 4m+3 (16 lanes per row); lane l
+    // lands in physical chunk 16v + l % 16 of row 4m + l / 16 and fetches logical chunk
+    // 16v + ((l % 16) ^ (row % 16)); the global lane offset depends on m % 4 only
+    uint32_t vo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r = 4 * m + (lane >> 4);
+        vo[m] = (lane >> 4) * kCkvRow + (16 * v + ((lane & 15) ^ (r & 15))) * 16;
+    }
     // RoPE rows 8v .. 8v+7 (8 lanes per row)
-    const uint32_t lane16 = lane << 4;
-    auto vd = [&](int r) -> uint32_t { return lane16 ^ (((8 * v + r) & 15) << 4); };
     const int kpe_r = 8 * v + (lane >> 3);
     const uint32_t voff_kpe = kpe_r * kKpeRow + (((lane & 7) ^ ((kpe_r >> 1) & 7)) << 4);
     // transposed V read of half h2 (tokens 8h2 ..), column block cb (latent 128v + 32cb ..):
@@ -339,19 +351,25 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
         for (int cb = 0; cb < 4; ++cb) {
             const int rv = 4 * ((lane & 15) >> 2) + 2 * h2 + g2;
             const int cl = 4 * cb + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-            vx[h2 * 4 + cb] = rv * kCkvRow + ((cl ^ (rv & 15)) << 4) + v * 256 + (lane & 1) * 8;
+            vx[h2 * 4 + cb] = v * kBlock + rv * 256 + ((cl ^ (rv & 15)) << 4) + (lane & 1) * 8;
         }
     // weights of k-step kq for B-operand lane (t32, g2): slot (2kq + g2)*32 + (t32 ^ 4(2kq + g2))
     const uint32_t pr0 = (g2 * 32 + (t32 ^ (4 * g2))) * 16;
     const uint32_t pr1 = ((2 + g2) * 32 + (t32 ^ (4 * (2 + g2)))) * 16;
     const uint32_t ar_off = t32 * 8;                   // rescale factors of head t32 in both blocks
 
-    auto stage_of = [&](int t) -> uint32_t { return sm + (t % kStages) * kStage; };
+    auto stage_of = [&](int t) -> uint32_t { return sm + (t % kStages) * kTileCkv; };
     auto page_of = [&](int t) -> int64_t { return __builtin_amdgcn_readlane(plist, (t >> 1) - pl_base); };
-    // Copies of tile t.  A tile past the segment's end (real = false) gets a
-    // zero-length buffer: its loads move no memory, so every iteration issues the
-    // same copies and the vmcnt accounting is the same in all of them.
-    auto issue_tile = [&](int t) {
+    // Copies of tile t into block v of its stage (two instructions of four) and RoPE
+    // rows 8v .. 8v+7 into its slot (one).  A tile past the segment's end (real =
+    // false) gets a zero-length buffer: its loads move no memory, so every iteration
+    // issues the same copies and the vmcnt accounting is the same in all of them.
+    struct TileSrc {
+        const char *ckv;
+        const uint16_t *kpe;
+        uint32_t ckv_bytes, kpe_bytes, st, rope;
+    };
+    auto tile_src = [&](int t) -> TileSrc {
         const bool real = t < n_tiles;
         if (real && (t >> 1) - pl_base >= 64) {
             // the next 64 pages: a load and its wait in one statement (the wait also
@@ -362,21 +380,28 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
         }
         const int64_t phys = real ? page_of(t) : 0;
         const int64_t crow0 = phys * kPage + (t & 1) * kTile;   // first cache row of the tile
-        const uint32_t st = stage_of(t);
-        const uint32_t r0 = 8 * v;
-        const char *src = c_kv + crow0 * kCkvRow;
-        const uint32_t bytes = real ? kTileCkv : 0u;
-        dma_rows4(src, bytes, st + r0 * kCkvRow, r0 * kCkvRow, vd(0), vd(1), vd(2), vd(3));
-        dma_rows4(src, bytes, st + (r0 + 4) * kCkvRow, (r0 + 4) * kCkvRow, vd(4), vd(5), vd(6), vd(7));
-        dma_x4(k_pe + crow0 * kDr, real ? kTileKpe : 0u, st + kTileCkv + v * 1024, 0, voff_kpe);
+        return TileSrc{c_kv + crow0 * kCkvRow, k_pe + crow0 * kDr, real ? kTileCkv : 0u, real ? kTileKpe : 0u,
+                       stage_of(t) + v * kBlock, sm + kOffRope + (t % kStages) * kTileKpe + v * 1024};
+    };
+    // part 0: rows 0..15, part 1: rows 16..31, part 2: RoPE rows
+    auto copy_part = [&](const TileSrc &ts, int part) {
+        if (part < 2)
+            dma_blk4(ts.ckv, ts.ckv_bytes, ts.st + part * 4096, part * 16 * kCkvRow, vo[0], vo[1], vo[2], vo[3]);
+        else
+            dma_x4(ts.kpe, ts.kpe_bytes, ts.rope, 0, voff_kpe);
+    };
+    auto issue_tile = [&](int t) {
+        const TileSrc ts = tile_src(t);
+        copy_part(ts, 0);
+        copy_part(ts, 1);
+        copy_part(ts, 2);
     };
     // rows past the sequence end in a partial last tile: zero, so that their (zero)
     // weights never meet stale values in the latent product
     auto zero_tail = [&](int t) {
-        const uint32_t st = stage_of(t);
-        for (int k = lane; k < (kTile - si.last_valid) * 16; k += 64)   // this wave's 16 chunks of each row
-            lds_store<u32x4>(st + (si.last_valid + (k >> 4)) * kCkvRow + (v * 16 + (k & 15)) * 16,
-                             u32x4{0u, 0u, 0u, 0u});
+        const uint32_t st = stage_of(t) + v * kBlock;  // this wave's block
+        for (int k = lane; k < (kTile - si.last_valid) * 16; k += 64)
+            lds_store<u32x4>(st + (si.last_valid + (k >> 4)) * 256 + (k & 15) * 16, u32x4{0u, 0u, 0u, 0u});
     };
 
     f32x16 oacc[2][4];                 // [hb][cb]: latent 128v + 32cb .., heads 32hb + t32
@@ -387,26 +412,32 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[hb][cb][e] = 0.f;
 
-    // latent update of tile t: 21 LDS reads (rescale factors, weights, transposed V),
-    // each MFMA group after a counted wait for its operands (capped at 15: stricter)
-    auto latent_tile = [&](int t) {
+    // latent update of tile t: 21 LDS reads (rescale factors, weights, transposed V of
+    // block v), all complete before the MFMAs, so that copy(g), run after MFMA group g,
+    // may refill block v of this stage
+    auto latent_tile = [&](int t, auto &&copy) {
         const uint32_t vb = stage_of(t);
         const uint32_t pb = sm + kOffP + (t & 1) * kPBuf;
         u32x2 al = lds_read_b64<0>(sm + kOffAlpha + (t & 1) * kABuf + ar_off);
         u32x4 pw00 = lds_read_b128<0>(pb + pr0), pw10 = lds_read_b128<2048>(pb + pr0);
+        u32x4 pw01 = lds_read_b128<0>(pb + pr1), pw11 = lds_read_b128<2048>(pb + pr1);
         v4i16 lo[2][4], hi[2][4];
 #define MLA_VR(kq)                                                                                     \
-        lo[kq][0] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[0]); hi[kq][0] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[4]); \
-        lo[kq][1] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[1]); hi[kq][1] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[5]); \
-        lo[kq][2] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[2]); hi[kq][2] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[6]); \
-        lo[kq][3] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[3]); hi[kq][3] = lds_read_tr16<(kq) * 16 * kCkvRow>(vb + vx[7]);
+        lo[kq][0] = lds_read_tr16<(kq) * 4096>(vb + vx[0]); hi[kq][0] = lds_read_tr16<(kq) * 4096>(vb + vx[4]); \
+        lo[kq][1] = lds_read_tr16<(kq) * 4096>(vb + vx[1]); hi[kq][1] = lds_read_tr16<(kq) * 4096>(vb + vx[5]); \
+        lo[kq][2] = lds_read_tr16<(kq) * 4096>(vb + vx[2]); hi[kq][2] = lds_read_tr16<(kq) * 4096>(vb + vx[6]); \
+        lo[kq][3] = lds_read_tr16<(kq) * 4096>(vb + vx[3]); hi[kq][3] = lds_read_tr16<(kq) * 4096>(vb + vx[7]);
         MLA_VR(0)
-        u32x4 pw01 = lds_read_b128<0>(pb + pr1), pw11 = lds_read_b128<2048>(pb + pr1);
         MLA_VR(1)
 #undef MLA_VR
-        pin();
-        // rescale (rare: the first tiles) once the factors are in
-        asm volatile("s_waitcnt lgkmcnt(15)" : "+v"(al) :: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(al), "+v"(pw00), "+v"(pw10), "+v"(pw01), "+v"(pw11), "+v"(lo[0][0]), "+v"(hi[0][0]),
+                       "+v"(lo[0][1]), "+v"(hi[0][1]), "+v"(lo[0][2]), "+v"(hi[0][2]), "+v"(lo[0][3]), "+v"(hi[0][3]),
+                       "+v"(lo[1][0]), "+v"(hi[1][0]), "+v"(lo[1][1]), "+v"(hi[1][1]), "+v"(lo[1][2]), "+v"(hi[1][2]),
+                       "+v"(lo[1][3]), "+v"(hi[1][3])
+                     :
+                     : "memory");
+        // rescale (rare: the first tiles)
         {
             const float a0 = __uint_as_float(al[0]), a1 = __uint_as_float(al[1]);
             if (__builtin_amdgcn_ballot_w64(a0 != 1.f || a1 != 1.f)) {
@@ -418,35 +449,39 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
             }
         }
         pin();
-        // ops in issue order: al 0, pw00 1, pw10 2, V(kq0, cb) 3+2cb, 4+2cb, pw01 11, pw11 12,
-        // V(kq1, cb) 13+2cb, 14+2cb; an MFMA group waits until at most 20 - (its last op) are younger
-#define MLA_PV(kq, cb, younger, p0, p1)                                                                  \
-        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[kq][cb]), "+v"(hi[kq][cb]), "+v"(p0), "+v"(p1) : "n"(younger) : "memory"); \
+#define MLA_PV(kq, cb, p0, p1)                                                                           \
         oacc[0][cb] = mfma32(tr_op(lo[kq][cb], hi[kq][cb]), as_bf16x8(p0), oacc[0][cb]);              \
         oacc[1][cb] = mfma32(tr_op(lo[kq][cb], hi[kq][cb]), as_bf16x8(p1), oacc[1][cb]);              \
+        copy((kq) * 4 + (cb));                                                                           \
         pin();
-        MLA_PV(0, 0, 15, pw00, pw10) MLA_PV(0, 1, 14, pw00, pw10) MLA_PV(0, 2, 12, pw00, pw10) MLA_PV(0, 3, 10, pw00, pw10)
-        MLA_PV(1, 0, 6, pw01, pw11) MLA_PV(1, 1, 4, pw01, pw11) MLA_PV(1, 2, 2, pw01, pw11) MLA_PV(1, 3, 0, pw01, pw11)
+        MLA_PV(0, 0, pw00, pw10) MLA_PV(0, 1, pw00, pw10) MLA_PV(0, 2, pw00, pw10) MLA_PV(0, 3, pw00, pw10)
+        MLA_PV(1, 0, pw01, pw11) MLA_PV(1, 1, pw01, pw11) MLA_PV(1, 2, pw01, pw11) MLA_PV(1, 3, pw01, pw11)
 #undef MLA_PV
     };
+    auto no_copy = [](int) {};
 
-    // prologue: copies of tiles 0 and 1; tile 0 lands (barrier); tile 1 lands and the
+    // prologue: copies of tiles 0, 1, 2; tile 0 lands (barrier); tile 1 lands and the
     // weights of tile 0 are out (barrier)
     issue_tile(0);
     issue_tile(1);
-    wait_vmcnt<kLoads>();
+    issue_tile(2);
+    wait_vmcnt<2 * kLoads>();                          // tile 0 landed
     barrier_lds();
     if (n_tiles == 1 && si.last_valid < kTile) zero_tail(0);
-    if (n_tiles > 1) wait_vmcnt<0>();
+    if (n_tiles > 1) wait_vmcnt<kLoads>();             // tile 1 landed
     barrier_lds();
     for (int i = 0; i + 1 < n_tiles; ++i) {
-        issue_tile(i + 2);                             // into the stage of tile i-1
-        latent_tile(i);
+        // latent update of tile i; block v of its stage takes tile i+3 once the V reads
+        // are in, the RoPE slot of tile i (last read in the previous iteration) too
+        const TileSrc ts = tile_src(i + 3);
+        latent_tile(i, [&](int g) {
+            if (g < 3) copy_part(ts, g);
+        });
         if (i + 2 == n_tiles && si.last_valid < kTile) zero_tail(i + 1);   // before its V reads
-        if (i + 2 < n_tiles) wait_vmcnt<0>();          // tile i+2 landed
+        if (i + 2 < n_tiles) wait_vmcnt<kLoads>();     // tile i+2 landed (tile i+3 in flight)
         barrier_lds();
     }
-    latent_tile(n_tiles - 1);
+    latent_tile(n_tiles - 1, no_copy);
     barrier_lds();                                     // the owners' 1 / sums are out
     const u32x2 inv = lds_load<u32x2>(sm + kOffFin + ar_off);
     // oacc[hb][cb][e]: head 32hb + t32, latent 128v + 32cb + 8*(e/4) + 4*g2 + e%4
