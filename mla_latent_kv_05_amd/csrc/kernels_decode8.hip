@@ -65,6 +65,14 @@ constexpr uint32_t kSpinLimit = 1u << 22;               // bound of the flag wai
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 static_assert(kRows == 64, "two head blocks of 32");
 
+// LDS reads in this kernel are plain loads: the compiler places the counted waits
+// before each use (it counts the LDS operations it issued; the asm LDS operations here
+// only make those waits stricter) and keeps the values in place until they land.
+__device__ __forceinline__ u32x4 ld128(uint32_t addr) { return lds_load<u32x4>(addr); }
+__device__ __forceinline__ v4i16 ld_tr16(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS_AS v4i16 *>(static_cast<uintptr_t>(addr)));
+}
+
 // K operand of score step k for half KH of the 576 dims:
 //   KH = 0: latent chunk 2k + g2 (dims 16k ..), k < 18
 //   KH = 1: latent chunk 2k + 36 + g2 (dims 288 + 16k ..) for k < 14, then RoPE chunk 2(k-14) + g2
@@ -72,16 +80,16 @@ static_assert(kRows == 64, "two head blocks of 32");
 template <int KH, int k>
 __device__ __forceinline__ u32x4 k_operand(const uint32_t *kb, const uint32_t *kp) {
     if constexpr (KH == 1 && k >= 14) {
-        return lds_read_b128<0>(kp[k - 14]);
+        return ld128(kp[k - 14]);
     } else {
         constexpr int chunk = 2 * k + 36 * KH;
-        return lds_read_b128<(chunk >> 4) * kBlock>(kb[(chunk >> 1) & 7]);
+        return ld128(kb[(chunk >> 1) & 7] + (chunk >> 4) * kBlock);
     }
 }
 
 // Partial scores S^T[token, head] of one tile over half KH of the dims: one MFMA
-// chain of 18 steps with the K operands read kKAhead steps ahead (the score wave
-// issues no other LDS operation meanwhile, so each counted wait is exact).
+// chain of 18 steps with the K operands read kKAhead steps ahead (the compiler's
+// counted waits keep them in flight).
 template <int KH>
 __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t *kp, const bf16x8 *qreg) {
     u32x4 a[kSSteps];
@@ -93,8 +101,6 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
     pin();
 #define MLA_KSTEP(k)                                                                   \
     {                                                                                  \
-        constexpr int younger = (kSSteps - 1 - (k)) < kKAhead - 1 ? (kSSteps - 1 - (k)) : kKAhead - 1; \
-        wait_lgkm_tied<younger>(a[k]);                                                 \
         acc = mfma32(as_bf16x8(a[k]), qreg[k], acc);                                   \
         if constexpr ((k) + kKAhead < kSSteps) MLA_KREAD((k) + kKAhead)                \
         pin();                                                                         \
@@ -107,12 +113,6 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
     return acc;
 }
 
-template <int kOff>
-__device__ __forceinline__ u32x2 lds_read_b64(uint32_t addr) {
-    u32x2 r;
-    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(kOff) : "memory");
-    return r;
-}
 
 __device__ __forceinline__ bf16x8 tr_op(const v4i16 &lo, const v4i16 &hi) {
     return __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -247,9 +247,8 @@ __device__ __forceinline__ void score_role(char *smem, const mla_params_t &p, co
             __builtin_amdgcn_s_sleep(1);
         }
         // both partials of the owned heads, in the owner layout
-        u32x4 x0 = lds_read_b128<0>(pr_addr), x1 = lds_read_b128<1024>(pr_addr);
-        u32x4 y0 = lds_read_b128<kPartWave>(pr_addr), y1 = lds_read_b128<kPartWave + 1024>(pr_addr);
-        wait_lgkm_tied4<0>(x0, x1, y0, y1);
+        const u32x4 x0 = ld128(pr_addr), x1 = ld128(pr_addr + 1024);
+        const u32x4 y0 = ld128(pr_addr + kPartWave), y1 = ld128(pr_addr + kPartWave + 1024);
         float sc[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -418,25 +417,20 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
     auto latent_tile = [&](int t, auto &&copy) {
         const uint32_t vb = stage_of(t);
         const uint32_t pb = sm + kOffP + (t & 1) * kPBuf;
-        u32x2 al = lds_read_b64<0>(sm + kOffAlpha + (t & 1) * kABuf + ar_off);
-        u32x4 pw00 = lds_read_b128<0>(pb + pr0), pw10 = lds_read_b128<2048>(pb + pr0);
-        u32x4 pw01 = lds_read_b128<0>(pb + pr1), pw11 = lds_read_b128<2048>(pb + pr1);
+        const u32x2 al = lds_load<u32x2>(sm + kOffAlpha + (t & 1) * kABuf + ar_off);
+        const u32x4 pw00 = ld128(pb + pr0), pw10 = ld128(pb + pr0 + 2048);
+        const u32x4 pw01 = ld128(pb + pr1), pw11 = ld128(pb + pr1 + 2048);
         v4i16 lo[2][4], hi[2][4];
 #define MLA_VR(kq)                                                                                     \
-        lo[kq][0] = lds_read_tr16<(kq) * 4096>(vb + vx[0]); hi[kq][0] = lds_read_tr16<(kq) * 4096>(vb + vx[4]); \
-        lo[kq][1] = lds_read_tr16<(kq) * 4096>(vb + vx[1]); hi[kq][1] = lds_read_tr16<(kq) * 4096>(vb + vx[5]); \
-        lo[kq][2] = lds_read_tr16<(kq) * 4096>(vb + vx[2]); hi[kq][2] = lds_read_tr16<(kq) * 4096>(vb + vx[6]); \
-        lo[kq][3] = lds_read_tr16<(kq) * 4096>(vb + vx[3]); hi[kq][3] = lds_read_tr16<(kq) * 4096>(vb + vx[7]);
+        lo[kq][0] = ld_tr16(vb + vx[0] + (kq) * 4096); hi[kq][0] = ld_tr16(vb + vx[4] + (kq) * 4096); \
+        lo[kq][1] = ld_tr16(vb + vx[1] + (kq) * 4096); hi[kq][1] = ld_tr16(vb + vx[5] + (kq) * 4096); \
+        lo[kq][2] = ld_tr16(vb + vx[2] + (kq) * 4096); hi[kq][2] = ld_tr16(vb + vx[6] + (kq) * 4096); \
+        lo[kq][3] = ld_tr16(vb + vx[3] + (kq) * 4096); hi[kq][3] = ld_tr16(vb + vx[7] + (kq) * 4096);
         MLA_VR(0)
         MLA_VR(1)
 #undef MLA_VR
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(al), "+v"(pw00), "+v"(pw10), "+v"(pw01), "+v"(pw11), "+v"(lo[0][0]), "+v"(hi[0][0]),
-                       "+v"(lo[0][1]), "+v"(hi[0][1]), "+v"(lo[0][2]), "+v"(hi[0][2]), "+v"(lo[0][3]), "+v"(hi[0][3]),
-                       "+v"(lo[1][0]), "+v"(hi[1][0]), "+v"(lo[1][1]), "+v"(hi[1][1]), "+v"(lo[1][2]), "+v"(hi[1][2]),
-                       "+v"(lo[1][3]), "+v"(hi[1][3])
-                     :
-                     : "memory");
+        // every read of block v has completed before copy() may refill it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // rescale (rare: the first tiles)
         {
             const float a0 = __uint_as_float(al[0]), a1 = __uint_as_float(al[1]);
