@@ -27,10 +27,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # rocprofv3 counter summary of the attention kernel on this workload (FETCH_SIZE /
 # WRITE_SIZE in KiB per dispatch) and the hash of the kernel source it was taken on
-COUNTERS = os.path.join(ROOT, "profiles", "decode_mfma_bf16_v3_b64_counters.txt")
-KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc", "kernels_decode.hip")
-FETCH_SCALE = 2.0              # FETCH_SIZE reads as half the bytes of a 256 MiB device copy
-WRITE_SCALE = 1.0              # WRITE_SIZE reads exactly
+COUNTERS = os.path.join(ROOT, "profiles", "decode8_bf16_v3_b64_counters.txt")
+# the sources of the attention kernel the counters were taken on
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc", f)
+               for f in ("kernels_decode8.hip", "decode_common.h", "gfx950.h")]
 
 
 def parse():
@@ -175,19 +175,22 @@ def main():
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter summary, scaled by
-    the copy-kernel calibration; None when the summary is missing, for another
-    workload, or was taken on a different version of the kernel source."""
+    """HBM bytes per attention launch from the committed counter summary, each counter
+    scaled by its reading for a device copy of known size in the same profiling run;
+    None when the summary is missing, for another workload, or was taken on a
+    different version of the kernel sources."""
     import hashlib
     try:
         kv = dict(l.split("=", 1) for l in open(COUNTERS).read().split("\n") if "=" in l and not l.startswith("#"))
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SRCS)).hexdigest()
     except OSError:
         return None
     if kv.get("kernel_source_sha256", "").strip() != src or kv.get("workload", "").strip() != workload:
         return None
-    fetch = float(kv["fetch_size_kib"]) * 1024 * FETCH_SCALE
-    write = float(kv["write_size_kib"]) * 1024 * WRITE_SCALE
+    # each counter scaled by what it reads for a device copy of known size in the same run
+    probe = float(kv["copy_probe_bytes"])
+    fetch = float(kv["fetch_size_kib"]) / float(kv["copy_probe_fetch_size_kib"]) * probe
+    write = float(kv["write_size_kib"]) / float(kv["copy_probe_write_size_kib"]) * probe
     return round(fetch + write)
 
 
