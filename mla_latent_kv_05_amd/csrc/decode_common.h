@@ -1,7 +1,7 @@
 // Device code shared by the two attention kernels (kernels_decode.hip,
 // kernels_decode8.hip): tile constants, the global->LDS copy instructions, the
-// LDS tile layout and its asm reads with counted waits, and the walk over the
-// segments of a work part.
+// LDS tile layout and its operand reads, and the walk over the segments of a
+// work part.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -119,39 +119,15 @@ __device__ __forceinline__ int perm_tok(int x) {
     return (x & 16) | ((x & 3) << 2) | (((x >> 3) & 1) << 1) | ((x >> 2) & 1);
 }
 
-// LDS reads issued as inline asm, each waited on by an explicit counted
-// lgkmcnt wait tied to its result.  LDS operations complete in issue order, so
-// any other LDS traffic in the window only makes a counted wait stricter; the
-// loop issues no scalar memory loads (which complete out of order).
-template <int kOff>
-__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(kOff) : "memory");
-    return r;
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm_tied(u32x4 &a) {
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N) : "memory");
-}
+// LDS operand reads are plain loads: the compiler places a counted lgkmcnt wait
+// before each use (LDS operations complete in issue order; it counts the ones it
+// issued, and LDS operations written as inline asm elsewhere only make those waits
+// stricter) and keeps each value in its registers until it has landed.
+__device__ __forceinline__ u32x4 ld128(uint32_t addr) { return lds_load<u32x4>(addr); }
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // receives element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3.
-template <int kOff>
-__device__ __forceinline__ v4i16 lds_read_tr16(uint32_t addr) {
-    v4i16 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(kOff) : "memory");
-    return r;
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm_tied2(v4i16 &a, v4i16 &b) {
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_lgkm_tied4(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d) {
-    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N) : "memory");
-}
-template <int kOff>
-__device__ __forceinline__ void lds_write_b128(uint32_t addr, u32x4 v) {
-    asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(kOff) : "memory");
+__device__ __forceinline__ v4i16 ld_tr16(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS_AS v4i16 *>(static_cast<uintptr_t>(addr)));
 }
 // Nothing moves across: the instruction order of a phase is the source order.
 __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }

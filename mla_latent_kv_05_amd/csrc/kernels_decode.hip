@@ -39,7 +39,7 @@
 //               keeps both the K-operand reads (16 rows, one column) and the
 //               transposing V reads (4 rows x 64 bytes per 16 lanes) free of
 //               bank conflicts.  The K operands are read 8 steps ahead of
-//               their MFMA, with explicit counted waits.
+//               their MFMA (the compiler places the counted waits).
 //   scores    = S^T[token, head] = K[token, k] . Q^T[k, head]: K from LDS
 //               (A operand), the query rows in registers (B operand).
 //   softmax   = online, in the exp2 domain; a head's 32 scores of a tile sit
@@ -86,29 +86,27 @@ static_assert(kRows == 64, "four waves of 32 heads in pairs");
 
 // O^T[256 latent columns of this wave, 32 heads] += V^T[., 16 tokens] P^T[16 tokens, heads]
 // for one 16-token k-step kq of a tile: 16 transposing reads, then per column
-// block a counted wait, the MFMA and fill(blk) (VALU work slotted under the
-// MFMAs).  vx[h*4 + b4]: lane address of the transposing read of half h
-// (tokens 8h..) for column blocks blk = b4, b4+4.  LDS operations issued
-// before the call and still in flight only make the waits stricter.
+// block the MFMA and fill(blk) (VALU work slotted under the MFMAs).  vx[h*4 +
+// b4]: lane address of the transposing read of half h (tokens 8h..) for column
+// blocks blk = b4, b4+4.
 template <int kq, typename Fill>
 __device__ __forceinline__ void latent_step(uint32_t base, const uint32_t *vx, bf16x8 pb, f32x16 *oacc,
                                             Fill &&fill) {
     constexpr int kq_off = kq * 16 * kCkvRow;
     v4i16 lo[8], hi[8];
 #define MLA_TR(blk) \
-    lo[blk] = lds_read_tr16<kq_off + ((blk) >> 2) * 256>(base + vx[(blk) & 3]); \
-    hi[blk] = lds_read_tr16<kq_off + ((blk) >> 2) * 256>(base + vx[4 + ((blk) & 3)]);
+    lo[blk] = ld_tr16(base + vx[(blk) & 3] + kq_off + ((blk) >> 2) * 256); \
+    hi[blk] = ld_tr16(base + vx[4 + ((blk) & 3)] + kq_off + ((blk) >> 2) * 256);
     MLA_TR(0) MLA_TR(1) MLA_TR(2) MLA_TR(3) MLA_TR(4) MLA_TR(5) MLA_TR(6) MLA_TR(7)
 #undef MLA_TR
     pin();
-#define MLA_PV(blk, n)                                                                              \
-    wait_lgkm_tied2<n>(lo[blk], hi[blk]);                                                           \
+#define MLA_PV(blk)                                                                                 \
     oacc[blk] = mfma32(__builtin_bit_cast(bf16x8, v8i16{lo[blk][0], lo[blk][1], lo[blk][2], lo[blk][3], \
                                                         hi[blk][0], hi[blk][1], hi[blk][2], hi[blk][3]}), \
                        pb, oacc[blk]);                                                              \
     fill(blk);                                                                                      \
     pin();
-    MLA_PV(0, 14) MLA_PV(1, 12) MLA_PV(2, 10) MLA_PV(3, 8) MLA_PV(4, 6) MLA_PV(5, 4) MLA_PV(6, 2) MLA_PV(7, 0)
+    MLA_PV(0) MLA_PV(1) MLA_PV(2) MLA_PV(3) MLA_PV(4) MLA_PV(5) MLA_PV(6) MLA_PV(7)
 #undef MLA_PV
 }
 
@@ -119,10 +117,10 @@ __device__ __forceinline__ void latent_step(uint32_t base, const uint32_t *vx, b
 template <int KH, int k>
 __device__ __forceinline__ u32x4 k_operand(const uint32_t *kb, const uint32_t *kp) {
     if constexpr (KH == 1 && k >= 14) {
-        return lds_read_b128<0>(kp[k - 14]);
+        return ld128(kp[k - 14]);
     } else {
         constexpr int chunk = 2 * k + 36 * KH;             // logical chunk for g2 = 0
-        return lds_read_b128<(chunk & ~15) << 4>(kb[(chunk >> 1) & 7]);
+        return ld128(kb[(chunk >> 1) & 7] + ((chunk & ~15) << 4));
     }
 }
 
@@ -144,8 +142,6 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
     // step k: wait for read k (reads up to k+7 may be in flight), MFMA, read k+8
 #define MLA_KSTEP(k)                                                                   \
     {                                                                                  \
-        constexpr int inflight = (kSteps - 1 - (k)) < 7 ? (kSteps - 1 - (k)) : 7;      \
-        wait_lgkm_tied<inflight>(a[k]);                                                \
         if constexpr (kFp8 && (k) == kContent) {                                       \
             for (int j = 0; j < 16; ++j) acc[j] *= tsc[j];                              \
         }                                                                              \
@@ -176,15 +172,14 @@ __device__ __forceinline__ f32x16 score_tile(const uint32_t *kb, const uint32_t 
 //   first latent k-step: slot b waits for T(2b, 2b+1) and issues U(2b, 2b+1), the
 //                reads of the second k-step
 //   barrier (after W3 completed), exchange reads X0..X3
-//   second latent k-step: waits for U, then X
-// LDS operations complete in issue order, so each counted wait below is the
-// number of younger operations issued before it (capped at 15, which only
-// makes the wait stricter).
+//   second latent k-step: uses U, then X
+// The reads are plain loads: the compiler's counted waits before each use keep the
+// later ones in flight.
 // ---------------------------------------------------------------------------
 // transposing reads of column block blk (halves lo / hi) of k-step kq
 #define MLA_TR_PAIR(kq, blk, lo, hi, base, vx)                                                         \
-    lo = lds_read_tr16<(kq) * 16 * kCkvRow + ((blk) >> 2) * 256>((base) + (vx)[(blk) & 3]);            \
-    hi = lds_read_tr16<(kq) * 16 * kCkvRow + ((blk) >> 2) * 256>((base) + (vx)[4 + ((blk) & 3)]);
+    lo = ld_tr16((base) + (vx)[(blk) & 3] + (kq) * 16 * kCkvRow + ((blk) >> 2) * 256);                 \
+    hi = ld_tr16((base) + (vx)[4 + ((blk) & 3)] + (kq) * 16 * kCkvRow + ((blk) >> 2) * 256);
 
 __device__ __forceinline__ bf16x8 tr_operand(const v4i16 &lo, const v4i16 &hi) {
     return __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -206,8 +201,6 @@ __device__ __forceinline__ f32x16 score_tile_ahead(const uint32_t *kb, const uin
     // slot k waits for R(k): younger are R(k+1..min(k+7,17)) and the T pairs of slots 10..k-1
 #define MLA_KSTEP(k)                                                                   \
     {                                                                                  \
-        constexpr int younger = (k) <= 10 ? 7 : (k) - 3;                               \
-        wait_lgkm_tied<younger>(a[k]);                                                 \
         if constexpr (kFp8 && (k) == kContent) {                                       \
             for (int j = 0; j < 16; ++j) acc[j] *= tsc[j];                              \
         }                                                                              \
@@ -231,14 +224,12 @@ __device__ __forceinline__ f32x16 score_tile_ahead(const uint32_t *kb, const uin
 }
 
 // First latent k-step on the reads T issued in the score phase (the four exchange
-// writes follow them); slot b issues the reads U of the second k-step.  Each slot
-// has 18 younger operations (T after the pair, W, U so far): lgkmcnt(15).
+// writes follow them); slot b issues the reads U of the second k-step.
 __device__ __forceinline__ void latent_first(const v4i16 *tlo, const v4i16 *thi, bf16x8 pb, f32x16 *oacc,
                                              uint32_t vbase, const uint32_t *vx, v4i16 *ulo, v4i16 *uhi) {
 #define MLA_B1(blk)                                                                    \
     {                                                                                  \
         v4i16 lo = tlo[blk], hi = thi[blk];                                            \
-        wait_lgkm_tied2<15>(lo, hi);                                                   \
         oacc[blk] = mfma32(tr_operand(lo, hi), pb, oacc[blk]);                         \
         MLA_TR_PAIR(1, blk, ulo[blk], uhi[blk], vbase, vx)                             \
         pin();                                                                         \
@@ -248,21 +239,18 @@ __device__ __forceinline__ void latent_first(const v4i16 *tlo, const v4i16 *thi,
 }
 
 // Second latent k-step on the reads U, with the exchange reads X0..X3 issued after
-// them: slots 0..3 wait for their U pair (younger: later U pairs and X), slot 4
-// waits for everything (then X has landed too); fill(b) runs after MFMA b.
+// them; fill(b) runs after MFMA b.
 template <typename Fill>
 __device__ __forceinline__ void latent_second(const v4i16 *ulo, const v4i16 *uhi, bf16x8 pb, f32x16 *oacc,
                                               u32x4 *xr, Fill &&fill) {
-#define MLA_B2(blk, n)                                                                 \
+#define MLA_B2(blk)                                                                    \
     {                                                                                  \
         v4i16 lo = ulo[blk], hi = uhi[blk];                                            \
-        wait_lgkm_tied2<n>(lo, hi);                                                    \
-        if constexpr ((blk) == 4) wait_lgkm_tied4<0>(xr[0], xr[1], xr[2], xr[3]);      \
         oacc[blk] = mfma32(tr_operand(lo, hi), pb, oacc[blk]);                         \
         fill(blk);                                                                     \
         pin();                                                                         \
     }
-    MLA_B2(0, 15) MLA_B2(1, 15) MLA_B2(2, 14) MLA_B2(3, 12) MLA_B2(4, 0) MLA_B2(5, 0) MLA_B2(6, 0) MLA_B2(7, 0)
+    MLA_B2(0) MLA_B2(1) MLA_B2(2) MLA_B2(3) MLA_B2(4) MLA_B2(5) MLA_B2(6) MLA_B2(7)
 #undef MLA_B2
 }
 
@@ -485,18 +473,18 @@ __device__ __forceinline__ void attend_segment(
     auto exchange_write = [&](const f32x16 &sp) {
         const uint32_t w = xchg + wave * kXchgWave + lane * 16;
 #define MLA_XW(jq) \
-        lds_write_b128<(jq) * 1024>(w, u32x4{__float_as_uint(sp[4 * (jq)]), __float_as_uint(sp[4 * (jq) + 1]), \
-                                             __float_as_uint(sp[4 * (jq) + 2]), __float_as_uint(sp[4 * (jq) + 3])});
+        lds_store<u32x4>(w + (jq) * 1024, u32x4{__float_as_uint(sp[4 * (jq)]), __float_as_uint(sp[4 * (jq) + 1]), \
+                                                __float_as_uint(sp[4 * (jq) + 2]), __float_as_uint(sp[4 * (jq) + 3])});
         MLA_XW(0) MLA_XW(1) MLA_XW(2) MLA_XW(3)
 #undef MLA_XW
     };
     u32x4 xr[4];                                       // the partner's partial scores, as read
     auto exchange_read = [&]() {
         const uint32_t r = xchg + (wave ^ 1) * kXchgWave + lane * 16;
-        xr[0] = lds_read_b128<0>(r);
-        xr[1] = lds_read_b128<1024>(r);
-        xr[2] = lds_read_b128<2048>(r);
-        xr[3] = lds_read_b128<3072>(r);
+        xr[0] = ld128(r);
+        xr[1] = ld128(r + 1024);
+        xr[2] = ld128(r + 2048);
+        xr[3] = ld128(r + 3072);
     };
 
     float m_ref = -INFINITY;   // reference maximum (log2 domain), identical in a head's lanes
@@ -598,7 +586,6 @@ __device__ __forceinline__ void attend_segment(
     exchange_write(own);
     barrier_lds();
     exchange_read();
-    wait_lgkm_tied4<0>(xr[0], xr[1], xr[2], xr[3]);
 #pragma unroll
     for (int piece = 0; piece < 5; ++piece) max_piece(0, own, piece);
     float m_use = max_finish();
@@ -630,9 +617,11 @@ __device__ __forceinline__ void attend_segment(
             if (k < 16) weight_piece(k, m_cur, tsc_cur, pw, pk);
         }, vbase, tlo, thi);
         exchange_write(own);
+        pin();                                         // the writes precede the reads U
         // latent MFMAs of tile i, first k-step (issuing the second k-step's reads)
         latent_first(tlo, thi, as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]}), oacc, vbase, vx, ulo, uhi);
-        // the exchange writes have completed (15 younger reads at most): partner may read
+        // the exchange writes have completed (they precede the 16 reads U, and LDS
+        // operations complete in order): partner may read
         asm volatile("s_waitcnt lgkmcnt(15)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");

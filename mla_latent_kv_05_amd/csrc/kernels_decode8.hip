@@ -65,14 +65,6 @@ constexpr uint32_t kSpinLimit = 1u << 22;               // bound of the flag wai
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 static_assert(kRows == 64, "two head blocks of 32");
 
-// LDS reads in this kernel are plain loads: the compiler places the counted waits
-// before each use (it counts the LDS operations it issued; the asm LDS operations here
-// only make those waits stricter) and keeps the values in place until they land.
-__device__ __forceinline__ u32x4 ld128(uint32_t addr) { return lds_load<u32x4>(addr); }
-__device__ __forceinline__ v4i16 ld_tr16(uint32_t addr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS_AS v4i16 *>(static_cast<uintptr_t>(addr)));
-}
-
 // K operand of score step k for half KH of the 576 dims:
 //   KH = 0: latent chunk 2k + g2 (dims 16k ..), k < 18
 //   KH = 1: latent chunk 2k + 36 + g2 (dims 288 + 16k ..) for k < 14, then RoPE chunk 2(k-14) + g2
