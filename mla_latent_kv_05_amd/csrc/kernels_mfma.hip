@@ -21,12 +21,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return cvt_p
 
 // ---------------------------------------------------------------------------
 // mla_absorb_q: q_abs[r, h, m] = sum_d q_nope[r, h, d] W_UK[h, d, m]
-// One wave per (head, 128-column quarter of d_c): the wave reads its 128 x 128
+// One wave per (head, 64-column eighth of d_c): the wave reads its 128 x 64
 // slice of W_UK[h] once, all loads in flight together, keeps it in registers
-// as MFMA operands and applies it to the rows 64 at a time.
-// D^T[m, r] = W^T[m, d] . q^T[d, r]: W rows are read 8 at a time (16 bytes
-// each) and transposed in registers into 8 A operands; MFMA i of a k-step
-// covers columns col0 + i of the 16 lanes' column groups.
+// as MFMA operands and applies it to the rows 64 at a time (1024 waves at the
+// DeepSeek-V3 shapes: four per compute unit, so that loads and stores overlap).
+// D^T[m, r] = W^T[m, d] . q^T[d, r]: each lane reads 4 columns of 8 W rows
+// (8 bytes each) and transposes them in registers into 4 A operands; MFMA i of
+// a k-step covers column col0 + i of the 16 lanes' column groups.
 // ---------------------------------------------------------------------------
 template <int kDh>
 __global__ __launch_bounds__(64) void absorb_mfma_kernel(
@@ -35,16 +36,16 @@ __global__ __launch_bounds__(64) void absorb_mfma_kernel(
     constexpr int kKs = kDh / 32;                 // 32-deep k-steps
     const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
     const int R = p.B * p.Sq;
-    const int h = blockIdx.x >> 2;
-    const int cq = blockIdx.x & 3;                // 128-column quarter of d_c
-    const int col0 = cq * 128 + r16 * 8;          // this lane's 8 columns
+    const int h = blockIdx.x >> 3;
+    const int c8 = blockIdx.x & 7;                // 64-column eighth of d_c
+    const int col0 = c8 * 64 + r16 * 4;           // this lane's 4 columns
     const uint16_t *W = W_UK + static_cast<int64_t>(h) * kDh * kDc;
-    u32x4 rows[kKs][8];
+    u32x2 rows[kKs][8];
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            rows[ks][e] = *reinterpret_cast<const u32x4 *>(W + static_cast<int64_t>(ks * 32 + g * 8 + e) * kDc + col0);
+            rows[ks][e] = *reinterpret_cast<const u32x2 *>(W + static_cast<int64_t>(ks * 32 + g * 8 + e) * kDc + col0);
     // the first row chunk's query loads go out with the weight loads
     auto load_q = [&](int r0, bf16x8 (&bq)[kKs][4]) {
 #pragma unroll
@@ -61,11 +62,12 @@ __global__ __launch_bounds__(64) void absorb_mfma_kernel(
     };
     bf16x8 bq[kKs][4];
     load_q(0, bq);
-    bf16x8 a[kKs][8];
+    // A operand i: column col0 + i, d = ks*32 + g*8 + 0..7
+    bf16x8 a[kKs][4];
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             u32x4 v;
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2)
@@ -74,90 +76,102 @@ __global__ __launch_bounds__(64) void absorb_mfma_kernel(
             a[ks][i] = as_bf16x8(v);
         }
     for (int r0 = 0; r0 < R; r0 += 64) {
-        f32x4 acc[8][4];
+        f32x4 acc[4][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) acc[i][rt] = mfma16(a[ks][i], bq[ks][rt], acc[i][rt]);
         if (r0 + 64 < R) load_q(r0 + 64, bq);          // next chunk, in flight under the stores
-        // acc[i][rt][j]: row r0 + rt*16 + r16, column cq*128 + 8*(4g + j) + i
+        // acc[i][rt][j]: row r0 + rt*16 + r16, column c8*64 + 4*(4g + j) + i
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int r = r0 + rt * 16 + r16;
             if (r >= R) continue;
-            uint16_t *dst = q_abs + (static_cast<int64_t>(r) * p.H + h) * kDc + cq * 128;
+            uint16_t *dst = q_abs + (static_cast<int64_t>(r) * p.H + h) * kDc + c8 * 64;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x4 v;
-#pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) v[k2] = pack_bf16x2(acc[2 * k2][rt][j], acc[2 * k2 + 1][rt][j]);
-                *reinterpret_cast<u32x4 *>(dst + (g * 4 + j) * 8) = v;
-            }
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2 *>(dst + (g * 4 + j) * 4) =
+                    u32x2{pack_bf16x2(acc[0][rt][j], acc[1][rt][j]), pack_bf16x2(acc[2][rt][j], acc[3][rt][j])};
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // mla_up_v: out[r, h, d] = sum_m o_latent[r, h, m] W_UV[h, d, m]
-// One wave per (head, 64-row chunk, quarter of the d_h output rows):
-// D^T[d, r] = W_UV[d, m] . o^T[m, r]; both operands are contiguous along m,
-// so no transpose is needed.
+// One workgroup of 4 waves per (head, 32-row chunk): the chunk's latent rows go
+// to LDS once (16-byte chunks XOR-swizzled by row, so that the 16 rows an MFMA
+// operand reads at one column hit distinct banks); wave w holds the weight rows
+// d = 32w .. 32w+31 in registers (all loads in flight together) and forms
+// D^T[d, r] = W_UV[d, m] . o^T[m, r]; both operands are contiguous along m.  The
+// two chunks of a head run on the same XCD, so the second weight read hits L2.
 // ---------------------------------------------------------------------------
+constexpr int kUpRows = 32;                       // rows per workgroup
+
 template <int kDh, bool kOutBf16>
-__global__ __launch_bounds__(64) void up_v_mfma_kernel(
+__global__ __launch_bounds__(256) void up_v_mfma_kernel(
     const mla_params_t p, const uint16_t *__restrict__ o_latent, const uint16_t *__restrict__ W_UV,
     void *__restrict__ out) {
-    constexpr int kDt = kDh / 4 / 16;             // 16-row d tiles per wave
-    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    static_assert(kDh == 128, "four waves of 32 output rows");
+    __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2];
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = p.B * p.Sq;
-    const int h = blockIdx.x % p.H;
-    const int rest = blockIdx.x / p.H;
-    const int dq = rest & 3;
-    const int r0 = (rest >> 2) * 64;
-    const int d0 = dq * (kDh / 4);
-    f32x4 acc[kDt][4];
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int n_rc = (R + kUpRows - 1) / kUpRows;
+    // workgroup -> (head, row chunk): consecutive chunks of a head are 8 workgroups
+    // apart (workgroup i runs on XCD i % 8)
+    const int q = blockIdx.x >> 3;
+    const int rc = q % n_rc;
+    const int h = (q / n_rc) * 8 + (blockIdx.x & 7);
+    if (h >= p.H) return;                         // grid rounded up to 8 heads
+    const int r0 = rc * kUpRows;
+    const int d0 = w * 32;
+    const uint32_t sm = lds_addr(smem);
+    // this wave's weights: d-tile dt (16 rows), k-step ks (32 columns m)
     const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
-    bool rvalid[4];
-    const uint16_t *orow[4];
+    bf16x8 wa[kDc / 32][2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int r = r0 + rt * 16 + r16;
-        rvalid[rt] = r < R;
-        orow[rt] = o_latent + (static_cast<int64_t>(rvalid[rt] ? r : 0) * p.H + h) * kDc;
+    for (int ks = 0; ks < kDc / 32; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+            wa[ks][dt] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + dt * 16 + r16) * kDc + ks * 32 + g * 8);
+    // the chunk's latent rows into LDS: row rr, 16-byte chunk c at rr*1024 + ((c ^ (rr % 16)) << 4)
+#pragma unroll
+    for (int k = threadIdx.x; k < kUpRows * 64; k += 256) {
+        const int rr = k >> 6, c = k & 63;
+        const int r = r0 + rr;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r < R) v = *reinterpret_cast<const u32x4 *>(o_latent + (static_cast<int64_t>(r) * p.H + h) * kDc + c * 8);
+        lds_store<u32x4>(sm + rr * 1024 + ((c ^ (rr & 15)) << 4), v);
     }
-#pragma unroll 2
-    for (int ks = 0; ks < kDc / 32; ++ks) {
-        bf16x8 bo[4];
+    __syncthreads();
+    f32x4 acc[2][2];                              // [dt][rt]
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (rvalid[rt]) v = *reinterpret_cast<const u32x4 *>(orow[rt] + ks * 32 + g * 8);
-            bo[rt] = as_bf16x8(v);
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDc / 32; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int rr = rt * 16 + r16, c = ks * 4 + g;
+            const bf16x8 bo = as_bf16x8(lds_load<u32x4>(sm + rr * 1024 + ((c ^ (rr & 15)) << 4)));
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) acc[dt][rt] = mfma16(wa[ks][dt], bo, acc[dt][rt]);
         }
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + dt * 16 + r16) * kDc + ks * 32 + g * 8);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[dt][rt] = mfma16(a, bo[rt], acc[dt][rt]);
-        }
-    }
     // acc[dt][rt][j]: row r0 + rt*16 + r16, d = d0 + dt*16 + 4g + j
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        if (!rvalid[rt]) continue;
-        const int64_t base = (static_cast<int64_t>(r0 + rt * 16 + r16) * p.H + h) * kDh + d0;
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = r0 + rt * 16 + r16;
+        if (r >= R) continue;
+        const int64_t base = (static_cast<int64_t>(r) * p.H + h) * kDh + d0;
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
+        for (int dt = 0; dt < 2; ++dt) {
             if constexpr (kOutBf16) {
                 uint16_t *o = static_cast<uint16_t *>(out) + base + dt * 16 + g * 4;
                 *reinterpret_cast<u32x2 *>(o) = u32x2{pack_bf16x2(acc[dt][rt][0], acc[dt][rt][1]),
@@ -247,7 +261,7 @@ bool absorb_mfma_supported(const mla_params_t &p) {
 
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
                               void *q_abs, hipStream_t stream) {
-    const int64_t blocks = static_cast<int64_t>(p.H) * 4;
+    const int64_t blocks = static_cast<int64_t>(p.H) * 8;
     hipLaunchKernelGGL(absorb_mfma_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, p,
                        static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(W_UK),
                        static_cast<uint16_t *>(q_abs));
@@ -262,14 +276,14 @@ bool up_v_mfma_supported(const mla_params_t &p) {
 hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,
                             void *out, hipStream_t stream) {
     const int64_t R = static_cast<int64_t>(p.B) * p.Sq;
-    const int64_t blocks = static_cast<int64_t>(p.H) * 4 * ((R + 63) / 64);
+    const int64_t blocks = (static_cast<int64_t>(p.H) + 7) / 8 * 8 * ((R + kUpRows - 1) / kUpRows);
     const auto ol = static_cast<const uint16_t *>(o_latent);
     const auto w = static_cast<const uint16_t *>(W_UV);
     if (p.out_dtype == MLA_BF16)
-        hipLaunchKernelGGL((up_v_mfma_kernel<128, true>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
+        hipLaunchKernelGGL((up_v_mfma_kernel<128, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                            p, ol, w, out);
     else
-        hipLaunchKernelGGL((up_v_mfma_kernel<128, false>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream,
+        hipLaunchKernelGGL((up_v_mfma_kernel<128, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                            p, ol, w, out);
     return hipGetLastError();
 }
