@@ -179,10 +179,9 @@ def measured_traffic(workload: str):
     scaled by its reading for a device copy of known size in the same profiling run;
     None when the summary is missing, for another workload, or was taken on a
     different version of the kernel sources."""
-    import hashlib
     try:
         kv = dict(l.split("=", 1) for l in open(COUNTERS).read().split("\n") if "=" in l and not l.startswith("#"))
-        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SRCS)).hexdigest()
+        src = code_hash(KERNEL_SRCS)
     except OSError:
         return None
     if kv.get("kernel_source_sha256", "").strip() != src or kv.get("workload", "").strip() != workload:
@@ -192,6 +191,19 @@ def measured_traffic(workload: str):
     fetch = float(kv["fetch_size_kib"]) / float(kv["copy_probe_fetch_size_kib"]) * probe
     write = float(kv["write_size_kib"]) / float(kv["copy_probe_write_size_kib"]) * probe
     return round(fetch + write)
+
+
+def code_hash(paths):
+    """sha256 of the sources' code: comments dropped and whitespace runs collapsed,
+    so that an edit of a comment keeps the hash (string literals are kept whole)."""
+    import hashlib
+    import re
+    tok = re.compile(r'("(?:\\.|[^"\\])*")|//[^\n]*|/\*.*?\*/', re.S)
+    parts = []
+    for f in paths:
+        text = tok.sub(lambda m: m.group(1) or " ", open(f).read())
+        parts.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
 def cpu_baseline(case, budget_s):

@@ -1,6 +1,8 @@
 // mla_decode_splitkv on bf16 MFMA: absorbed-MLA attention over the paged
 // latent cache at the DeepSeek-V3 head shapes (d_c = 512 latent, d_r = 64
-// RoPE key, page = 64 tokens), gfx950 / CDNA4.
+// RoPE key, page = 64 tokens), gfx950 / CDNA4.  Launched for the e4m3 cache
+// (a bf16 cache runs on the eight-wave kernel of kernels_decode8.hip, so only
+// the kFp8 = true instance of the template is built).
 //
 // Attention ("MLA Matrix Absorption" sec. 4.1-4.2; "DeepSeek-MLA-Principle"
 // sec. 2 and matrix absorption 3)): every head of a sequence attends to the
@@ -749,12 +751,11 @@ hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const vo
     const auto qa = static_cast<const uint16_t *>(q_abs);
     const auto qr = static_cast<const uint16_t *>(q_rope);
     const auto kp = static_cast<const uint16_t *>(k_pe);
-    if (p.kv_dtype == MLA_FP8_E4M3)
-        hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                           p, qa, qr, c_kv, kp, kv_scale, block_table, seq_lens, o_part, lse_part);
-    else
-        hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                           p, qa, qr, c_kv, kp, kv_scale, block_table, seq_lens, o_part, lse_part);
+    // a bf16 cache runs on the eight-wave kernel (kernels_decode8.hip); this one
+    // serves the e4m3 cache
+    if (p.kv_dtype != MLA_FP8_E4M3) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                       p, qa, qr, c_kv, kp, kv_scale, block_table, seq_lens, o_part, lse_part);
     return hipGetLastError();
 }
 

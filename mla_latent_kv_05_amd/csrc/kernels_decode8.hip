@@ -26,7 +26,8 @@
 //   wave's MFMAs.
 // Pipeline: iteration i (one workgroup barrier at its end) computes the scores and
 // weights of tile i+1 in the score waves and the latent update of tile i in the
-// latent waves, which also copy tile i+2 into the stage tile i-1 used.
+// latent waves; once its V reads of tile i are in, latent wave v refills its
+// column block of that stage with tile i+3 (copies run two to three tiles ahead).
 // Layouts of the latent / RoPE rows in a stage and the token order are those of
 // decode_common.h.  The output is the normalised partial O_c (fp32) and its
 // log-sum-exp per row, as for every other decode kernel.
