@@ -1,0 +1,135 @@
+"""Plain CPU oracle of the cache append (numpy, fp64 for the rotation).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the bench's CPU
+baseline use this module.  It shares nothing with the HIP path.
+
+What it computes, with the passages it follows:
+
+  position      the Sq new tokens of sequence b take positions
+                seq_lens[b] - Sq + s (s < Sq): seq_lens already counts them, as
+                in the decode module of "DeepSeek MLA 架构详解", which appends the
+                new token to both caches and then attends over all of them.
+  slot          position t lives at page block_table[b, t // 64], slot t % 64
+                (the paged cache with a block table that "DeepSeek-MLA-Principle"
+                lists among FlashMLA's ideas, sec. 3).
+  RoPE          the decode module's rotation of the shared RoPE key (and of the
+                query's RoPE part) at the token's position, rotate-half form with
+                base 10000: with half = d_r / 2 and
+                theta_i = pos * 10000^(-i / half), i < half,
+                    y[i]        = x[i] cos theta_i - x[i + half] sin theta_i
+                    y[i + half] = x[i + half] cos theta_i + x[i] sin theta_i
+                ("DeepSeek-MLA-Principle" sec. 3, why RoPE: the rotation R_pos
+                makes <R_m q, R_n k> depend on n - m only).
+  e4m3 cache    the pages fix no quantiser.  Per token: amax = max |x| over the
+                latent row, scale = max(amax, 2^-20) / 448 and r_j = x_j / scale,
+                both divisions in fp32 (the precision the kernel decides in);
+                the code is the E4M3 value nearest to r_j, ties to the even code,
+                magnitudes above 448 saturating to 448, sign kept.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import oracle as O
+
+E4M3_MAX = 448.0
+MIN_AMAX = 2.0 ** -20
+
+
+def positions(seq_lens: np.ndarray, Sq: int) -> np.ndarray:
+    """pos[b, s] = seq_lens[b] - Sq + s."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    return seq_lens[:, None] - Sq + np.arange(Sq, dtype=np.int64)[None, :]
+
+
+def slots(block_table: np.ndarray, seq_lens: np.ndarray, Sq: int):
+    """(page, slot) of every new token, each [B, Sq]."""
+    pos = positions(seq_lens, Sq)
+    bt = np.asarray(block_table, dtype=np.int64)
+    page = np.take_along_axis(bt, pos // 64, axis=1)
+    return page, pos % 64
+
+
+def rope(x: np.ndarray, pos) -> np.ndarray:
+    """Rotate-half RoPE of the last axis of x (float64) at position pos
+    (a scalar or an array broadcasting against x[..., 0])."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % 2 == 0, "RoPE needs an even dimension"
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    freq = np.exp(-np.log(10000.0) * i / half)             # 10000^(-i/half)
+    theta = np.asarray(pos, dtype=np.float64)[..., None] * freq
+    c, s = np.cos(theta), np.sin(theta)
+    lo, hi = x[..., :half], x[..., half:]
+    y = np.empty_like(x)
+    y[..., :half] = lo * c - hi * s
+    y[..., half:] = hi * c + lo * s
+    return y
+
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the non-negative finite codes 0x00 .. 0x7E (the oracle's decoder)."""
+    L = O.lib()
+    return np.array([L.orc_e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+
+
+_TABLE = None
+
+
+def e4m3_nearest(r: np.ndarray) -> np.ndarray:
+    """Code of the E4M3 value nearest to each r (float32 array): ties go to the
+    even code, magnitudes above 448 saturate, the sign bit follows r's sign."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = _e4m3_table()
+    r = np.asarray(r, dtype=np.float32)
+    a = np.abs(r.astype(np.float64)).reshape(-1)
+    dist = np.abs(a[:, None] - _TABLE[None, :])             # [n, 127]
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best                                      # one or two codes (a tie)
+    codes = np.arange(0x7F)
+    # among the nearest codes prefer an even one (at a tie exactly one is even)
+    even_pick = np.where(cand & (codes[None, :] % 2 == 0), codes[None, :], 0x7F).min(axis=1)
+    any_pick = np.where(cand, codes[None, :], 0x7F).min(axis=1)
+    mag = np.where(even_pick < 0x7F, even_pick, any_pick)
+    sign = np.signbit(r.reshape(-1)).astype(np.int64) << 7
+    return (mag | sign).astype(np.uint8).reshape(r.shape)
+
+
+def quantize_e4m3_rows(x: np.ndarray):
+    """Per-row E4M3 quantisation of float32 rows [n, d]: (codes [n, d] uint8,
+    scales [n] float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.maximum(amax, np.float32(MIN_AMAX)).astype(np.float32) / np.float32(E4M3_MAX)
+    r = x / scale[..., None]                                 # float32 division
+    return e4m3_nearest(r), scale.astype(np.float32)
+
+
+def append_kv(c_new, kpe_new, block_table, seq_lens, Sq: int, q_rope=None):
+    """Expected effect of appending the new tokens.
+
+    c_new [B, Sq, d_c], kpe_new [B, Sq, d_r] and q_rope [B, Sq, H, d_r] are the
+    exact float64 values of the stored inputs.  Returns a dict with
+      page, slot  [B, Sq]  where each token is written
+      c           [B, Sq, d_c] float64 latent rows (to be stored in the cache dtype)
+      codes, scales  [B, Sq, d_c] uint8, [B, Sq] float32 (the e4m3 form of c)
+      kpe         [B, Sq, d_r] float64 rotated RoPE keys
+      q_rope      [B, Sq, H, d_r] float64 rotated query RoPE parts (None if not given)
+    """
+    c_new = np.asarray(c_new, dtype=np.float64)
+    pos = positions(seq_lens, Sq)
+    page, slot = slots(block_table, seq_lens, Sq)
+    out = {"page": page, "slot": slot, "pos": pos, "c": c_new}
+    codes, scales = quantize_e4m3_rows(c_new.astype(np.float32).reshape(-1, c_new.shape[-1]))
+    out["codes"] = codes.reshape(c_new.shape)
+    out["scales"] = scales.reshape(c_new.shape[:-1])
+    kpe_new = np.asarray(kpe_new, dtype=np.float64)
+    out["kpe"] = rope(kpe_new, pos) if kpe_new.shape[-1] > 0 else kpe_new
+    if q_rope is not None:
+        q = np.asarray(q_rope, dtype=np.float64)
+        out["q_rope"] = rope(q, pos[:, :, None])
+    else:
+        out["q_rope"] = None
+    return out
