@@ -128,6 +128,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    append = append_bench(mla, A, wl, p, reps[0], dev, stream, args)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_budget_s)
@@ -168,10 +170,70 @@ def main():
         },
         "step_roofline": {"bytes": cost.total_bytes, "flops": cost.flops, "t_roof_us": round(roofline_us, 2),
                           "frac": round(roofline_us / (ms_step * 1e3), 4)},
+        "append": append,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(result), flush=True)
+
+
+def append_bench(mla, A, wl, p, t, dev, stream, args):
+    """mla_append_kv timed on its own (not part of the step): the step's batch
+    (one new token per sequence, query rotated in place) and a bulk append of
+    16 new tokens into each of 16,384 sequences (lengths U[16, 8192], one page
+    per touched page slot), which is HBM-bound."""
+    import numpy as np
+    import torch
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    # the step's batch: new token at position seq_len - 1 of every sequence
+    rng = np.random.default_rng(wl.seed + 77)
+    c_new = torch.from_numpy(rng.standard_normal((wl.B, wl.Sq, wl.d_c), dtype=np.float32)).to(dev).bfloat16()
+    r_new = torch.from_numpy(rng.standard_normal((wl.B, wl.Sq, wl.d_r), dtype=np.float32)).to(dev).bfloat16()
+    q = t["q_rope"].clone()
+    us_step = timed(lambda: mla.append_kv(p, c_new, r_new, t["block_table"], t["seq_lens"], t["c_kv"],
+                                          t["k_pe"], t["kv_scale"], q_rope_in=q, q_rope_out=q), 20)
+
+    # bulk: 16,384 sequences x 16 new tokens
+    Bb, Sqb = 16384, 16
+    lens = rng.integers(Sqb, 8192, size=Bb, endpoint=True)
+    max_pages = int((lens.max() + 63) // 64)
+    bt = np.full((Bb, max_pages), -1, dtype=np.int32)
+    first = (lens - Sqb) // 64
+    last = (lens - 1) // 64
+    n_need = int((last - first + 1).sum())
+    perm = rng.permutation(n_need).astype(np.int32)
+    k = 0
+    for b in range(Bb):
+        for j in range(first[b], last[b] + 1):
+            bt[b, j] = perm[k]
+            k += 1
+    pb = mla.make_params(Bb, Sqb, wl.H, wl.d_h, wl.d_c, wl.d_r, n_need, max_pages)
+    cb = torch.empty((n_need, 64, wl.d_c), dtype=torch.bfloat16, device=dev)
+    rb = torch.empty((n_need, 64, wl.d_r), dtype=torch.bfloat16, device=dev)
+    cn = torch.randn((Bb, Sqb, wl.d_c), device=dev).bfloat16()
+    rn = torch.randn((Bb, Sqb, wl.d_r), device=dev).bfloat16()
+    btd = torch.from_numpy(bt).to(dev)
+    sld = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    us_bulk = timed(lambda: mla.append_kv(pb, cn, rn, btd, sld, cb, rb), 20)
+    nbytes = A.append_bytes(Bb * Sqb, wl.H, wl.d_c, wl.d_r)
+    gbs = nbytes / (us_bulk * 1e-6) / 1e9
+    return {"kernel": "mla_append_kv", "step_batch_us": round(us_step, 2),
+            "step_batch_bytes": A.append_bytes(wl.B * wl.Sq, wl.H, wl.d_c, wl.d_r, with_query=True),
+            "bulk": {"workload": f"{Bb} sequences x {Sqb} new tokens, lengths U[{Sqb},8192], bf16",
+                     "tokens": Bb * Sqb, "us": round(us_bulk, 2), "bytes": nbytes,
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
 def measured_traffic(workload: str):

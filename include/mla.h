@@ -3,7 +3,8 @@
  * (MLA) decode over a paged latent KV cache, hand-written HIP kernels for
  * AMD Instinct MI355X (gfx950).
  *
- * One decode step is four stream-ordered calls:
+ * The new tokens enter the cache with mla_append_kv (RoPE, optional e4m3
+ * quantisation); one decode step is then four stream-ordered calls:
  *
  *   mla_absorb_q        q_abs  = q_nope . W_UK            (key absorption)
  *   mla_decode_splitkv  per split c: scores, softmax, latent sum -> (O_c, lse_c)
@@ -188,6 +189,44 @@ mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const f
  */
 mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W_UV,
                       void *out, void *stream);
+
+/*
+ * mla_append_kv -- write the Sq new tokens of every sequence into the paged
+ * cache, rotating the shared RoPE key at each token's position; optionally
+ * rotate the query's RoPE part at the same positions.  The decode module of
+ * "DeepSeek MLA 架构详解" computes the new token's latent row and RoPE key,
+ * rotates the key at the token's position and appends both to the caches
+ * before attending; "DeepSeek-MLA-Principle" sec. 3 (why RoPE) gives the
+ * rotation's relative-position property.
+ *
+ * Token s of sequence b takes position pos = seq_lens[b] - Sq + s (seq_lens
+ * already counts the new tokens, as for mla_decode_splitkv) and cache row
+ * block_table[b, pos / 64] * 64 + pos % 64.  RoPE, rotate-half form, base 10000:
+ * with half = d_r / 2 and theta_i = pos * 10000^(-i / half), i < half,
+ *   y[i]        = x[i] cos theta_i - x[i + half] sin theta_i
+ *   y[i + half] = x[i + half] cos theta_i + x[i] sin theta_i
+ * computed in fp64, rounded once to fp32, then to the destination format.
+ * Latent rows are stored in kv_dtype (round to nearest even from fp32).  For an
+ * FP8_E4M3 cache, per token: scale = max(amax, 2^-20) / 448 and r_j = x_j / scale
+ * (correctly rounded fp32 divisions), code_j = the E4M3 value nearest to r_j
+ * (ties to even, |r_j| > 448 saturating to 448, sign kept), and the token's
+ * kv_scale entry = scale.
+ *
+ *   c_new      [B,Sq,d_c]    q_dtype  (in: latent rows of the new tokens)
+ *   kpe_new    [B,Sq,d_r]    q_dtype  (in: RoPE keys before rotation; may be NULL iff d_r == 0)
+ *   q_rope_in  [B,Sq,H,d_r]  q_dtype  (in, may be NULL: query RoPE parts before rotation)
+ *   q_rope_out [B,Sq,H,d_r]  q_dtype  (out; NULL iff q_rope_in is NULL; may equal q_rope_in)
+ *   block_table, seq_lens    as for mla_decode_splitkv; seq_lens[b] >= Sq
+ *   c_kv       [num_pages,64,d_c] kv_dtype (in/out: only the new tokens' rows are written)
+ *   k_pe       [num_pages,64,d_r] pe_dtype (in/out: likewise)
+ *   kv_scale   [num_pages,64] fp32 (out for the new rows; required iff kv_dtype == FP8_E4M3)
+ * d_r must be even.  Two new tokens must not map to the same cache row
+ * (distinct pages per sequence), else the result is undefined.
+ */
+mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void *kpe_new,
+                           const void *q_rope_in, void *q_rope_out, const int32_t *block_table,
+                           const int32_t *seq_lens, void *c_kv, void *k_pe, float *kv_scale,
+                           void *stream);
 
 /* Host-only validation of *p (no GPU needed).  Returns MLA_OK or the first error. */
 mla_status_t mla_check_params(const mla_params_t *p);

@@ -85,3 +85,17 @@ def step_cost(B: int, Sq: int, H: int, d_h: int, d_c: int, d_r: int, seq_lens,
     decode_bytes = cache + rows * (d_c + d_r) * lat_elem
     return StepCost(cache, weights, query, out, attend_flops + proj_flops,
                     decode_bytes, attend_flops)
+
+
+def append_bytes(tokens: int, H: int, d_c: int, d_r: int, in_fmt: str = "bf16", kv_fmt: str = "bf16",
+                 pe_fmt: str = "bf16", with_query: bool = False) -> int:
+    """Algorithmic bytes of appending `tokens` new tokens: the latent rows and RoPE
+    keys read in the activation format and written in the cache formats (fp8:
+    e4m3 codes plus one fp32 scale per token), and, with the query rotation, the
+    query RoPE parts read and written."""
+    a = FORMAT_BYTES[in_fmt]
+    c_out = d_c + 4 if kv_fmt == "fp8" else d_c * FORMAT_BYTES[kv_fmt]
+    per_tok = (d_c + d_r) * a + c_out + d_r * FORMAT_BYTES[pe_fmt]
+    if with_query:
+        per_tok += 2 * H * d_r * a
+    return tokens * per_tok

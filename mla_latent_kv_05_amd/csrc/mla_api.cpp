@@ -199,4 +199,23 @@ mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W
     return hip_status(mla::launch_up_v_generic(*p, o_latent, W_UV, out, st), "mla_up_v launch");
 }
 
+mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void *kpe_new, const void *q_rope_in,
+                           void *q_rope_out, const int32_t *block_table, const int32_t *seq_lens, void *c_kv,
+                           void *k_pe, float *kv_scale, void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!c_new || !block_table || !seq_lens || !c_kv) return fail(MLA_ERR_NULL, "mla_append_kv: NULL tensor pointer");
+    if (p->d_r > 0 && (!kpe_new || !k_pe)) return fail(MLA_ERR_NULL, "mla_append_kv: NULL kpe_new/k_pe with d_r > 0");
+    if (p->d_r % 2 != 0) return fail(MLA_ERR_SHAPE, "mla_append_kv: d_r must be even for the rotation (got %d)", p->d_r);
+    if ((q_rope_in == nullptr) != (q_rope_out == nullptr))
+        return fail(MLA_ERR_NULL, "mla_append_kv: q_rope_in and q_rope_out must be both given or both NULL");
+    if (p->kv_dtype == MLA_FP8_E4M3 && !kv_scale)
+        return fail(MLA_ERR_NULL, "mla_append_kv: kv_scale is required for an FP8_E4M3 cache");
+    if ((int64_t)p->B * p->Sq > 0x7fffffffll) return fail(MLA_ERR_SHAPE, "mla_append_kv: B*Sq too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_append(*p, c_new, kpe_new, q_rope_in, q_rope_out, block_table, seq_lens, c_kv, k_pe,
+                                         kv_scale, st),
+                      "mla_append_kv launch");
+}
+
 }  // extern "C"

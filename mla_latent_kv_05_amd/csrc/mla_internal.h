@@ -44,6 +44,11 @@ hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const
 hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,
                             void *out, hipStream_t stream);
 
+// cache append with RoPE and the e4m3 quantiser (kernels_append.hip)
+hipError_t launch_append(const mla_params_t &p, const void *c_new, const void *kpe_new, const void *q_rope_in,
+                         void *q_rope_out, const int32_t *block_table, const int32_t *seq_lens, void *c_kv,
+                         void *k_pe, float *kv_scale, hipStream_t stream);
+
 // Heads x query rows handled by one attention workgroup of the MFMA kernel.
 constexpr int kDecodeRowsPerBlock = 64;
 

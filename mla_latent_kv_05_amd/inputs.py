@@ -245,3 +245,15 @@ def random_o_latent(wl: Workload, seed: int) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((wl.B, wl.Sq, wl.H, wl.d_c), dtype=np.float32)
     return _to_store(x, latent_format(wl))
+
+
+def random_new_tokens(wl: Workload, seed: int, fmt: Optional[str] = None, latent_std: float = 3.0):
+    """The new tokens' latent rows [B, Sq, d_c] and un-rotated RoPE keys
+    [B, Sq, d_r] of an append (normal; latent rows with standard deviation
+    ``latent_std``, 3 by default so that the per-token e4m3 scales vary), stored
+    as ``fmt`` (default: the workload's activation format)."""
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal((wl.B, wl.Sq, wl.d_c), dtype=np.float32) * np.float32(latent_std)
+    r = rng.standard_normal((wl.B, wl.Sq, wl.d_r), dtype=np.float32)
+    fmt = fmt or ("f32" if wl.dtype == "f32" else "bf16")
+    return _to_store(c, fmt), _to_store(r, fmt)

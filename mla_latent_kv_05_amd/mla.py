@@ -26,7 +26,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v",
-           "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
+           "mla_append_kv", "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
 
@@ -76,6 +76,7 @@ def lib():
             ("mla_decode_splitkv", [PP, P, P, P, P, P, P, P, P, P, P]),
             ("mla_combine_lse", [PP, P, P, P, P, P]),
             ("mla_up_v", [PP, P, P, P, P]),
+            ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
             ("mla_check_params", [PP]),
             ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
         ):
@@ -206,6 +207,27 @@ def up_v(p: Params, o_latent, W_UV, out, stream=None) -> None:
                           _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
                           _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
                           _stream(stream)))
+
+
+def append_kv(p: Params, c_new, kpe_new, block_table, seq_lens, c_kv, k_pe, kv_scale=None,
+              q_rope_in=None, q_rope_out=None, stream=None) -> None:
+    """Write the new tokens' latent rows and rotated RoPE keys into the cache
+    (and rotate q_rope_in into q_rope_out, which may be the same tensor)."""
+    tok = (p.B, p.Sq)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    _check(lib().mla_append_kv(
+        ctypes.byref(p),
+        _ptr(c_new, "c_new", tok + (p.d_c,), p.q_dtype),
+        _ptr(kpe_new, "kpe_new", tok + (p.d_r,), p.q_dtype),
+        _ptr(q_rope_in, "q_rope_in", tok + (p.H, p.d_r), p.q_dtype),
+        _ptr(q_rope_out, "q_rope_out", tok + (p.H, p.d_r), p.q_dtype),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+        _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+        _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+        _stream(stream)))
 
 
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}

@@ -99,6 +99,29 @@ def test_null_pointers_rejected_without_launch():
     assert L.mla_up_v(ctypes.byref(bad), dummy, dummy, dummy, None) == 2
 
 
+def test_append_arguments_rejected_without_launch():
+    """mla_append_kv validates its pointers and shapes on the host."""
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)              # never dereferenced: validation fails first
+    p = v3()
+    pp = ctypes.byref(p)
+    # c_new, block_table, seq_lens, c_kv are required; kpe_new / k_pe when d_r > 0
+    assert L.mla_append_kv(pp, None, d, None, None, d, d, d, d, None, None) == 1
+    assert L.mla_append_kv(pp, d, None, None, None, d, d, d, d, None, None) == 1
+    assert L.mla_append_kv(pp, d, d, None, None, d, None, d, d, None, None) == 1
+    assert L.mla_append_kv(pp, d, d, None, None, d, d, d, None, None, None) == 1
+    # q_rope_in and q_rope_out go together
+    assert L.mla_append_kv(pp, d, d, d, None, d, d, d, d, None, None) == 1
+    assert L.mla_append_kv(pp, d, d, None, d, d, d, d, d, None, None) == 1
+    # an e4m3 cache needs kv_scale
+    q = v3(kv_dtype=mla.FP8_E4M3)
+    assert L.mla_append_kv(ctypes.byref(q), d, d, None, None, d, d, d, d, None, None) == 1
+    # the rotation pairs dims i and i + d_r/2: d_r must be even
+    r = v3(d_r=63)
+    assert L.mla_append_kv(ctypes.byref(r), d, d, None, None, d, d, d, d, None, None) == 2
+    assert "even" in L.mla_last_error().decode()
+
+
 def test_status_strings():
     L = mla.lib()
     for code, name in mla.STATUS.items():
