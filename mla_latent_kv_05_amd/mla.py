@@ -230,6 +230,63 @@ def append_kv(p: Params, c_new, kpe_new, block_table, seq_lens, c_kv, k_pe, kv_s
         _stream(stream)))
 
 
+class BoundCalls:
+    """The four calls of a decode step with their arguments checked and marshalled
+    once: each call afterwards is a bare ctypes call (the library still validates
+    the parameters on every call).  The tensors must stay alive and in place."""
+
+    def __init__(self, p: Params, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
+                 W_UK, W_UV, q_abs, o_part, lse_part, o_latent, lse, out, stream=None):
+        rows = (p.B, p.Sq, p.H)
+        if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+            raise ValueError("block_table and seq_lens must be int32")
+        self.p = p
+        pp = ctypes.byref(p)
+        st = _stream(stream)
+        L = lib()
+        self._calls = (
+            (L.mla_absorb_q, (pp, _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
+                              _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
+                              _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype), st)),
+            (L.mla_decode_splitkv, (pp, _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype),
+                                    _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
+                                    _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+                                    _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+                                    _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+                                    _ptr(block_table, "block_table", (p.B, p.max_pages)),
+                                    _ptr(seq_lens, "seq_lens", (p.B,)),
+                                    _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                    _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32), st)),
+            (L.mla_combine_lse, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                 _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
+                                 _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
+                                 _ptr(lse, "lse_out", rows, F32), st)),
+            (L.mla_up_v, (pp, _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
+                          _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+                          _ptr(out, "out", rows + (p.d_h,), p.out_dtype), st)),
+        )
+
+    def absorb_q(self):
+        f, a = self._calls[0]
+        _check(f(*a))
+
+    def decode_splitkv(self):
+        f, a = self._calls[1]
+        _check(f(*a))
+
+    def combine_lse(self):
+        f, a = self._calls[2]
+        _check(f(*a))
+
+    def up_v(self):
+        f, a = self._calls[3]
+        _check(f(*a))
+
+    def __call__(self):
+        for f, a in self._calls:
+            _check(f(*a))
+
+
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 
 
@@ -246,6 +303,12 @@ class DecodeStep:
         self.o_latent = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
         self.lse = torch.empty(rows, dtype=torch.float32, device=device)
         self.out = torch.empty(rows + (p.d_h,), dtype=_TORCH[p.out_dtype], device=device)
+
+    def bind(self, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
+             stream=None) -> BoundCalls:
+        """The four calls on these inputs, marshalled once (see BoundCalls)."""
+        return BoundCalls(self.p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
+                          self.q_abs, self.o_part, self.lse_part, self.o_latent, self.lse, self.out, stream)
 
     def __call__(self, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
                  stream=None):

@@ -364,3 +364,23 @@ def test_full_size_sampled(wl_name, n_seq, n_heads):
     note(f"  sampled out err {e:.3e}")
     assert e <= tol_of(wl)
     assert np.abs(got_l[rows] - lse).max() <= 2e-3
+
+
+def test_bound_calls_match_unbound():
+    """The pre-marshalled calls the bench uses give bit-identical results to the
+    per-call binding (same kernels, same arguments)."""
+    wl = I.workload("v3_b64", B=5)
+    case = I.make_case(wl, seq_lens=[1, 64, 700, 3000, 5000])
+    validate(case)
+    p = params_for(case, plan=True)
+    dc = DeviceCase(case)
+    note("bound calls vs per-call binding")
+    st = dc.step(p)
+    torch.cuda.synchronize()
+    ref = st.out.clone()
+    st.out.zero_()
+    b = st.bind(dc.q_nope, dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table, dc.seq_lens, dc.W_UK, dc.W_UV)
+    b()
+    b()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, ref)
