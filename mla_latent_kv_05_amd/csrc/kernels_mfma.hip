@@ -150,15 +150,16 @@ __global__ __launch_bounds__(256) void up_v_mfma_kernel(
         lds_store<u32x4>(sm + rr * 1024 + ((c ^ (rr & 15)) << 4), v);
     }
     __syncthreads();
-    f32x4 acc[2][2];                              // [dt][rt]
+    constexpr int kRt = kUpRows / 16;             // 16-row tiles
+    f32x4 acc[2][kRt];                            // [dt][rt]
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < kRt; ++rt) acc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kDc / 32; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < kRt; ++rt) {
             const int rr = rt * 16 + r16, c = ks * 4 + g;
             const bf16x8 bo = as_bf16x8(lds_load<u32x4>(sm + rr * 1024 + ((c ^ (rr & 15)) << 4)));
 #pragma unroll
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void up_v_mfma_kernel(
         }
     // acc[dt][rt][j]: row r0 + rt*16 + r16, d = d0 + dt*16 + 4g + j
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < kRt; ++rt) {
         const int r = r0 + rt * 16 + r16;
         if (r >= R) continue;
         const int64_t base = (static_cast<int64_t>(r) * p.H + h) * kDh + d0;
