@@ -228,6 +228,65 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
                            const int32_t *seq_lens, void *c_kv, void *k_pe, float *kv_scale,
                            void *stream);
 
+/*
+ * The non-absorbed path, for many new tokens per sequence (prefill, chunked
+ * prefill).  "MLA Matrix Absorption" sec. 6 describes the switch: with x new tokens
+ * per sequence at or above a threshold (about 64) the per-head keys and values are
+ * decompressed from the latent cache and a standard attention runs; below it the
+ * absorbed path (the four calls above) wins.  "DeepSeek-MLA-Principle" eqs. (2),
+ * (4), (10): k_{t,h} = [W_UK[h] c_t ; k_pe_t], v_{t,h} = W_UV[h] c_t.  Both paths
+ * compute the same attention (absorption is an exact re-association).
+ *
+ * These entry points take Sq = x new tokens per sequence with 1 <= x <= 65536
+ * (token s of sequence b at position seq_lens[b] - x + s, as for the decode).
+ * Kernels exist for d_h = 128, d_c = 512, d_r = 64 with bf16 queries, weights,
+ * latent cache and RoPE keys; other requests return MLA_ERR_UNSUPPORTED.
+ * Lmax = max_pages * 64 is the row stride of the decompressed tensors.
+ */
+
+/*
+ * mla_decompress_kv -- per-head keys (content part) and values of every cached
+ * position t < seq_lens[b]:
+ *   k_nope[b, t, h, d] = sum_m W_UK[h,d,m] c_t[m]
+ *   v_t[b, h, d, t]    = sum_m W_UV[h,d,m] c_t[m]      (values stored transposed)
+ * accumulated in fp32, rounded once to latent_dtype.  Positions at or past
+ * seq_lens[b] are not written.
+ *
+ *   c_kv, block_table, seq_lens   as for mla_decode_splitkv (bf16 cache)
+ *   W_UK, W_UV  [H,d_h,d_c]         w_dtype        (in)
+ *   k_nope      [B,Lmax,H,d_h]      latent_dtype   (out)
+ *   v_t         [B,H,d_h,Lmax]      latent_dtype   (out)
+ */
+mla_status_t mla_decompress_kv(const mla_params_t *p, const void *c_kv, const int32_t *block_table,
+                               const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *k_nope,
+                               void *v_t, void *stream);
+
+/*
+ * mla_prefill_attention -- standard causal attention of the Sq new tokens of
+ * every sequence with the decompressed keys and values: for row (b,s,h),
+ * n = seq_lens[b] - Sq + 1 + s visible positions,
+ *   z_t = scale * (q_nope[b,s,h,:] . k_nope[b,t,h,:] + q_rope[b,s,h,:] . k_pe_t),  t < n
+ *   out[b,s,h,:] = sum_{t<n} softmax(z)_t v[b,t,h,:]
+ * (out = 0 when n <= 0).  The weights are rounded to bf16 for the value product
+ * and the sum is normalised by the weights as rounded.
+ *
+ *   q_nope [B,Sq,H,d_h], q_rope [B,Sq,H,d_r]   q_dtype       (in)
+ *   k_nope [B,Lmax,H,d_h], v_t [B,H,d_h,Lmax]  latent_dtype  (in: from mla_decompress_kv)
+ *   k_pe, block_table, seq_lens                as for mla_decode_splitkv
+ *   out    [B,Sq,H,d_h]                        out_dtype     (out)
+ */
+mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, const void *q_rope,
+                                   const void *k_nope, const void *v_t, const void *k_pe,
+                                   const int32_t *block_table, const int32_t *seq_lens, void *out,
+                                   void *stream);
+
+/* The switch of "MLA Matrix Absorption" sec. 6 (host-only): 1 when Sq new tokens
+ * per sequence are served by the absorbed path, 0 when by the non-absorbed one;
+ * -1 for invalid parameters.  The pages put the crossover near 64; the absorbed
+ * kernels here take at most 16 new tokens per sequence, so the switch is at
+ * Sq <= 16 (both paths accept 1 <= Sq <= 16 and agree there). */
+int32_t mla_prefer_absorbed(const mla_params_t *p);
+
 /* Host-only validation of *p (no GPU needed).  Returns MLA_OK or the first error. */
 mla_status_t mla_check_params(const mla_params_t *p);
 

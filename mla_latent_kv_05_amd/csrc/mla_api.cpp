@@ -31,10 +31,16 @@ mla_status_t fail(mla_status_t s, const char *fmt, ...) {
 
 bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
-mla_status_t check(const mla_params_t *p) {
+// new tokens per sequence: at most kMaxAbsorbedSq on the absorbed path, kMaxPrefill on
+// the non-absorbed one
+constexpr int kMaxAbsorbedSq = 16;
+constexpr int kMaxPrefill = 65536;
+
+mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
     if (!p) return fail(MLA_ERR_NULL, "params is NULL");
-    if (p->B < 1 || p->Sq < 1 || p->Sq > 16 || p->H < 1)
-        return fail(MLA_ERR_SHAPE, "need B >= 1, 1 <= Sq <= 16, H >= 1 (got B=%d Sq=%d H=%d)", p->B, p->Sq, p->H);
+    if (p->B < 1 || p->Sq < 1 || p->Sq > max_sq || p->H < 1)
+        return fail(MLA_ERR_SHAPE, "need B >= 1, 1 <= Sq <= %d, H >= 1 (got B=%d Sq=%d H=%d)", max_sq, p->B, p->Sq,
+                    p->H);
     if (p->d_h < 1 || p->d_h > 256 || p->d_c < 1 || p->d_c > 1024 || p->d_r < 0 || p->d_r > 256)
         return fail(MLA_ERR_SHAPE, "need 1<=d_h<=256, 1<=d_c<=1024, 0<=d_r<=256 (got %d, %d, %d)", p->d_h, p->d_c, p->d_r);
     if (p->page_size != 64) return fail(MLA_ERR_SHAPE, "page_size must be 64 (got %d)", p->page_size);
@@ -216,6 +222,47 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
     return hip_status(mla::launch_append(*p, c_new, kpe_new, q_rope_in, q_rope_out, block_table, seq_lens, c_kv, k_pe,
                                          kv_scale, st),
                       "mla_append_kv launch");
+}
+
+int32_t mla_prefer_absorbed(const mla_params_t *p) {
+    if (check(p, kMaxPrefill) != MLA_OK) return -1;
+    return p->Sq <= kMaxAbsorbedSq ? 1 : 0;
+}
+
+mla_status_t mla_decompress_kv(const mla_params_t *p, const void *c_kv, const int32_t *block_table,
+                               const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *k_nope,
+                               void *v_t, void *stream) {
+    mla_status_t s = check(p, kMaxPrefill);
+    if (s != MLA_OK) return s;
+    if (!c_kv || !block_table || !seq_lens || !W_UK || !W_UV || !k_nope || !v_t)
+        return fail(MLA_ERR_NULL, "mla_decompress_kv: NULL tensor pointer");
+    if (!mla::prefill_supported(*p))
+        return fail(MLA_ERR_UNSUPPORTED, "mla_decompress_kv: kernels exist for d_h=128, d_c=512, d_r=64 with bf16 "
+                                         "weights, cache and latent");
+    if ((int64_t)p->B * p->max_pages * 2 * ((p->H + 7) / 8) > 0x7fffffffll)
+        return fail(MLA_ERR_SHAPE, "mla_decompress_kv: grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_decompress(*p, c_kv, block_table, seq_lens, W_UK, W_UV, k_nope, v_t, st),
+                      "mla_decompress_kv launch");
+}
+
+mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, const void *q_rope,
+                                   const void *k_nope, const void *v_t, const void *k_pe,
+                                   const int32_t *block_table, const int32_t *seq_lens, void *out,
+                                   void *stream) {
+    mla_status_t s = check(p, kMaxPrefill);
+    if (s != MLA_OK) return s;
+    if (!q_nope || !q_rope || !k_nope || !v_t || !k_pe || !block_table || !seq_lens || !out)
+        return fail(MLA_ERR_NULL, "mla_prefill_attention: NULL tensor pointer");
+    if (!mla::prefill_supported(*p))
+        return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_attention: kernels exist for d_h=128, d_c=512, d_r=64 with "
+                                         "bf16 queries, weights, cache and latent");
+    if ((int64_t)p->B * p->H * ((p->Sq + 127) / 128) > 0x7fffffffll)
+        return fail(MLA_ERR_SHAPE, "mla_prefill_attention: grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_prefill_attention(*p, q_nope, q_rope, k_nope, v_t, k_pe, block_table, seq_lens,
+                                                    out, st),
+                      "mla_prefill_attention launch");
 }
 
 }  // extern "C"

@@ -49,6 +49,16 @@ hipError_t launch_append(const mla_params_t &p, const void *c_new, const void *k
                          void *q_rope_out, const int32_t *block_table, const int32_t *seq_lens, void *c_kv,
                          void *k_pe, float *kv_scale, hipStream_t stream);
 
+// non-absorbed path for many new tokens (kernels_prefill.hip)
+bool prefill_supported(const mla_params_t &p);
+hipError_t launch_decompress(const mla_params_t &p, const void *c_kv, const int32_t *block_table,
+                             const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *k_nope, void *v_t,
+                             hipStream_t stream);
+hipError_t launch_prefill_attention(const mla_params_t &p, const void *q_nope, const void *q_rope,
+                                    const void *k_nope, const void *v_t, const void *k_pe,
+                                    const int32_t *block_table, const int32_t *seq_lens, void *out,
+                                    hipStream_t stream);
+
 // Heads x query rows handled by one attention workgroup of the MFMA kernel.
 constexpr int kDecodeRowsPerBlock = 64;
 

@@ -26,7 +26,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v",
-           "mla_append_kv", "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
+           "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed",
+           "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
 
@@ -77,6 +78,8 @@ def lib():
             ("mla_combine_lse", [PP, P, P, P, P, P]),
             ("mla_up_v", [PP, P, P, P, P]),
             ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
+            ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
+            ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
             ("mla_check_params", [PP]),
             ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
         ):
@@ -89,6 +92,8 @@ def lib():
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_error.argtypes = []
         L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_prefer_absorbed.argtypes = [PP]
+        L.mla_prefer_absorbed.restype = ctypes.c_int32
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = ctypes.c_int32
         if L.mla_abi_version() != 2:
@@ -227,6 +232,59 @@ def append_kv(p: Params, c_new, kpe_new, block_table, seq_lens, c_kv, k_pe, kv_s
         _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
         _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
         _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+        _stream(stream)))
+
+
+def prefer_absorbed(p: Params) -> bool:
+    """The switch of "MLA Matrix Absorption" sec. 6: True when p.Sq new tokens per
+    sequence are served by the absorbed path (the four decode calls), False when by
+    decompress_kv + prefill_attention."""
+    r = lib().mla_prefer_absorbed(ctypes.byref(p))
+    if r < 0:
+        raise MLAError(2, lib().mla_last_error().decode())
+    return bool(r)
+
+
+def lmax(p: Params) -> int:
+    """Row stride (positions) of the decompressed keys and values."""
+    return p.max_pages * PAGE
+
+
+def decompress_kv(p: Params, c_kv, block_table, seq_lens, W_UK, W_UV, k_nope, v_t, stream=None) -> None:
+    """Per-head keys k_nope [B, Lmax, H, d_h] and transposed values v_t [B, H, d_h, Lmax]
+    of every cached position (non-absorbed path)."""
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    L = lmax(p)
+    _check(lib().mla_decompress_kv(
+        ctypes.byref(p),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(k_nope, "k_nope", (p.B, L, p.H, p.d_h), p.latent_dtype),
+        _ptr(v_t, "v_t", (p.B, p.H, p.d_h, L), p.latent_dtype),
+        _stream(stream)))
+
+
+def prefill_attention(p: Params, q_nope, q_rope, k_nope, v_t, k_pe, block_table, seq_lens, out,
+                      stream=None) -> None:
+    """Causal attention of the p.Sq new tokens with the decompressed keys and values."""
+    rows = (p.B, p.Sq, p.H)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    L = lmax(p)
+    _check(lib().mla_prefill_attention(
+        ctypes.byref(p),
+        _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
+        _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
+        _ptr(k_nope, "k_nope", (p.B, L, p.H, p.d_h), p.latent_dtype),
+        _ptr(v_t, "v_t", (p.B, p.H, p.d_h, L), p.latent_dtype),
+        _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
         _stream(stream)))
 
 

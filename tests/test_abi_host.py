@@ -122,6 +122,24 @@ def test_append_arguments_rejected_without_launch():
     assert "even" in L.mla_last_error().decode()
 
 
+def test_prefill_entry_points_validate_on_the_host():
+    """The non-absorbed entry points accept many new tokens, report shapes without a
+    kernel as unsupported, and check pointers before launching."""
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    p = v3(Sq=4096)
+    assert mla.lib().mla_check_params(ctypes.byref(p)) == 2          # too many rows for the absorbed path
+    assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=16))
+    assert not mla.prefer_absorbed(v3(Sq=17)) and not mla.prefer_absorbed(p)
+    assert L.mla_decompress_kv(ctypes.byref(p), d, d, d, d, d, d, None, None) == 1
+    assert L.mla_prefill_attention(ctypes.byref(p), d, d, d, d, d, d, d, None, None) == 1
+    q = v3(Sq=128, d_c=256)
+    assert L.mla_decompress_kv(ctypes.byref(q), d, d, d, d, d, d, d, None) == 6
+    assert L.mla_prefill_attention(ctypes.byref(q), d, d, d, d, d, d, d, d, None) == 6
+    bad = v3(Sq=70000)
+    assert L.mla_prefill_attention(ctypes.byref(bad), d, d, d, d, d, d, d, d, None) == 2
+
+
 def test_status_strings():
     L = mla.lib()
     for code, name in mla.STATUS.items():
