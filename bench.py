@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="v3_b64")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this size (for scaling HBM counters)")
@@ -150,6 +152,7 @@ def main():
         torch.cuda.synchronize()
 
     append = append_bench(mla, A, wl, p, reps[0], dev, stream, args)
+    prefill = None if args.no_prefill else prefill_bench(mla, A, dev, stream, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -192,6 +195,7 @@ def main():
         "step_roofline": {"bytes": cost.total_bytes, "flops": cost.flops, "t_roof_us": round(roofline_us, 2),
                           "frac": round(roofline_us / (ms_step * 1e3), 4)},
         "append": append,
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
@@ -255,6 +259,76 @@ def append_bench(mla, A, wl, p, t, dev, stream, args):
                      "tokens": Bb * Sqb, "us": round(us_bulk, 2), "bytes": nbytes,
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def prefill_bench(mla, A, dev, stream, args, B=4, x=4096):
+    """The non-absorbed path (mla_decompress_kv + mla_prefill_attention) timed on its
+    own: whole-prompt prefill of B sequences of x tokens (seq_len = x new tokens),
+    DeepSeek-V3 head shapes, bf16, permuted pages, bf16 output.  Inputs are drawn
+    on the device (normal(0, 1) activations, cache and RoPE keys; weights
+    normal(0, 0.02)).  Each kernel's average launch duration comes from an event
+    pair around each launch on its stream."""
+    import numpy as np
+    import torch
+
+    H, d_h, d_c, d_r = 128, 128, 512, 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    pages = B * ((x + 63) // 64)
+    mp = (x + 63) // 64
+    perm = np.random.default_rng(2024).permutation(pages).astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(B, mp)).to(dev)
+    sl = torch.full((B,), x, dtype=torch.int32, device=dev)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=g, device=dev) * std).bfloat16()
+
+    c_kv, k_pe = rnd(pages, 64, d_c), rnd(pages, 64, d_r)
+    W_UK, W_UV = rnd(H, d_h, d_c, std=0.02), rnd(H, d_h, d_c, std=0.02)
+    q_nope, q_rope = rnd(B, x, H, d_h), rnd(B, x, H, d_r)
+    pp = mla.make_params(B, x, H, d_h, d_c, d_r, pages, mp, out_dtype=mla.BF16)
+    L = mla.lmax(pp)
+    kn = torch.empty((B, L, H, d_h), dtype=torch.bfloat16, device=dev)
+    vt = torch.empty((B, H, d_h, L), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, x, H, d_h), dtype=torch.bfloat16, device=dev)
+
+    def dec():
+        mla.decompress_kv(pp, c_kv, bt, sl, W_UK, W_UV, kn, vt, stream)
+
+    def att():
+        mla.prefill_attention(pp, q_nope, q_rope, kn, vt, k_pe, bt, sl, out, stream)
+
+    for _ in range(2):
+        dec()
+        att()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "non-finite prefill output"
+    n = args.prefill_reps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        dec()
+        ev[i][1].record(stream)
+        att()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    d_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+    a_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+    cost = A.prefill_cost(x, H, d_h, d_c, d_r, [x] * B, out_fmt="bf16")
+
+    def roof(flops, us):
+        t = flops / (us * 1e-6) / 1e12
+        return {"us": round(us, 1), "flops": flops, "achieved": round(t, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(t / BF16_PEAK_TFLOPS, 4)}
+
+    tot = cost.decompress_flops + cost.attention_flops
+    return {"workload": f"whole-prompt prefill, B={B} sequences x {x} new tokens (seq_len {x}), H={H}, "
+                        f"d_h={d_h}, d_c={d_c}, d_r={d_r}, bf16, permuted pages, bf16 out",
+            "tokens_per_s": round(B * x / ((d_us + a_us) * 1e-6), 0),
+            "bound": "mfma",
+            "decompress": roof(cost.decompress_flops, d_us),
+            "attention": roof(cost.attention_flops, a_us),
+            "path": roof(tot, d_us + a_us)}
 
 
 def measured_traffic(workload: str):

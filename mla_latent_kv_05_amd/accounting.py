@@ -99,3 +99,39 @@ def append_bytes(tokens: int, H: int, d_c: int, d_r: int, in_fmt: str = "bf16", 
     if with_query:
         per_tok += 2 * H * d_r * a
     return tokens * per_tok
+
+
+def visible_pairs(seq_lens, Sq: int) -> int:
+    """visible_positions in closed form: row s of a sequence of n tokens sees
+    max(0, n - Sq + 1 + s) positions."""
+    tot = 0
+    for n in seq_lens:
+        lo = max(0, int(n) - Sq + 1)          # positions seen by row 0 (or the first row that sees any)
+        hi = int(n)                            # positions seen by the last row
+        if hi <= 0:
+            continue
+        first = max(lo, 1)
+        tot += (first + hi) * (hi - first + 1) // 2
+    return tot
+
+
+@dataclasses.dataclass
+class PrefillCost:
+    decompress_flops: int   # K and V of every cached position, every head
+    attention_flops: int    # scores (d_h + d_r) and values (d_h) of every visible pair
+    decompress_bytes: int   # latent rows read, K and V written (bf16)
+    attention_bytes: int    # Q read, K, V, k_pe read once, output written
+
+
+def prefill_cost(Sq: int, H: int, d_h: int, d_c: int, d_r: int, seq_lens, out_fmt: str = "bf16") -> PrefillCost:
+    """Algorithmic FLOP/bytes of the non-absorbed path ("MLA Matrix Absorption"
+    sec. 6): decompression 2 * 2*H*d_h*d_c per cached position, attention
+    2*H*(2*d_h + d_r) per visible (query, position) pair (causal pairs only)."""
+    tokens = sum(int(n) for n in seq_lens)
+    rows = len(seq_lens) * Sq * H
+    pairs = visible_pairs(seq_lens, Sq)
+    dflops = 2 * 2 * H * d_h * d_c * tokens
+    aflops = 2 * H * (2 * d_h + d_r) * pairs
+    dbytes = tokens * (2 * d_c + 2 * 2 * H * d_h)
+    abytes = rows * (d_h + d_r) * 2 + tokens * (2 * 2 * H * d_h + 2 * d_r) + rows * d_h * FORMAT_BYTES[out_fmt]
+    return PrefillCost(dflops, aflops, dbytes, abytes)

@@ -18,17 +18,20 @@
 // consecutive latent values per lane), so each value row lands contiguous along
 // t.  The weights are read from L2.
 //
-// Attention: one workgroup (4 waves) per (sequence, head, 128 new tokens); wave w
-// takes 32 of them.  Per tile of 32 positions:
-//   S^T[t, q] = K_tile . Q^T over the 192 dims (12 MFMAs; Q^T in registers).  Tile
-//   row r holds position swap23(r) (bits 2 and 3 of r exchanged), so that the 16
-//   weights a lane holds for query q are, as the B operand of the next product,
-//   positions 16ks + 8g + e in order;
-//   online softmax per query in the exp2 domain (a lane pair per query);
-//   O^T[d, q] += V^T[d, t] . P^T[t, q] (8 MFMAs; V^T rows read 16 bytes at a time
-//   from the transposed values).
-// Positions at or past seq_len inside the last tile are masked in the scores and
-// zeroed in the value operand (the decompressed tensors are not written there).
+// Attention: one workgroup (8 waves) per (sequence, head, 256 new tokens); wave w
+// takes 32 of them.  Keys and transposed values of 64 positions (one page) at a
+// time are staged in LDS once per workgroup, double-buffered, and read by every
+// wave.  Per staged tile and wave:
+//   S^T[t, q] = K_tile . Q^T over the 192 dims (2 x 12 MFMAs; Q^T in registers).
+//   Tile row r of each 32-row half holds position swap23(r) (bits 2 and 3 of r
+//   exchanged), so that the 16 weights a lane holds for query q are, as the B
+//   operand of the value product, positions 16ks + 8g + e in order;
+//   online softmax per query in the exp2 domain (a lane pair per query); the
+//   running maximum only moves when exceeded by more than 2^8, so the rescale of
+//   the accumulators is skipped on most tiles;
+//   O^T[d, q] += V^T[d, t] . P^T[t, q] (16 MFMAs).
+// Positions past a query's own or past seq_len are masked in the scores; values
+// past seq_len (never written) are zeroed when staged.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -44,7 +47,6 @@ constexpr int kDh = 128;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kHeadsPerWg = 8;                 // heads of one decompress workgroup
-constexpr int kQPerWg = 128;                   // new tokens of one attention workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
@@ -118,125 +120,227 @@ __global__ __launch_bounds__(256) void decompress_kernel(const mla_params_t p, c
 }
 
 // ---------------------------------------------------------------------------
+// Attention: one workgroup of 8 waves per (sequence, head, 256 new tokens); wave
+// w takes 32 of them.  Keys ([content ; RoPE], 192 dims) and transposed values of
+// 64 positions at a time are staged once per workgroup in LDS (two stages: the
+// next tile's global loads are in flight while the current one is used) and read
+// by all 8 waves.
+constexpr int kQWaves = 8;
+constexpr int kQPerWg = 32 * kQWaves;                // new tokens of one workgroup
+constexpr int kKvTile = 64;                          // positions of one stage
+constexpr int kKStride = 2 * (kDh + kDr) + 16;       // bytes per key row in LDS (padded: no bank conflicts)
+constexpr int kVStride = 2 * kKvTile + 16;           // bytes per value row in LDS (padded)
+constexpr int kKBytes = kKvTile * kKStride;
+constexpr int kStageBytes = kKBytes + kDh * kVStride;
+constexpr float kRescaleLog2 = 8.f;                  // running maximum moves when exceeded by more than this
+
 template <bool kOutBf16>
-__global__ __launch_bounds__(256) void prefill_attention_kernel(
+__global__ __launch_bounds__(512) void prefill_attention_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_nope, const uint16_t *__restrict__ q_rope,
     const uint16_t *__restrict__ k_nope, const uint16_t *__restrict__ v_t, const uint16_t *__restrict__ k_pe,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, void *__restrict__ out) {
-    const int lane = threadIdx.x & 63, t32 = lane & 31, g = lane >> 5;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
+    const int tid = threadIdx.x, lane = tid & 63, t32 = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_qb = (p.Sq + kQPerWg - 1) / kQPerWg;
     const int64_t lmax = static_cast<int64_t>(p.max_pages) * 64;
-    int64_t bid = blockIdx.x;
-    const int qb = static_cast<int>(bid % n_qb);
-    bid /= n_qb;
-    const int h = static_cast<int>(bid % p.H);
-    const int b = static_cast<int>(bid / p.H);
-    const int s0 = qb * kQPerWg + 32 * w;      // this wave's first new token
-    if (s0 >= p.Sq) return;
+    // Block order: the blocks of one (sequence, head) are consecutive and the
+    // heaviest (latest new tokens) first; with a multiple of 8 blocks, XCD x (which
+    // receives blocks x, x+8, ...) gets one contiguous range of that order, so the
+    // blocks sharing a head's keys and values run together on one L2.
+    const int64_t nblk = gridDim.x;
+    int64_t lb = blockIdx.x;
+    if ((nblk & 7) == 0) lb = (lb & 7) * (nblk >> 3) + (lb >> 3);
+    const int qb = n_qb - 1 - static_cast<int>(lb % n_qb);
+    lb /= n_qb;
+    const int h = static_cast<int>(lb % p.H);
+    const int b = static_cast<int>(lb / p.H);
     const int L = seq_lens[b];
-    const int base = L - p.Sq;                 // position of new token 0
-    const int s = s0 + t32;                    // this lane's query
+    const int base = L - p.Sq;                           // position of new token 0
+    const int q0 = qb * kQPerWg;
+    const int s0 = q0 + 32 * w;                          // this wave's first new token
+    const int s = s0 + t32;                              // this lane's query
     const bool q_ok = s < p.Sq;
-    const int pos_q = base + s;                // last visible position of the query
-    // last visible position of any query of the wave (uniform)
-    const int pos_max = __builtin_amdgcn_readfirstlane(base + min(s0 + 31, p.Sq - 1));
-    const int64_t qrow = (static_cast<int64_t>(b) * p.Sq + (q_ok ? s : s0)) * p.H + h;
+    const int pos_q = base + s;                          // last position the query sees
+    const int pos_wave = base + min(s0 + 31, p.Sq - 1);  // last position any query of the wave sees
+    const int pos_wg = base + min(q0 + kQPerWg - 1, p.Sq - 1);
+    const int n_tiles = pos_wg >= 0 ? pos_wg / kKvTile + 1 : 0;
+
     // Q^T (B operand): k-steps 0..7 the content dims, 8..11 the RoPE dims
     bf16x8 qreg[12];
+    {
+        const int64_t qrow = (static_cast<int64_t>(b) * p.Sq + (q_ok ? s : 0)) * p.H + h;
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (q_ok) {
-            if (ks < 8) v = *reinterpret_cast<const u32x4 *>(q_nope + qrow * kDh + ks * 16 + g * 8);
-            else v = *reinterpret_cast<const u32x4 *>(q_rope + qrow * kDr + (ks - 8) * 16 + g * 8);
+        for (int ks = 0; ks < 12; ++ks) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (q_ok) {
+                if (ks < 8) v = *reinterpret_cast<const u32x4 *>(q_nope + qrow * kDh + ks * 16 + g * 8);
+                else v = *reinterpret_cast<const u32x4 *>(q_rope + qrow * kDr + (ks - 8) * 16 + g * 8);
+            }
+            qreg[ks] = as_bf16x8(v);
         }
-        qreg[ks] = as_bf16x8(v);
     }
+
+    // Staging: thread tid moves five 16-byte chunks per tile: key content rows
+    // tid/16 and 32 + tid/16 (part tid%16), the RoPE key of row tid/8 (part tid%8),
+    // and value rows tid/8 and 64 + tid/8 (positions 8 (tid%8) ..).
+    const int32_t *bt = block_table + static_cast<int64_t>(b) * p.max_pages;
+    const uint16_t *kbase = k_nope + (static_cast<int64_t>(b) * lmax * p.H + h) * kDh;
+    const uint16_t *vbase = v_t + (static_cast<int64_t>(b) * p.H + h) * kDh * lmax;
+    const int kr = tid >> 4, kc = tid & 15, rr = tid >> 3, rc = tid & 7;
+    u32x4 stg[5];
+    // a tile is one page: its RoPE keys are rows of page `page` (rows past the
+    // sequence end read its last position instead)
+    auto load_tile = [&](int k0, int page) {
+        const int t_a = min(k0 + kr, L - 1), t_b = min(k0 + 32 + kr, L - 1), t_r = min(k0 + rr, L - 1);
+        stg[0] = *reinterpret_cast<const u32x4 *>(kbase + static_cast<int64_t>(t_a) * p.H * kDh + kc * 8);
+        stg[1] = *reinterpret_cast<const u32x4 *>(kbase + static_cast<int64_t>(t_b) * p.H * kDh + kc * 8);
+        const int64_t prow = static_cast<int64_t>(page) * 64 + (t_r & 63);
+        stg[2] = *reinterpret_cast<const u32x4 *>(k_pe + prow * kDr + rc * 8);
+        const int pv = k0 + rc * 8;                      // within the row: k0 + 64 <= lmax
+        stg[3] = *reinterpret_cast<const u32x4 *>(vbase + static_cast<int64_t>(rr) * lmax + pv);
+        stg[4] = *reinterpret_cast<const u32x4 *>(vbase + static_cast<int64_t>(64 + rr) * lmax + pv);
+    };
+    const uint32_t lds0 = lds_addr(lds);
+    auto store_tile = [&](int k0, int stage) {
+        const int pv = k0 + rc * 8;
+        if (pv + 8 > L) {                                // values past the sequence end are never written
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t keep = (pv + 2 * e2 < L ? 0x0000ffffu : 0u) | (pv + 2 * e2 + 1 < L ? 0xffff0000u : 0u);
+                stg[3][e2] &= keep;
+                stg[4][e2] &= keep;
+            }
+        }
+        const uint32_t st = lds0 + stage * kStageBytes;
+        lds_store<u32x4>(st + kr * kKStride + kc * 16, stg[0]);
+        lds_store<u32x4>(st + (32 + kr) * kKStride + kc * 16, stg[1]);
+        lds_store<u32x4>(st + rr * kKStride + 2 * kDh + rc * 16, stg[2]);
+        lds_store<u32x4>(st + kKBytes + rr * kVStride + rc * 16, stg[3]);
+        lds_store<u32x4>(st + kKBytes + (64 + rr) * kVStride + rc * 16, stg[4]);
+    };
+
     const float zscale = p.scale * kLog2e;
-    float m_run = -INFINITY;                   // running maximum (log2 domain), same in the lane pair
-    float l_run = 0.f;                         // this lane's share of the sum of bf16-rounded weights
-    f32x16 o[4];                               // O^T tiles: dims 32dt .., query t32
+    float m_run = -INFINITY;                             // running maximum (log2 domain), same in the lane pair
+    float l_run = 0.f;                                   // this lane's share of the sum of bf16-rounded weights
+    f32x16 o[4];                                         // O^T tiles: dims 32dt + .., query t32
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
-    const uint16_t *vrow = v_t + ((static_cast<int64_t>(b) * p.H + h) * kDh + t32) * lmax;   // + 32dt*lmax
-    const int32_t *bt = block_table + static_cast<int64_t>(b) * p.max_pages;
-    const int n_tiles = pos_max >= 0 ? pos_max / 32 + 1 : 0;
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int k0 = kt * 32;
-        // K operand: tile row t32 holds position k0 + swap23(t32)
-        const int key = k0 + swap23(t32);
-        const bool key_ok = key < L;
-        const int kk = key_ok ? key : L - 1;
-        const uint16_t *krow = k_nope + ((static_cast<int64_t>(b) * lmax + kk) * p.H + h) * kDh + g * 8;
-        const int64_t prow = static_cast<int64_t>(bt[kk / 64]) * 64 + kk % 64;
-        const uint16_t *rrow = k_pe + prow * kDr + g * 8;
-        f32x16 sacc;
+    // key operand rows of this lane: tile rows swap23(t32) and 32 + swap23(t32)
+    const uint32_t k_off = swap23(t32) * kKStride + g * 16;
+    const uint32_t v_off = kKBytes + t32 * kVStride + g * 16;
+
+    if (n_tiles == 0) {                                  // no new token of the block sees any position
+        if (q_ok) {
+            const int64_t orow = ((static_cast<int64_t>(b) * p.Sq + s) * p.H + h) * kDh;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < 12; ++ks) {
-            const u32x4 a = ks < 8 ? *reinterpret_cast<const u32x4 *>(krow + ks * 16)
-                                   : *reinterpret_cast<const u32x4 *>(rrow + (ks - 8) * 16);
-            sacc = mfma32(as_bf16x8(a), qreg[ks], sacc);
-        }
-        // sacc[j]: position k0 + swap23(8(j/4) + 4g + j%4) = k0 + 16(j/8) + 8g + (j%8), query t32
-        float sc[16];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int pos = k0 + 16 * (j >> 3) + 8 * g + (j & 7);
-            sc[j] = (pos <= pos_q && pos < L) ? sacc[j] * zscale : -INFINITY;
-            mloc = fmaxf(mloc, sc[j]);
-        }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // nothing visible yet: weights 0
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 0 on the first visible tile
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-        // weights, rounded to bf16 for the value product; B operand of k-step kp:
-        // positions k0 + 16kp + 8g + e, e < 8
-        uint32_t pk[2][4];
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[8 * kp + 2 * e2] - m_use);
-                const float p1 = __builtin_amdgcn_exp2f(sc[8 * kp + 2 * e2 + 1] - m_use);
-                const uint32_t pr = cvt_pk_bf16(p0, p1);
-                pk[kp][e2] = pr;
-                l_run += __uint_as_float(pr << 16) + __uint_as_float(pr & 0xffff0000u);
-            }
-        // O^T += V^T . P^T: A operand of dim tile dt, k-step kp: dims 32dt + t32,
-        // positions k0 + 16kp + 8g .. +7 (zero past the sequence end)
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            const int pv0 = k0 + 16 * kp + 8 * g;
-            const bf16x8 pb = as_bf16x8(u32x4{pk[kp][0], pk[kp][1], pk[kp][2], pk[kp][3]});
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                u32x4 va = *reinterpret_cast<const u32x4 *>(vrow + static_cast<int64_t>(32 * dt) * lmax + pv0);
-                if (pv0 + 8 > L) {
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const uint32_t lo_ok = pv0 + 2 * e2 < L ? 0x0000ffffu : 0u;
-                        const uint32_t hi_ok = pv0 + 2 * e2 + 1 < L ? 0xffff0000u : 0u;
-                        va[e2] &= lo_ok | hi_ok;
-                    }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * dt + 8 * q4 + 4 * g;
+                    if constexpr (kOutBf16) *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(out) + orow + d0) = u32x2{0u, 0u};
+                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + orow + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                o[dt] = mfma32(as_bf16x8(va), pb, o[dt]);
+        }
+        return;
+    }
+    load_tile(0, bt[0]);
+    int page_next = n_tiles > 1 ? bt[1] : 0;             // page of the next tile, read one tile ahead
+    store_tile(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        const int k0 = kt * kKvTile;
+        const bool more = kt + 1 < n_tiles;
+        if (more) load_tile(k0 + kKvTile, page_next);
+        if (s0 < p.Sq && k0 <= pos_wave) {
+            const uint32_t st = lds0 + (kt & 1) * kStageBytes;
+            // S^T[t, q] for positions k0 + 32ps + swap23(row)
+            f32x16 sacc[2];
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sacc[ps][j] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks)
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps) {
+                    const u32x4 a = lds_load<u32x4>(st + k_off + ps * 32 * kKStride + ks * 32);
+                    sacc[ps] = mfma32(as_bf16x8(a), qreg[ks], sacc[ps]);
+                }
+            // sacc[ps][j]: position k0 + 32ps + 16(j/8) + 8g + (j%8), query s
+            float mt = -INFINITY;
+            if (k0 + kKvTile - 1 > base + s0 || k0 + kKvTile > L) {
+                // the tile reaches past the first query's position or the sequence end
+                const int lim = min(pos_q, L - 1) - (k0 + 8 * g);
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int rel = 32 * ps + 16 * (j >> 3) + (j & 7);
+                        const float z = rel <= lim ? sacc[ps][j] * zscale : -INFINITY;
+                        sacc[ps][j] = z;
+                        mt = fmaxf(mt, z);
+                    }
+            } else {
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float z = sacc[ps][j] * zscale;
+                        sacc[ps][j] = z;
+                        mt = fmaxf(mt, z);
+                    }
+            }
+            mt = pair_max(mt);
+            // the running maximum moves only when this tile's exceeds it by more than
+            // kRescaleLog2, so the weights stay below 2^kRescaleLog2 and the rescale of
+            // the accumulators is skipped on most tiles
+            const bool grow = mt > m_run + kRescaleLog2;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;   // 0 the first time
+                m_run = grow ? mt : m_run;
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;    // nothing visible yet: weights 0
+            // weights rounded to bf16; k-step kk of the value product takes positions
+            // 16kk + 8g + e, which are sacc[kk/2][8(kk%2) + e]
+            uint32_t pk[4][4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int j = 8 * (kk & 1) + 2 * e2;
+                    const uint32_t pr = cvt_pk_bf16(__builtin_amdgcn_exp2f(sacc[kk >> 1][j] - m_use),
+                                                    __builtin_amdgcn_exp2f(sacc[kk >> 1][j + 1] - m_use));
+                    pk[kk][e2] = pr;
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
+                                                            bf16x2{(__bf16)1.f, (__bf16)1.f}, l_run, false);
+                }
+            // O^T[d, q] += V^T[d, t] . P^T[t, q]
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 pb = as_bf16x8(u32x4{pk[kk][0], pk[kk][1], pk[kk][2], pk[kk][3]});
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const u32x4 a = lds_load<u32x4>(st + v_off + dt * 32 * kVStride + kk * 32);
+                    o[dt] = mfma32(as_bf16x8(a), pb, o[dt]);
+                }
             }
         }
+        if (more) {
+            page_next = kt + 2 < n_tiles ? bt[kt + 2] : 0;
+            store_tile(k0 + kKvTile, (kt + 1) & 1);
+        }
+        __syncthreads();
     }
     if (!q_ok) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // o[dt][j]: dim 32dt + 8(j/4) + 4g + j%4, query s
     const int64_t orow = ((static_cast<int64_t>(b) * p.Sq + s) * p.H + h) * kDh;
@@ -285,10 +389,10 @@ hipError_t launch_prefill_attention(const mla_params_t &p, const void *q_nope, c
     const auto vt = static_cast<const uint16_t *>(v_t);
     const auto kp = static_cast<const uint16_t *>(k_pe);
     if (p.out_dtype == MLA_BF16)
-        hipLaunchKernelGGL(prefill_attention_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(prefill_attention_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                            p, qn, qr, kn, vt, kp, block_table, seq_lens, out);
     else
-        hipLaunchKernelGGL(prefill_attention_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(prefill_attention_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
                            p, qn, qr, kn, vt, kp, block_table, seq_lens, out);
     return hipGetLastError();
 }

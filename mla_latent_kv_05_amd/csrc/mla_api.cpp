@@ -257,7 +257,7 @@ mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, co
     if (!mla::prefill_supported(*p))
         return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_attention: kernels exist for d_h=128, d_c=512, d_r=64 with "
                                          "bf16 queries, weights, cache and latent");
-    if ((int64_t)p->B * p->H * ((p->Sq + 127) / 128) > 0x7fffffffll)
+    if ((int64_t)p->B * p->H * ((p->Sq + 255) / 256) > 0x7fffffffll)
         return fail(MLA_ERR_SHAPE, "mla_prefill_attention: grid too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     return hip_status(mla::launch_prefill_attention(*p, q_nope, q_rope, k_nope, v_t, k_pe, block_table, seq_lens,
