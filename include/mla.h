@@ -241,7 +241,8 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
  * (token s of sequence b at position seq_lens[b] - x + s, as for the decode).
  * Kernels exist for d_h = 128, d_c = 512, d_r = 64 with bf16 queries, weights,
  * latent cache and RoPE keys; other requests return MLA_ERR_UNSUPPORTED.
- * Lmax = max_pages * 64 is the row stride of the decompressed tensors.
+ * Lmax = mla_prefill_lmax(p) (max_pages * 64 rounded up to a multiple of 256) is
+ * the row stride of the decompressed tensors.
  */
 
 /*
@@ -249,8 +250,9 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
  * position t < seq_lens[b]:
  *   k_nope[b, t, h, d] = sum_m W_UK[h,d,m] c_t[m]
  *   v_t[b, h, d, t]    = sum_m W_UV[h,d,m] c_t[m]      (values stored transposed)
- * accumulated in fp32, rounded once to latent_dtype.  Positions at or past
- * seq_lens[b] are not written.
+ * accumulated in fp32, rounded once to latent_dtype.  Positions from seq_lens[b]
+ * up to the next multiple of 256 are written with zeros; later positions are not
+ * written.
  *
  *   c_kv, block_table, seq_lens   as for mla_decode_splitkv (bf16 cache)
  *   W_UK, W_UV  [H,d_h,d_c]         w_dtype        (in)
@@ -279,6 +281,10 @@ mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, co
                                    const void *k_nope, const void *v_t, const void *k_pe,
                                    const int32_t *block_table, const int32_t *seq_lens, void *out,
                                    void *stream);
+
+/* Row stride Lmax (positions) of the decompressed tensors for *p: max_pages * 64
+ * rounded up to a multiple of 256 (host-only; -1 for invalid parameters). */
+int64_t mla_prefill_lmax(const mla_params_t *p);
 
 /* The switch of "MLA Matrix Absorption" sec. 6 (host-only): 1 when Sq new tokens
  * per sequence are served by the absorbed path, 0 when by the non-absorbed one;

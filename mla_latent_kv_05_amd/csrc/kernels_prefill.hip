@@ -9,14 +9,19 @@
 // of head h at position t is [W_UK[h] c_t ; k_pe_t], its value W_UV[h] c_t, the
 // score scale 1/sqrt(d_h + d_r), and row s attends to positions t <= its own.
 //
-// Decompress: one workgroup (4 waves) per (sequence, 32-position tile, group of 8
-// heads).  Every wave holds the tile's latent rows as MFMA operands (128 VGPRs)
-// and, for each head of the group, forms its 32 output dims of the keys
-// K[t, d] = c_t . W_UK[h, d, :] and of the transposed values V^T[d, t] =
-// W_UV[h, d, :] . c_t: the latent row is the A operand of the first product and
-// the B operand of the second, with the same register contents (both read 8
-// consecutive latent values per lane), so each value row lands contiguous along
-// t.  The weights are read from L2.
+// Decompress: one workgroup (4 waves) per (group of 16 heads, sequence, 128
+// positions); wave w holds the latent rows of 32 of the positions as MFMA operands
+// (128 VGPRs) for the whole workgroup.  The weights of each head stream through
+// LDS in chunks of 64 latent dims (double-buffered, shared by the 4 waves), first
+// W_UK[h] then W_UV[h]:
+//   keys:   D[d, t] = W_UK[h] . c^T (weight rows as the A operand, latent rows as B),
+//   values: D[t, d] = c . W_UV[h]^T (latent rows as A, weight rows as B),
+// the latent registers serving both roles unchanged (both operands take 8
+// consecutive latent dims per lane).  A-operand rows are taken in swap23 order,
+// so each lane ends with 8 consecutive output rows twice per 32-row tile: the keys
+// are written 8 dims (16 bytes) and the transposed values 8 positions at a time.
+// Blocks are ordered head group first, and with a multiple of 8 blocks XCD x gets
+// one contiguous range, so each XCD's L2 serves few head groups' weights.
 //
 // Attention: one workgroup (8 waves) per (sequence, head, 256 new tokens); wave w
 // takes 32 of them.  Keys and transposed values of 64 positions (one page) at a
@@ -46,76 +51,166 @@ using namespace gfx;
 constexpr int kDh = 128;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kHeadsPerWg = 8;                 // heads of one decompress workgroup
+constexpr int kDecHeads = 16;                  // heads of one decompress workgroup
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecPos = 32 * kDecWaves;        // positions of one decompress workgroup (32 per wave)
+constexpr int kDecRows = 64;                   // weight rows (output dims) of one pass
+constexpr int kWChunk = 128;                   // latent dims of one staged weight chunk
+constexpr int kWStride = 2 * kWChunk + 16;     // bytes per staged weight row (padded: no bank conflicts)
+constexpr int kWStage = kDecRows * kWStride;
+static_assert(kDecPos == 256, "prefill_lmax rounds the row stride to whole decompression tiles");
+constexpr int kDecDepth = 2;                   // weight chunks in flight ahead of the one in use
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);           // round to nearest even (finite values)
-    return static_cast<uint16_t>(u >> 16);
-}
 
 // tile row r holds position swap23(r) of the tile
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void decompress_kernel(const mla_params_t p, const uint16_t *__restrict__ c_kv,
-                                                         const int32_t *__restrict__ block_table,
-                                                         const int32_t *__restrict__ seq_lens,
-                                                         const uint16_t *__restrict__ W_UK,
-                                                         const uint16_t *__restrict__ W_UV,
-                                                         uint16_t *__restrict__ k_nope, uint16_t *__restrict__ v_t) {
-    const int lane = threadIdx.x & 63, t32 = lane & 31, g = lane >> 5;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n_hg = (p.H + kHeadsPerWg - 1) / kHeadsPerWg;
-    const int64_t lmax = static_cast<int64_t>(p.max_pages) * 64;
-    const int tiles = p.max_pages * 2;
-    int64_t bid = blockIdx.x;
-    const int hg = static_cast<int>(bid % n_hg);
-    bid /= n_hg;
-    const int tile = static_cast<int>(bid % tiles);
-    const int b = static_cast<int>(bid / tiles);
+__global__ __launch_bounds__(kDecThreads) void decompress_kernel(
+    const mla_params_t p, const uint16_t *__restrict__ c_kv, const int32_t *__restrict__ block_table,
+    const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ W_UK, const uint16_t *__restrict__ W_UV,
+    uint16_t *__restrict__ k_nope, uint16_t *__restrict__ v_t) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kWStage];
+    const int tid = threadIdx.x, lane = tid & 63, t32 = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t lmax = prefill_lmax(p);               // a multiple of kDecPos
+    const int n_pt = static_cast<int>(lmax / kDecPos);
+    const int64_t nblk = gridDim.x;
+    int64_t lb = blockIdx.x;
+    if ((nblk & 7) == 0) lb = (lb & 7) * (nblk >> 3) + (lb >> 3);
+    const int pt = static_cast<int>(lb % n_pt);
+    lb /= n_pt;
+    const int b = static_cast<int>(lb % p.B);
+    const int hg = static_cast<int>(lb / p.B);
     const int L = seq_lens[b];
-    const int t0 = tile * 32;
+    const int t0 = pt * kDecPos;
     if (t0 >= L) return;
-    // the latent row of position t0 + t32: dims 16ks + 8g .. 16ks + 8g + 7
-    const int t = t0 + t32;
-    const bool valid = t < L;
-    int64_t crow = 0;
-    if (valid) crow = static_cast<int64_t>(block_table[static_cast<int64_t>(b) * p.max_pages + t / 64]) * 64 + t % 64;
+    // this lane's latent row: position t0 + 32w + swap23(t32), dims 16ks + 8g .. +7
+    const int tw = t0 + 32 * w;
+    const int pos = tw + swap23(t32);
+    const bool valid = pos < L;
     bf16x8 cop[kDc / 16];
-#pragma unroll
-    for (int ks = 0; ks < kDc / 16; ++ks) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (valid) v = *reinterpret_cast<const u32x4 *>(c_kv + crow * kDc + ks * 16 + g * 8);
-        cop[ks] = as_bf16x8(v);
-    }
-    const int d = 32 * w + t32;                // this lane's weight row (operand) / output dim
-    for (int hh = 0; hh < kHeadsPerWg; ++hh) {
-        const int h = hg * kHeadsPerWg + hh;
-        if (h >= p.H) break;
-        const uint16_t *wk = W_UK + (static_cast<int64_t>(h) * kDh + d) * kDc + g * 8;
-        const uint16_t *wv = W_UV + (static_cast<int64_t>(h) * kDh + d) * kDc + g * 8;
-        f32x16 ak, av;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            ak[j] = 0.f;
-            av[j] = 0.f;
-        }
+    {
+        int64_t crow = 0;
+        if (valid) crow = static_cast<int64_t>(block_table[static_cast<int64_t>(b) * p.max_pages + pos / 64]) * 64 + pos % 64;
 #pragma unroll
         for (int ks = 0; ks < kDc / 16; ++ks) {
-            const bf16x8 bk = as_bf16x8(*reinterpret_cast<const u32x4 *>(wk + ks * 16));
-            const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4 *>(wv + ks * 16));
-            ak = mfma32(cop[ks], bk, ak);      // D[position, d]
-            av = mfma32(bv, cop[ks], av);      // D[d, position]
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (valid) v = *reinterpret_cast<const u32x4 *>(c_kv + crow * kDc + ks * 16 + g * 8);
+            cop[ks] = as_bf16x8(v);
         }
-        // ak[j]: position t0 + 8(j/4) + 4g + j%4, dim d;  av[j]: dim 32w + 8(j/4) + 4g + j%4, position t
+    }
+
+    // staging: thread tid moves 16 bytes (8 latent dims) of kStgPass weight rows
+    constexpr int kPartsPerRow = kWChunk / 8;
+    constexpr int kRowsPerPass = kDecThreads / kPartsPerRow;
+    constexpr int kStgPass = kDecRows / kRowsPerPass;
+    const int sr = tid / kPartsPerRow, sp = tid % kPartsPerRow;
+    const uint32_t lds0 = lds_addr(lds);
+    // kDecDepth register sets: the chunk kDecDepth stages ahead is in flight
+    u32x4 stg[kDecDepth][kStgPass];
+    auto load_w = [&](int set, const uint16_t *Wrows, int kc) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = 8 * (j >> 2) + 4 * g + (j & 3);
-            if (t0 + r < L) k_nope[((static_cast<int64_t>(b) * lmax + t0 + r) * p.H + h) * kDh + d] = bf16_bits(ak[j]);
-            if (valid) v_t[((static_cast<int64_t>(b) * p.H + h) * kDh + 32 * w + r) * lmax + t] = bf16_bits(av[j]);
+        for (int i = 0; i < kStgPass; ++i)
+            stg[set][i] = *reinterpret_cast<const u32x4 *>(Wrows + static_cast<int64_t>(sr + kRowsPerPass * i) * kDc +
+                                                           kc * kWChunk + sp * 8);
+    };
+    auto settle = [&]() {
+#pragma unroll
+        for (int j = 0; j < kDecDepth; ++j)
+#pragma unroll
+            for (int i = 0; i < kStgPass; ++i) asm volatile("" ::"v"(stg[j][i]));
+    };
+    auto store_w = [&](int set, int buf) {
+#pragma unroll
+        for (int i = 0; i < kStgPass; ++i)
+            lds_store<u32x4>(lds0 + buf * kWStage + (sr + kRowsPerPass * i) * kWStride + sp * 16, stg[set][i]);
+    };
+    // passes: (head, keys | values, row half); pass ps covers rows kDecRows*(ps % 2) ..
+    constexpr int kHalves = kDh / kDecRows;
+    const int h0 = hg * kDecHeads;
+    const int n_ps = 2 * kHalves * min(kDecHeads, p.H - h0);
+    constexpr int kChunks = kDc / kWChunk;               // stages per pass; stage s uses LDS buffer s % 2
+    const int n_st = n_ps * kChunks;
+    auto wrows = [&](int ps) {
+        const int hk = ps / kHalves;
+        return ((hk & 1) ? W_UV : W_UK) + (static_cast<int64_t>(h0 + (hk >> 1)) * kDh + kDecRows * (ps % kHalves)) * kDc;
+    };
+    const uint32_t a_row = swap23(t32) * kWStride + g * 16;   // weight rows as the A operand (keys)
+    const uint32_t b_row = t32 * kWStride + g * 16;           // weight rows as the B operand (values)
+
+#pragma unroll
+    for (int i = 0; i < kDecDepth; ++i) load_w(i, wrows(0), i);
+    store_w(0, 0);
+    settle();                                            // nothing in flight on entry, as after every pass
+    __syncthreads();
+    for (int ps = 0; ps < n_ps; ++ps) {
+        const bool is_v = (ps / kHalves) & 1;
+        f32x16 acc[kDecRows / 32];
+#pragma unroll
+        for (int dt = 0; dt < kDecRows / 32; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[dt][j] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < kChunks; ++kc) {
+            const int st = ps * kChunks + kc;
+            // stage st + kDecDepth into register set st % kDecDepth (its previous
+            // contents, stage st, are already in LDS); unconditional (the last stage is
+            // re-read past the end) so that the wait before the store below counts only
+            // the older loads
+            const int st2 = min(st + kDecDepth, n_st - 1);
+            load_w(kc % kDecDepth, wrows(st2 / kChunks), st2 % kChunks);
+            const uint32_t buf = lds0 + (kc & 1) * kWStage;
+            if (is_v) {
+#pragma unroll
+                for (int ks = 0; ks < kWChunk / 16; ++ks)
+#pragma unroll
+                    for (int dt = 0; dt < kDecRows / 32; ++dt) {
+                        const u32x4 wb = lds_load<u32x4>(buf + b_row + dt * 32 * kWStride + ks * 32);
+                        acc[dt] = mfma32(cop[kc * (kWChunk / 16) + ks], as_bf16x8(wb), acc[dt]);
+                    }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < kWChunk / 16; ++ks)
+#pragma unroll
+                    for (int dt = 0; dt < kDecRows / 32; ++dt) {
+                        const u32x4 wa = lds_load<u32x4>(buf + a_row + dt * 32 * kWStride + ks * 32);
+                        acc[dt] = mfma32(as_bf16x8(wa), cop[kc * (kWChunk / 16) + ks], acc[dt]);
+                    }
+            }
+            if (st + 1 < n_st) store_w((kc + 1) % kDecDepth, (kc + 1) & 1);
+            __syncthreads();
         }
+        // The weight chunk in flight was issued a stage ago: wait for it here, before
+        // the output stores, so that no later wait for it also waits for them (the
+        // empty asm consumes the staging registers, which makes the compiler wait).
+        settle();
+        const int h = h0 + ps / (2 * kHalves);
+        const int d_base = kDecRows * (ps % kHalves);
+        // acc[dt][8hf + e]: keys: dim d_base + 32dt + 16hf + 8g + e of position pos;
+        //                   values: position tw + 16hf + 8g + e of dim d_base + 32dt + t32
+#pragma unroll
+        for (int dt = 0; dt < kDecRows / 32; ++dt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const u32x4 v = u32x4{cvt_pk_bf16(acc[dt][8 * hf], acc[dt][8 * hf + 1]),
+                                      cvt_pk_bf16(acc[dt][8 * hf + 2], acc[dt][8 * hf + 3]),
+                                      cvt_pk_bf16(acc[dt][8 * hf + 4], acc[dt][8 * hf + 5]),
+                                      cvt_pk_bf16(acc[dt][8 * hf + 6], acc[dt][8 * hf + 7])};
+                // unconditional (positions past seq_len hold zero latents, so their rows
+                // are written as zeros; the tile ends inside lmax): the compiler then
+                // counts these stores, and the wait for the next weight chunk does not
+                // wait for them
+                if (!is_v) {
+                    *reinterpret_cast<u32x4 *>(k_nope + ((static_cast<int64_t>(b) * lmax + pos) * p.H + h) * kDh +
+                                               d_base + 32 * dt + 16 * hf + 8 * g) = v;
+                } else {
+                    *reinterpret_cast<u32x4 *>(v_t + ((static_cast<int64_t>(b) * p.H + h) * kDh + d_base + 32 * dt + t32) *
+                                                         lmax +
+                                               tw + 16 * hf + 8 * g) = v;
+                }
+            }
     }
 }
 
@@ -143,7 +238,7 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
     const int tid = threadIdx.x, lane = tid & 63, t32 = lane & 31, g = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_qb = (p.Sq + kQPerWg - 1) / kQPerWg;
-    const int64_t lmax = static_cast<int64_t>(p.max_pages) * 64;
+    const int64_t lmax = prefill_lmax(p);
     // Block order: the blocks of one (sequence, head) are consecutive and the
     // heaviest (latest new tokens) first; with a multiple of 8 blocks, XCD x (which
     // receives blocks x, x+8, ...) gets one contiguous range of that order, so the
@@ -369,9 +464,10 @@ bool prefill_supported(const mla_params_t &p) {
 hipError_t launch_decompress(const mla_params_t &p, const void *c_kv, const int32_t *block_table,
                              const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *k_nope, void *v_t,
                              hipStream_t stream) {
-    const int64_t n_hg = (p.H + kHeadsPerWg - 1) / kHeadsPerWg;
-    const int64_t blocks = static_cast<int64_t>(p.B) * p.max_pages * 2 * n_hg;
-    hipLaunchKernelGGL(decompress_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p,
+    const int64_t n_hg = (p.H + kDecHeads - 1) / kDecHeads;
+    const int64_t n_pt = (static_cast<int64_t>(p.max_pages) * 64 + kDecPos - 1) / kDecPos;
+    const int64_t blocks = n_hg * p.B * n_pt;
+    hipLaunchKernelGGL(decompress_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kDecThreads), 0, stream, p,
                        static_cast<const uint16_t *>(c_kv), block_table, seq_lens,
                        static_cast<const uint16_t *>(W_UK), static_cast<const uint16_t *>(W_UV),
                        static_cast<uint16_t *>(k_nope), static_cast<uint16_t *>(v_t));

@@ -224,6 +224,11 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
                       "mla_append_kv launch");
 }
 
+int64_t mla_prefill_lmax(const mla_params_t *p) {
+    if (check(p, kMaxPrefill) != MLA_OK) return -1;
+    return mla::prefill_lmax(*p);
+}
+
 int32_t mla_prefer_absorbed(const mla_params_t *p) {
     if (check(p, kMaxPrefill) != MLA_OK) return -1;
     return p->Sq <= kMaxAbsorbedSq ? 1 : 0;
@@ -239,7 +244,7 @@ mla_status_t mla_decompress_kv(const mla_params_t *p, const void *c_kv, const in
     if (!mla::prefill_supported(*p))
         return fail(MLA_ERR_UNSUPPORTED, "mla_decompress_kv: kernels exist for d_h=128, d_c=512, d_r=64 with bf16 "
                                          "weights, cache and latent");
-    if ((int64_t)p->B * p->max_pages * 2 * ((p->H + 7) / 8) > 0x7fffffffll)
+    if ((int64_t)p->B * ((p->max_pages + 3) / 4) * ((p->H + 15) / 16) > 0x7fffffffll)
         return fail(MLA_ERR_SHAPE, "mla_decompress_kv: grid too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     return hip_status(mla::launch_decompress(*p, c_kv, block_table, seq_lens, W_UK, W_UV, k_nope, v_t, st),

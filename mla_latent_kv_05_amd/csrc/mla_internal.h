@@ -51,6 +51,9 @@ hipError_t launch_append(const mla_params_t &p, const void *c_new, const void *k
 
 // non-absorbed path for many new tokens (kernels_prefill.hip)
 bool prefill_supported(const mla_params_t &p);
+// Row stride (positions) of the decompressed keys and values: max_pages * 64 rounded
+// up to a whole number of 256-position decompression tiles.
+__host__ __device__ inline int64_t prefill_lmax(const mla_params_t &p) { return (static_cast<int64_t>(p.max_pages) * 64 + 255) / 256 * 256; }
 hipError_t launch_decompress(const mla_params_t &p, const void *c_kv, const int32_t *block_table,
                              const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *k_nope, void *v_t,
                              hipStream_t stream);

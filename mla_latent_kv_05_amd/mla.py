@@ -26,7 +26,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v",
-           "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed",
+           "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax",
            "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
@@ -92,6 +92,8 @@ def lib():
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_error.argtypes = []
         L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_prefill_lmax.argtypes = [PP]
+        L.mla_prefill_lmax.restype = ctypes.c_int64
         L.mla_prefer_absorbed.argtypes = [PP]
         L.mla_prefer_absorbed.restype = ctypes.c_int32
         L.mla_abi_version.argtypes = []
@@ -246,8 +248,12 @@ def prefer_absorbed(p: Params) -> bool:
 
 
 def lmax(p: Params) -> int:
-    """Row stride (positions) of the decompressed keys and values."""
-    return p.max_pages * PAGE
+    """Row stride (positions) of the decompressed keys and values: max_pages * 64
+    rounded up to a multiple of 256."""
+    r = lib().mla_prefill_lmax(ctypes.byref(p))
+    if r < 0:
+        raise MLAError(2, lib().mla_last_error().decode())
+    return int(r)
 
 
 def decompress_kv(p: Params, c_kv, block_table, seq_lens, W_UK, W_UV, k_nope, v_t, stream=None) -> None:

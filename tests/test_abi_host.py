@@ -129,6 +129,7 @@ def test_prefill_entry_points_validate_on_the_host():
     d = ctypes.c_void_p(0x1000)
     p = v3(Sq=4096)
     assert mla.lib().mla_check_params(ctypes.byref(p)) == 2          # too many rows for the absorbed path
+    assert [mla.lmax(v3(Sq=64, max_pages=n)) for n in (1, 4, 5, 8, 9)] == [256, 256, 512, 512, 768]
     assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=16))
     assert not mla.prefer_absorbed(v3(Sq=17)) and not mla.prefer_absorbed(p)
     assert L.mla_decompress_kv(ctypes.byref(p), d, d, d, d, d, d, None, None) == 1

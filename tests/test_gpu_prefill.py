@@ -9,7 +9,8 @@ tests pin to the non-absorbed definition.  The error is taken per row because th
 rows see from one to thousands of positions: a row that sees one position returns
 that position's value row (bf16-rounded), whose size is that of a single value,
 while rows averaging many positions are smaller.  Rows that see nothing are 0
-exactly.  Positions at or past seq_len are never written.
+exactly.  Decompressed positions from seq_len to the next multiple of 256 are
+zeros and later ones are never written.
 """
 import sys
 
@@ -87,7 +88,9 @@ def check_decompressed(case, kn, vt):
         K, V = PF.decompress_kv(PF.sequence_latents(c, case.block_table.numpy()[b], L), wuk, wuv)
         assert_bf16_rounding(knd[b, :L], K, acc_rel=1e-4)
         assert_bf16_rounding(vtd[b, :, :, :L], V.transpose(1, 2, 0), acc_rel=1e-4)
-        assert (knd[b, L:] == SENT).all() and (vtd[b, :, :, L:] == SENT).all()
+        Lz = -(-L // 256) * 256
+        assert (knd[b, L:Lz] == 0).all() and (vtd[b, :, :, L:Lz] == 0).all()
+        assert (knd[b, Lz:] == SENT).all() and (vtd[b, :, :, Lz:] == SENT).all()
 
 
 @pytest.mark.parametrize("B,Sq,lens", [
