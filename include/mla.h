@@ -10,6 +10,7 @@
  *   mla_decode_splitkv  per split c: scores, softmax, latent sum -> (O_c, lse_c)
  *   mla_combine_lse     log-sum-exp merge of the splits   -> o_latent (+ lse)
  *   mla_up_v            out    = o_latent . W_UV^T        (value up-projection)
+ *   mla_combine_up_v    the last two in one launch
  *
  * Sources ("the pages"): "MLA 矩阵吸收 & 吸收分离 原理详解" (MLA Matrix
  * Absorption), sections 2.1, 4.1, 4.2; "DeepSeek-MLA-Principle", section 2
@@ -189,6 +190,25 @@ mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const f
  */
 mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W_UV,
                       void *out, void *stream);
+
+/*
+ * mla_combine_up_v -- mla_combine_lse followed by mla_up_v in one launch, the
+ * merged latent rows kept on chip: the fusion of the decode step's tail that the
+ * value absorption allows ("DeepSeek-MLA-Principle", matrix absorption 3) (2):
+ * the up-projection needs only the merged latent row of its own query row).
+ * The merged rows are rounded to bf16 as mla_combine_lse rounds o_latent, and
+ * the result is bit for bit that of the two calls with latent_dtype = bf16.
+ * Kernels exist for d_h = 128, d_c = 512, bf16 weights and latent_dtype = bf16;
+ * other parameters return MLA_ERR_UNSUPPORTED.
+ *
+ *   o_part   [B,Sq,H,num_splits,d_c] fp32 (in)
+ *   lse_part [B,Sq,H,num_splits]     fp32 (in)
+ *   W_UV     [H,d_h,d_c]   w_dtype      (in)
+ *   out      [B,Sq,H,d_h]  out_dtype    (out)
+ *   lse_out  [B,Sq,H] fp32 (out; may be NULL)
+ */
+mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const float *lse_part, const void *W_UV,
+                              void *out, float *lse_out, void *stream);
 
 /*
  * mla_append_kv -- write the Sq new tokens of every sequence into the paged

@@ -252,7 +252,151 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
     if (lse_out && lane == 0) lse_out[row] = mx == -INFINITY ? -INFINITY : mx + __logf(sum);
 }
 
+// ---------------------------------------------------------------------------
+// mla_combine_up_v: the split merge and the up-projection in one launch, without
+// the merged latent rows leaving the chip.  One workgroup of 8 waves per (head,
+// 32-row chunk), as for up_v: wave w first merges rows 4w .. 4w+3 of the chunk
+// from their split partials (the arithmetic and order of combine_kernel_512, four
+// rows at a time so that their loads overlap), rounds them to bf16 into the
+// swizzled LDS layout of up_v, and then forms output dims 16w .. 16w+15 from its
+// weight rows, which were loaded before the merge.
+// ---------------------------------------------------------------------------
+constexpr int kCuRowsPerWave = kUpRows / 8;
+
+template <bool kOutBf16>
+__global__ __launch_bounds__(512) void combine_up_v_kernel(
+    const mla_params_t p, const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    const uint16_t *__restrict__ W_UV, void *__restrict__ out, float *__restrict__ lse_out) {
+    constexpr int kDh = 128;
+    __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2];
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int R = p.B * p.Sq;
+    const int n_rc = (R + kUpRows - 1) / kUpRows;
+    const int q = blockIdx.x >> 3;
+    const int rc = q % n_rc;
+    const int h = (q / n_rc) * 8 + (blockIdx.x & 7);
+    if (h >= p.H) return;                         // grid rounded up to 8 heads
+    const int r0 = rc * kUpRows;
+    const int d0 = w * 16;
+    const uint32_t sm = lds_addr(smem);
+    // this wave's weights (16 rows d0 ..), in flight during the merge
+    const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
+    bf16x8 wa[kDc / 32];
+#pragma unroll
+    for (int ks = 0; ks < kDc / 32; ++ks)
+        wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
+
+    // merge rows rr = 4w + i: lane owns latent columns 8 lane .. 8 lane + 7
+    const int S = p.num_splits;
+    int64_t row[kCuRowsPerWave];
+    bool ok[kCuRowsPerWave];
+    float mx[kCuRowsPerWave], sum[kCuRowsPerWave], acc[kCuRowsPerWave][8];
+#pragma unroll
+    for (int i = 0; i < kCuRowsPerWave; ++i) {
+        const int r = r0 + kCuRowsPerWave * w + i;
+        ok[i] = r < R;
+        row[i] = static_cast<int64_t>(ok[i] ? r : 0) * p.H + h;
+        mx[i] = -INFINITY;
+        sum[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    }
+    for (int c0 = 0; c0 < S; c0 += 64)
+#pragma unroll
+        for (int i = 0; i < kCuRowsPerWave; ++i)
+            mx[i] = fmaxf(mx[i], ok[i] && c0 + lane < S ? lse_part[row[i] * S + c0 + lane] : -INFINITY);
+#pragma unroll
+    for (int i = 0; i < kCuRowsPerWave; ++i) mx[i] = wave_max_f(mx[i]);
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        float wt[kCuRowsPerWave];
+        uint64_t live = 0;
+#pragma unroll
+        for (int i = 0; i < kCuRowsPerWave; ++i) {
+            const float lc = ok[i] && c0 + lane < S ? lse_part[row[i] * S + c0 + lane] : -INFINITY;
+            wt[i] = (lc == -INFINITY || mx[i] == -INFINITY) ? 0.f : __expf(lc - mx[i]);
+            sum[i] += wt[i];
+            live |= __builtin_amdgcn_ballot_w64(wt[i] != 0.f);
+        }
+        while (live) {
+            const int k = __builtin_ctzll(live);
+            live &= live - 1;
+#pragma unroll
+            for (int i = 0; i < kCuRowsPerWave; ++i) {
+                const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), k));
+                if (wk != 0.f) {
+                    const f32x4 *src = reinterpret_cast<const f32x4 *>(
+                        o_part + (row[i] * S + c0 + k) * static_cast<int64_t>(kDc) + lane * 8);
+                    const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] += wk * v0[j];
+                        acc[i][4 + j] += wk * v1[j];
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kCuRowsPerWave; ++i) {
+        const float tot = wave_sum_f(sum[i]);
+        const float inv = tot > 0.f ? 1.f / tot : 0.f;
+        const int rr = kCuRowsPerWave * w + i;
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[i][2 * k] * inv, acc[i][2 * k + 1] * inv);
+        lds_store<u32x4>(sm + rr * 1024 + ((lane ^ (rr & 15)) << 4), o);     // zero rows past R
+        if (lse_out && ok[i] && lane == 0) lse_out[row[i]] = mx[i] == -INFINITY ? -INFINITY : mx[i] + __logf(tot);
+    }
+    __syncthreads();
+
+    constexpr int kRt = kUpRows / 16;             // 16-row tiles
+    f32x4 acc2[kRt];
+#pragma unroll
+    for (int rt = 0; rt < kRt; ++rt) acc2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDc / 32; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < kRt; ++rt) {
+            const int rr = rt * 16 + r16, c = ks * 4 + g;
+            const bf16x8 bo = as_bf16x8(lds_load<u32x4>(sm + rr * 1024 + ((c ^ (rr & 15)) << 4)));
+            acc2[rt] = mfma16(wa[ks], bo, acc2[rt]);
+        }
+    // acc2[rt][j]: row r0 + rt*16 + r16, d = d0 + 4g + j
+#pragma unroll
+    for (int rt = 0; rt < kRt; ++rt) {
+        const int r = r0 + rt * 16 + r16;
+        if (r >= R) continue;
+        const int64_t base = (static_cast<int64_t>(r) * p.H + h) * kDh + d0 + g * 4;
+        if constexpr (kOutBf16) {
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(out) + base) =
+                u32x2{pack_bf16x2(acc2[rt][0], acc2[rt][1]), pack_bf16x2(acc2[rt][2], acc2[rt][3])};
+        } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + base) = acc2[rt];
+        }
+    }
+}
+
 }  // namespace
+
+bool combine_up_v_supported(const mla_params_t &p) {
+    if (p.flags & MLA_FLAG_GENERIC) return false;
+    return p.d_c == kDc && p.d_h == 128 && p.latent_dtype == MLA_BF16 && p.w_dtype == MLA_BF16;
+}
+
+hipError_t launch_combine_up_v(const mla_params_t &p, const float *o_part, const float *lse_part, const void *W_UV,
+                               void *out, float *lse_out, hipStream_t stream) {
+    const int64_t R = static_cast<int64_t>(p.B) * p.Sq;
+    const int64_t blocks = (static_cast<int64_t>(p.H) + 7) / 8 * 8 * ((R + kUpRows - 1) / kUpRows);
+    const auto w = static_cast<const uint16_t *>(W_UV);
+    if (p.out_dtype == MLA_BF16)
+        hipLaunchKernelGGL(combine_up_v_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, p,
+                           o_part, lse_part, w, out, lse_out);
+    else
+        hipLaunchKernelGGL(combine_up_v_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, p,
+                           o_part, lse_part, w, out, lse_out);
+    return hipGetLastError();
+}
 
 bool absorb_mfma_supported(const mla_params_t &p) {
     if (p.flags & MLA_FLAG_GENERIC) return false;

@@ -278,28 +278,29 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
 
     // Staging: thread tid moves five 16-byte chunks per tile: key content rows
     // tid/16 and 32 + tid/16 (part tid%16), the RoPE key of row tid/8 (part tid%8),
-    // and value rows tid/8 and 64 + tid/8 (positions 8 (tid%8) ..).
+    // and value rows tid/8 and 64 + tid/8 (positions 8 (tid%8) ..).  Every row of a
+    // tile lies inside lmax; rows past seq_len are masked in the scores (keys) or
+    // zeroed when staged (values), and a tile is one page, so its RoPE rows are
+    // rows of that page.
     const int32_t *bt = block_table + static_cast<int64_t>(b) * p.max_pages;
-    const uint16_t *kbase = k_nope + (static_cast<int64_t>(b) * lmax * p.H + h) * kDh;
-    const uint16_t *vbase = v_t + (static_cast<int64_t>(b) * p.H + h) * kDh * lmax;
     const int kr = tid >> 4, kc = tid & 15, rr = tid >> 3, rc = tid & 7;
+    const int64_t kstride = static_cast<int64_t>(p.H) * kDh;      // elements per key position
+    const uint16_t *kptr = k_nope + (static_cast<int64_t>(b) * lmax * p.H + h) * kDh + kr * kstride + kc * 8;
+    const uint16_t *vptr = v_t + ((static_cast<int64_t>(b) * p.H + h) * kDh + rr) * lmax + rc * 8;
+    const uint16_t *rptr = k_pe + rr * kDr + rc * 8;
     u32x4 stg[5];
-    // a tile is one page: its RoPE keys are rows of page `page` (rows past the
-    // sequence end read its last position instead)
     auto load_tile = [&](int k0, int page) {
-        const int t_a = min(k0 + kr, L - 1), t_b = min(k0 + 32 + kr, L - 1), t_r = min(k0 + rr, L - 1);
-        stg[0] = *reinterpret_cast<const u32x4 *>(kbase + static_cast<int64_t>(t_a) * p.H * kDh + kc * 8);
-        stg[1] = *reinterpret_cast<const u32x4 *>(kbase + static_cast<int64_t>(t_b) * p.H * kDh + kc * 8);
-        const int64_t prow = static_cast<int64_t>(page) * 64 + (t_r & 63);
-        stg[2] = *reinterpret_cast<const u32x4 *>(k_pe + prow * kDr + rc * 8);
-        const int pv = k0 + rc * 8;                      // within the row: k0 + 64 <= lmax
-        stg[3] = *reinterpret_cast<const u32x4 *>(vbase + static_cast<int64_t>(rr) * lmax + pv);
-        stg[4] = *reinterpret_cast<const u32x4 *>(vbase + static_cast<int64_t>(64 + rr) * lmax + pv);
+        const uint16_t *kp = kptr + k0 * kstride;
+        stg[0] = *reinterpret_cast<const u32x4 *>(kp);
+        stg[1] = *reinterpret_cast<const u32x4 *>(kp + 32 * kstride);
+        stg[2] = *reinterpret_cast<const u32x4 *>(rptr + static_cast<int64_t>(page) * 64 * kDr);
+        stg[3] = *reinterpret_cast<const u32x4 *>(vptr + k0);
+        stg[4] = *reinterpret_cast<const u32x4 *>(vptr + 64 * lmax + k0);
     };
     const uint32_t lds0 = lds_addr(lds);
     auto store_tile = [&](int k0, int stage) {
         const int pv = k0 + rc * 8;
-        if (pv + 8 > L) {                                // values past the sequence end are never written
+        if (pv + 8 > L) {                                // values past the sequence end: zeros (finite)
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 const uint32_t keep = (pv + 2 * e2 < L ? 0x0000ffffu : 0u) | (pv + 2 * e2 + 1 < L ? 0xffff0000u : 0u);
@@ -364,7 +365,8 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
                     const u32x4 a = lds_load<u32x4>(st + k_off + ps * 32 * kKStride + ks * 32);
                     sacc[ps] = mfma32(as_bf16x8(a), qreg[ks], sacc[ps]);
                 }
-            // sacc[ps][j]: position k0 + 32ps + 16(j/8) + 8g + (j%8), query s
+            // sacc[ps][j]: position k0 + 32ps + 16(j/8) + 8g + (j%8), query s; the
+            // maximum is taken on the raw scores (the scale is positive)
             float mt = -INFINITY;
             if (k0 + kKvTile - 1 > base + s0 || k0 + kKvTile > L) {
                 // the tile reaches past the first query's position or the sequence end
@@ -374,21 +376,16 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int rel = 32 * ps + 16 * (j >> 3) + (j & 7);
-                        const float z = rel <= lim ? sacc[ps][j] * zscale : -INFINITY;
-                        sacc[ps][j] = z;
-                        mt = fmaxf(mt, z);
+                        sacc[ps][j] = rel <= lim ? sacc[ps][j] : -INFINITY;
+                        mt = fmaxf(mt, sacc[ps][j]);
                     }
             } else {
 #pragma unroll
                 for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float z = sacc[ps][j] * zscale;
-                        sacc[ps][j] = z;
-                        mt = fmaxf(mt, z);
-                    }
+                    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[ps][j]);
             }
-            mt = pair_max(mt);
+            mt = pair_max(mt) * zscale;                  // log2 domain
             // the running maximum moves only when this tile's exceeds it by more than
             // kRescaleLog2, so the weights stay below 2^kRescaleLog2 and the rescale of
             // the accumulators is skipped on most tiles
@@ -402,17 +399,18 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
 #pragma unroll
                     for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
             }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;    // nothing visible yet: weights 0
-            // weights rounded to bf16; k-step kk of the value product takes positions
-            // 16kk + 8g + e, which are sacc[kk/2][8(kk%2) + e]
+            const float m_neg = m_run == -INFINITY ? 0.f : -m_run;   // nothing visible yet: weights 0
+            // weights exp2(scale * z - m), rounded to bf16; k-step kk of the value
+            // product takes positions 16kk + 8g + e, which are sacc[kk/2][8(kk%2) + e]
             uint32_t pk[4][4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const int j = 8 * (kk & 1) + 2 * e2;
-                    const uint32_t pr = cvt_pk_bf16(__builtin_amdgcn_exp2f(sacc[kk >> 1][j] - m_use),
-                                                    __builtin_amdgcn_exp2f(sacc[kk >> 1][j + 1] - m_use));
+                    const uint32_t pr =
+                        cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kk >> 1][j], zscale, m_neg)),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kk >> 1][j + 1], zscale, m_neg)));
                     pk[kk][e2] = pr;
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
                                                             bf16x2{(__bf16)1.f, (__bf16)1.f}, l_run, false);

@@ -205,6 +205,18 @@ mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W
     return hip_status(mla::launch_up_v_generic(*p, o_latent, W_UV, out, st), "mla_up_v launch");
 }
 
+mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const float *lse_part, const void *W_UV,
+                              void *out, float *lse_out, void *stream) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!o_part || !lse_part || !W_UV || !out) return fail(MLA_ERR_NULL, "mla_combine_up_v: NULL tensor pointer");
+    if (!mla::combine_up_v_supported(*p))
+        return fail(MLA_ERR_UNSUPPORTED, "mla_combine_up_v: kernels exist for d_h=128, d_c=512 with bf16 weights and "
+                                         "latent_dtype bf16");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_combine_up_v(*p, o_part, lse_part, W_UV, out, lse_out, st), "mla_combine_up_v launch");
+}
+
 mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void *kpe_new, const void *q_rope_in,
                            void *q_rope_out, const int32_t *block_table, const int32_t *seq_lens, void *c_kv,
                            void *k_pe, float *kv_scale, void *stream) {

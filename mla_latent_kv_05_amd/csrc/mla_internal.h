@@ -39,6 +39,9 @@ hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const v
                               void *q_abs, hipStream_t stream);
 bool up_v_mfma_supported(const mla_params_t &p);
 bool combine_fast_supported(const mla_params_t &p);
+bool combine_up_v_supported(const mla_params_t &p);
+hipError_t launch_combine_up_v(const mla_params_t &p, const float *o_part, const float *lse_part, const void *W_UV,
+                               void *out, float *lse_out, hipStream_t stream);
 hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,
                                void *o_latent, float *lse_out, hipStream_t stream);
 hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,

@@ -25,7 +25,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
           4: "MLA_ERR_SPLITS", 5: "MLA_ERR_HIP", 6: "MLA_ERR_UNSUPPORTED"}
 
 # every symbol include/mla.h declares
-EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v",
+EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
            "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax",
            "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
@@ -77,6 +77,7 @@ def lib():
             ("mla_decode_splitkv", [PP, P, P, P, P, P, P, P, P, P, P]),
             ("mla_combine_lse", [PP, P, P, P, P, P]),
             ("mla_up_v", [PP, P, P, P, P]),
+            ("mla_combine_up_v", [PP, P, P, P, P, P, P]),
             ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
             ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
             ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
@@ -216,6 +217,19 @@ def up_v(p: Params, o_latent, W_UV, out, stream=None) -> None:
                           _stream(stream)))
 
 
+def combine_up_v(p: Params, o_part, lse_part, W_UV, out, lse_out=None, stream=None) -> None:
+    """combine_lse followed by up_v in one launch (merged latent rows stay on chip)."""
+    rows = (p.B, p.Sq, p.H)
+    _check(lib().mla_combine_up_v(
+        ctypes.byref(p),
+        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+        _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
+        _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
+        _ptr(lse_out, "lse_out", rows, F32),
+        _stream(stream)))
+
+
 def append_kv(p: Params, c_new, kpe_new, block_table, seq_lens, c_kv, k_pe, kv_scale=None,
               q_rope_in=None, q_rope_out=None, stream=None) -> None:
     """Write the new tokens' latent rows and rotated RoPE keys into the cache
@@ -300,8 +314,9 @@ class BoundCalls:
     the parameters on every call).  The tensors must stay alive and in place."""
 
     def __init__(self, p: Params, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
-                 W_UK, W_UV, q_abs, o_part, lse_part, o_latent, lse, out, stream=None):
+                 W_UK, W_UV, q_abs, o_part, lse_part, o_latent, lse, out, stream=None, fused=False):
         rows = (p.B, p.Sq, p.H)
+        self.fused = fused
         if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
             raise ValueError("block_table and seq_lens must be int32")
         self.p = p
@@ -328,7 +343,13 @@ class BoundCalls:
             (L.mla_up_v, (pp, _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
                           _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
                           _ptr(out, "out", rows + (p.d_h,), p.out_dtype), st)),
+            (L.mla_combine_up_v, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                  _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
+                                  _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+                                  _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
+                                  _ptr(lse, "lse_out", rows, F32), st)),
         )
+        self._step = (self._calls[0], self._calls[1], self._calls[4]) if fused else self._calls[:4]
 
     def absorb_q(self):
         f, a = self._calls[0]
@@ -346,8 +367,12 @@ class BoundCalls:
         f, a = self._calls[3]
         _check(f(*a))
 
+    def combine_up_v(self):
+        f, a = self._calls[4]
+        _check(f(*a))
+
     def __call__(self):
-        for f, a in self._calls:
+        for f, a in self._step:
             _check(f(*a))
 
 
@@ -356,10 +381,12 @@ _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 
 class DecodeStep:
     """Owns the intermediates of one decode step (allocated once with torch) and
-    runs the four library calls on the current stream."""
+    runs the four library calls on the current stream (fused=True: absorb, decode
+    and the fused merge + up-projection; o_latent is then not written)."""
 
-    def __init__(self, p: Params, device="cuda"):
+    def __init__(self, p: Params, device="cuda", fused=False):
         self.p = p
+        self.fused = fused
         rows = (p.B, p.Sq, p.H)
         self.q_abs = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
         self.o_part = torch.empty(rows + (p.num_splits, p.d_c), dtype=torch.float32, device=device)
@@ -372,7 +399,8 @@ class DecodeStep:
              stream=None) -> BoundCalls:
         """The four calls on these inputs, marshalled once (see BoundCalls)."""
         return BoundCalls(self.p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
-                          self.q_abs, self.o_part, self.lse_part, self.o_latent, self.lse, self.out, stream)
+                          self.q_abs, self.o_part, self.lse_part, self.o_latent, self.lse, self.out, stream,
+                          fused=self.fused)
 
     def __call__(self, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
                  stream=None):
@@ -380,6 +408,9 @@ class DecodeStep:
         absorb_q(p, q_nope, W_UK, self.q_abs, stream)
         decode_splitkv(p, self.q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
                        self.o_part, self.lse_part, stream)
-        combine_lse(p, self.o_part, self.lse_part, self.o_latent, self.lse, stream)
-        up_v(p, self.o_latent, W_UV, self.out, stream)
+        if self.fused:
+            combine_up_v(p, self.o_part, self.lse_part, W_UV, self.out, self.lse, stream)
+        else:
+            combine_lse(p, self.o_part, self.lse_part, self.o_latent, self.lse, stream)
+            up_v(p, self.o_latent, W_UV, self.out, stream)
         return self.out

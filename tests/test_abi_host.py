@@ -141,6 +141,18 @@ def test_prefill_entry_points_validate_on_the_host():
     assert L.mla_prefill_attention(ctypes.byref(bad), d, d, d, d, d, d, d, d, None) == 2
 
 
+def test_fused_tail_validates_on_the_host():
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    p = v3(Sq=1)
+    assert L.mla_combine_up_v(ctypes.byref(p), d, d, None, d, None, None) == 1
+    q = v3(Sq=1, d_c=256)
+    assert L.mla_combine_up_v(ctypes.byref(q), d, d, d, d, None, None) == 6
+    r = v3(Sq=1, latent_dtype=mla.F32)
+    assert L.mla_combine_up_v(ctypes.byref(r), d, d, d, d, None, None) == 6
+    assert L.mla_combine_up_v(ctypes.byref(v3(Sq=17)), d, d, d, d, None, None) == 2
+
+
 def test_status_strings():
     L = mla.lib()
     for code, name in mla.STATUS.items():
