@@ -302,10 +302,28 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
     }
-    for (int c0 = 0; c0 < S; c0 += 64)
+    // split lse values, 64 at a time (lane = split); the first 64 are kept for the
+    // second pass.  Loads use a clamped index and a select, so all rows' loads issue
+    // together.
+    auto lse_of = [&](int i, int c0) {
+        const float v = lse_part[row[i] * S + min(c0 + lane, S - 1)];
+        return ok[i] && c0 + lane < S ? v : -INFINITY;
+    };
+    // each row's partials as a raw buffer of S * d_c floats
+    __amdgpu_buffer_rsrc_t prow[kCuRowsPerWave];
 #pragma unroll
-        for (int i = 0; i < kCuRowsPerWave; ++i)
-            mx[i] = fmaxf(mx[i], ok[i] && c0 + lane < S ? lse_part[row[i] * S + c0 + lane] : -INFINITY);
+    for (int i = 0; i < kCuRowsPerWave; ++i)
+        prow[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o_part) + row[i] * S * kDc, 0,
+                                                    ok[i] ? S * kDc * 4 : 0, 0x20000);
+    float l0[kCuRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kCuRowsPerWave; ++i) {
+        l0[i] = lse_of(i, 0);
+        mx[i] = l0[i];
+    }
+    for (int c0 = 64; c0 < S; c0 += 64)
+#pragma unroll
+        for (int i = 0; i < kCuRowsPerWave; ++i) mx[i] = fmaxf(mx[i], lse_of(i, c0));
 #pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i) mx[i] = wave_max_f(mx[i]);
     for (int c0 = 0; c0 < S; c0 += 64) {
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         uint64_t live = 0;
 #pragma unroll
         for (int i = 0; i < kCuRowsPerWave; ++i) {
-            const float lc = ok[i] && c0 + lane < S ? lse_part[row[i] * S + c0 + lane] : -INFINITY;
+            const float lc = c0 == 0 ? l0[i] : lse_of(i, c0);
             wt[i] = (lc == -INFINITY || mx[i] == -INFINITY) ? 0.f : __expf(lc - mx[i]);
             sum[i] += wt[i];
             live |= __builtin_amdgcn_ballot_w64(wt[i] != 0.f);
@@ -321,20 +339,27 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         while (live) {
             const int k = __builtin_ctzll(live);
             live &= live - 1;
+            // the loads of all rows first (one round trip per split), then the sums; a
+            // row without weight on this split loads past its buffer's end, which
+            // returns zeros without a memory access
+            float wk[kCuRowsPerWave];
+            f32x4 v0[kCuRowsPerWave], v1[kCuRowsPerWave];
 #pragma unroll
             for (int i = 0; i < kCuRowsPerWave; ++i) {
-                const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), k));
-                if (wk != 0.f) {
-                    const f32x4 *src = reinterpret_cast<const f32x4 *>(
-                        o_part + (row[i] * S + c0 + k) * static_cast<int64_t>(kDc) + lane * 8);
-                    const f32x4 v0 = src[0], v1 = src[1];
+                wk[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), k));
+                const uint32_t off = wk[i] != 0.f ? ((c0 + k) * kDc + lane * 8) * 4u : 0x80000000u;
+                v0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off, 0, 0));
+                v1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off + 16u, 0, 0));
+            }
+#pragma unroll
+            for (int i = 0; i < kCuRowsPerWave; ++i)
+                if (wk[i] != 0.f) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[i][j] += wk * v0[j];
-                        acc[i][4 + j] += wk * v1[j];
+                        acc[i][j] += wk[i] * v0[i][j];
+                        acc[i][4 + j] += wk[i] * v1[i][j];
                     }
                 }
-            }
         }
     }
 #pragma unroll
