@@ -220,17 +220,22 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
 // 64 positions at a time are staged once per workgroup in LDS (two stages: the
 // next tile's global loads are in flight while the current one is used) and read
 // by all 8 waves.
-constexpr int kQWaves = 8;
-constexpr int kQPerWg = 32 * kQWaves;                // new tokens of one workgroup
+constexpr int kQPerWg = 256;                         // new tokens of one workgroup
 constexpr int kKvTile = 64;                          // positions of one stage
 constexpr int kKStride = 2 * (kDh + kDr) + 16;       // bytes per key row in LDS (padded: no bank conflicts)
 constexpr int kVStride = 2 * kKvTile + 16;           // bytes per value row in LDS (padded)
 constexpr int kKBytes = kKvTile * kKStride;
 constexpr int kStageBytes = kKBytes + kDh * kVStride;
 constexpr float kRescaleLog2 = 8.f;                  // running maximum moves when exceeded by more than this
+#ifndef MLA_PREFILL_QT
+#define MLA_PREFILL_QT 1
+#endif
+constexpr int kQT = MLA_PREFILL_QT;                  // 32-query tiles per wave
+constexpr int kAttWaves = kQPerWg / (32 * kQT);
+constexpr int kAttThreads = 64 * kAttWaves;
 
 template <bool kOutBf16>
-__global__ __launch_bounds__(512) void prefill_attention_kernel(
+__global__ __launch_bounds__(kAttThreads) void prefill_attention_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_nope, const uint16_t *__restrict__ q_rope,
     const uint16_t *__restrict__ k_nope, const uint16_t *__restrict__ v_t, const uint16_t *__restrict__ k_pe,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens, void *__restrict__ out) {
@@ -253,17 +258,52 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
     const int L = seq_lens[b];
     const int base = L - p.Sq;                           // position of new token 0
     const int q0 = qb * kQPerWg;
-    const int s0 = q0 + 32 * w;                          // this wave's first new token
-    const int s = s0 + t32;                              // this lane's query
-    const bool q_ok = s < p.Sq;
-    const int pos_q = base + s;                          // last position the query sees
-    const int pos_wave = base + min(s0 + 31, p.Sq - 1);  // last position any query of the wave sees
+    const int s0 = q0 + 32 * kQT * w;                    // this wave's first new token; tile qt: s0 + 32 qt
+    const int pos_wave = base + min(s0 + 32 * kQT - 1, p.Sq - 1);  // last position any query of the wave sees
     const int pos_wg = base + min(q0 + kQPerWg - 1, p.Sq - 1);
     const int n_tiles = pos_wg >= 0 ? pos_wg / kKvTile + 1 : 0;
+    int pos_q[kQT];                                      // last position this lane's query of tile qt sees
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) pos_q[qt] = base + s0 + 32 * qt + t32;
 
-    // Q^T (B operand): k-steps 0..7 the content dims, 8..11 the RoPE dims
-    bf16x8 qreg[12];
-    {
+    auto store_out = [&](int qt, const f32x16 *o, float inv) {
+        const int s = s0 + 32 * qt + t32;
+        if (s >= p.Sq) return;
+        // o[dt][j]: dim 32dt + 8(j/4) + 4g + j%4, query s
+        const int64_t orow = ((static_cast<int64_t>(b) * p.Sq + s) * p.H + h) * kDh;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = 32 * dt + 8 * q4 + 4 * g;
+                const f32x4 v = f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+                if constexpr (kOutBf16) {
+                    uint16_t *dst = static_cast<uint16_t *>(out) + orow + d0;
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + orow + d0) = v;
+                }
+            }
+    };
+    f32x16 o[kQT][4];                                    // O^T tiles: dims 32dt + .., query of tile qt
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[qt][dt][j] = 0.f;
+    if (n_tiles == 0) {                                  // no new token of the block sees any position
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) store_out(qt, o[qt], 0.f);
+        return;
+    }
+
+    // Q^T (B operand) of each tile: k-steps 0..7 the content dims, 8..11 the RoPE dims
+    bf16x8 qreg[kQT][12];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        const int s = s0 + 32 * qt + t32;
+        const bool q_ok = s < p.Sq;
         const int64_t qrow = (static_cast<int64_t>(b) * p.Sq + (q_ok ? s : 0)) * p.H + h;
 #pragma unroll
         for (int ks = 0; ks < 12; ++ks) {
@@ -272,30 +312,35 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
                 if (ks < 8) v = *reinterpret_cast<const u32x4 *>(q_nope + qrow * kDh + ks * 16 + g * 8);
                 else v = *reinterpret_cast<const u32x4 *>(q_rope + qrow * kDr + (ks - 8) * 16 + g * 8);
             }
-            qreg[ks] = as_bf16x8(v);
+            qreg[qt][ks] = as_bf16x8(v);
         }
     }
 
-    // Staging: thread tid moves five 16-byte chunks per tile: key content rows
-    // tid/16 and 32 + tid/16 (part tid%16), the RoPE key of row tid/8 (part tid%8),
-    // and value rows tid/8 and 64 + tid/8 (positions 8 (tid%8) ..).  Every row of a
-    // tile lies inside lmax; rows past seq_len are masked in the scores (keys) or
-    // zeroed when staged (values), and a tile is one page, so its RoPE rows are
-    // rows of that page.
+    // Staging: a tile is 64 key rows of 16 content chunks and 8 RoPE chunks, and 128
+    // value rows of 8 chunks (16 bytes each); thread tid moves content chunk tid%16
+    // of rows tid/16 + (T/16)i, RoPE chunk tid%8 of rows tid/8 + (T/8)i and value
+    // chunk tid%8 of rows tid/8 + (T/8)i (T threads).  Every row of a tile lies
+    // inside lmax; rows past seq_len are masked in the scores (keys) or zeroed when
+    // staged (values), and a tile is one page, so its RoPE rows are rows of that page.
+    constexpr int kNK = 1024 / kAttThreads, kNR = 512 / kAttThreads, kNV = 1024 / kAttThreads;
     const int32_t *bt = block_table + static_cast<int64_t>(b) * p.max_pages;
     const int kr = tid >> 4, kc = tid & 15, rr = tid >> 3, rc = tid & 7;
     const int64_t kstride = static_cast<int64_t>(p.H) * kDh;      // elements per key position
     const uint16_t *kptr = k_nope + (static_cast<int64_t>(b) * lmax * p.H + h) * kDh + kr * kstride + kc * 8;
     const uint16_t *vptr = v_t + ((static_cast<int64_t>(b) * p.H + h) * kDh + rr) * lmax + rc * 8;
     const uint16_t *rptr = k_pe + rr * kDr + rc * 8;
-    u32x4 stg[5];
+    u32x4 stg_k[kNK], stg_r[kNR], stg_v[kNV];
     auto load_tile = [&](int k0, int page) {
         const uint16_t *kp = kptr + k0 * kstride;
-        stg[0] = *reinterpret_cast<const u32x4 *>(kp);
-        stg[1] = *reinterpret_cast<const u32x4 *>(kp + 32 * kstride);
-        stg[2] = *reinterpret_cast<const u32x4 *>(rptr + static_cast<int64_t>(page) * 64 * kDr);
-        stg[3] = *reinterpret_cast<const u32x4 *>(vptr + k0);
-        stg[4] = *reinterpret_cast<const u32x4 *>(vptr + 64 * lmax + k0);
+#pragma unroll
+        for (int i = 0; i < kNK; ++i)
+            stg_k[i] = *reinterpret_cast<const u32x4 *>(kp + (kAttThreads / 16) * i * kstride);
+#pragma unroll
+        for (int i = 0; i < kNR; ++i)
+            stg_r[i] = *reinterpret_cast<const u32x4 *>(rptr + (static_cast<int64_t>(page) * 64 + (kAttThreads / 8) * i) * kDr);
+#pragma unroll
+        for (int i = 0; i < kNV; ++i)
+            stg_v[i] = *reinterpret_cast<const u32x4 *>(vptr + (kAttThreads / 8) * i * lmax + k0);
     };
     const uint32_t lds0 = lds_addr(lds);
     auto store_tile = [&](int k0, int stage) {
@@ -304,44 +349,32 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 const uint32_t keep = (pv + 2 * e2 < L ? 0x0000ffffu : 0u) | (pv + 2 * e2 + 1 < L ? 0xffff0000u : 0u);
-                stg[3][e2] &= keep;
-                stg[4][e2] &= keep;
+#pragma unroll
+                for (int i = 0; i < kNV; ++i) stg_v[i][e2] &= keep;
             }
         }
         const uint32_t st = lds0 + stage * kStageBytes;
-        lds_store<u32x4>(st + kr * kKStride + kc * 16, stg[0]);
-        lds_store<u32x4>(st + (32 + kr) * kKStride + kc * 16, stg[1]);
-        lds_store<u32x4>(st + rr * kKStride + 2 * kDh + rc * 16, stg[2]);
-        lds_store<u32x4>(st + kKBytes + rr * kVStride + rc * 16, stg[3]);
-        lds_store<u32x4>(st + kKBytes + (64 + rr) * kVStride + rc * 16, stg[4]);
+#pragma unroll
+        for (int i = 0; i < kNK; ++i) lds_store<u32x4>(st + (kr + (kAttThreads / 16) * i) * kKStride + kc * 16, stg_k[i]);
+#pragma unroll
+        for (int i = 0; i < kNR; ++i)
+            lds_store<u32x4>(st + (rr + (kAttThreads / 8) * i) * kKStride + 2 * kDh + rc * 16, stg_r[i]);
+#pragma unroll
+        for (int i = 0; i < kNV; ++i)
+            lds_store<u32x4>(st + kKBytes + (rr + (kAttThreads / 8) * i) * kVStride + rc * 16, stg_v[i]);
     };
 
     const float zscale = p.scale * kLog2e;
-    float m_run = -INFINITY;                             // running maximum (log2 domain), same in the lane pair
-    float l_run = 0.f;                                   // this lane's share of the sum of bf16-rounded weights
-    f32x16 o[4];                                         // O^T tiles: dims 32dt + .., query t32
+    float m_run[kQT], l_run[kQT];                        // running maximum (log2 domain) and weight sum
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
+    for (int qt = 0; qt < kQT; ++qt) {
+        m_run[qt] = -INFINITY;
+        l_run[qt] = 0.f;
+    }
     // key operand rows of this lane: tile rows swap23(t32) and 32 + swap23(t32)
     const uint32_t k_off = swap23(t32) * kKStride + g * 16;
     const uint32_t v_off = kKBytes + t32 * kVStride + g * 16;
 
-    if (n_tiles == 0) {                                  // no new token of the block sees any position
-        if (q_ok) {
-            const int64_t orow = ((static_cast<int64_t>(b) * p.Sq + s) * p.H + h) * kDh;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d0 = 32 * dt + 8 * q4 + 4 * g;
-                    if constexpr (kOutBf16) *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(out) + orow + d0) = u32x2{0u, 0u};
-                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + orow + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-        }
-        return;
-    }
     load_tile(0, bt[0]);
     int page_next = n_tiles > 1 ? bt[1] : 0;             // page of the next tile, read one tile ahead
     store_tile(0, 0);
@@ -352,78 +385,86 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
         if (more) load_tile(k0 + kKvTile, page_next);
         if (s0 < p.Sq && k0 <= pos_wave) {
             const uint32_t st = lds0 + (kt & 1) * kStageBytes;
-            // S^T[t, q] for positions k0 + 32ps + swap23(row)
-            f32x16 sacc[2];
+            // the tile in two halves of 32 positions: scores, softmax, value product
 #pragma unroll
-            for (int ps = 0; ps < 2; ++ps)
+            for (int ps = 0; ps < 2; ++ps) {
+                const int kh = k0 + 32 * ps;                 // first position of the half
+                // S^T[t, q] for positions kh + swap23(row); each key operand serves
+                // every query tile of the wave
+                f32x16 sacc[kQT];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) sacc[ps][j] = 0.f;
+                for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
-            for (int ks = 0; ks < 12; ++ks)
+                    for (int j = 0; j < 16; ++j) sacc[qt][j] = 0.f;
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps) {
+                for (int ks = 0; ks < 12; ++ks) {
                     const u32x4 a = lds_load<u32x4>(st + k_off + ps * 32 * kKStride + ks * 32);
-                    sacc[ps] = mfma32(as_bf16x8(a), qreg[ks], sacc[ps]);
+#pragma unroll
+                    for (int qt = 0; qt < kQT; ++qt) sacc[qt] = mfma32(as_bf16x8(a), qreg[qt][ks], sacc[qt]);
                 }
-            // sacc[ps][j]: position k0 + 32ps + 16(j/8) + 8g + (j%8), query s; the
-            // maximum is taken on the raw scores (the scale is positive)
-            float mt = -INFINITY;
-            if (k0 + kKvTile - 1 > base + s0 || k0 + kKvTile > L) {
-                // the tile reaches past the first query's position or the sequence end
-                const int lim = min(pos_q, L - 1) - (k0 + 8 * g);
+                uint32_t pk[kQT][2][4];
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps)
+                for (int qt = 0; qt < kQT; ++qt) {
+                    // sacc[qt][j]: position kh + 16(j/8) + 8g + (j%8); the maximum is
+                    // taken on the raw scores (the scale is positive)
+                    float mt = -INFINITY;
+                    if (kh + 31 > base + s0 + 32 * qt || kh + 32 > L) {
+                        // the half reaches past the tile's first query position or the sequence end
+                        const int lim = min(pos_q[qt], L - 1) - (kh + 8 * g);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int rel = 32 * ps + 16 * (j >> 3) + (j & 7);
-                        sacc[ps][j] = rel <= lim ? sacc[ps][j] : -INFINITY;
-                        mt = fmaxf(mt, sacc[ps][j]);
+                        for (int j = 0; j < 16; ++j) {
+                            const int rel = 16 * (j >> 3) + (j & 7);
+                            sacc[qt][j] = rel <= lim ? sacc[qt][j] : -INFINITY;
+                            mt = fmaxf(mt, sacc[qt][j]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[qt][j]);
                     }
-            } else {
+                    mt = pair_max(mt) * zscale;          // log2 domain
+                    // the running maximum moves only when this half's exceeds it by more
+                    // than kRescaleLog2, so the weights stay below 2^kRescaleLog2 and the
+                    // rescale of the accumulators is skipped on most halves
+                    const bool grow = mt > m_run[qt] + kRescaleLog2;
+                    if (__builtin_amdgcn_ballot_w64(grow)) {
+                        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qt] - mt) : 1.f;   // 0 the first time
+                        m_run[qt] = grow ? mt : m_run[qt];
+                        l_run[qt] *= alpha;
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps)
+                        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[ps][j]);
-            }
-            mt = pair_max(mt) * zscale;                  // log2 domain
-            // the running maximum moves only when this tile's exceeds it by more than
-            // kRescaleLog2, so the weights stay below 2^kRescaleLog2 and the rescale of
-            // the accumulators is skipped on most tiles
-            const bool grow = mt > m_run + kRescaleLog2;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;   // 0 the first time
-                m_run = grow ? mt : m_run;
-                l_run *= alpha;
+                            for (int j = 0; j < 16; ++j) o[qt][dt][j] *= alpha;
+                    }
+                    const float m_neg = m_run[qt] == -INFINITY ? 0.f : -m_run[qt];   // nothing visible yet: weights 0
+                    // weights exp2(scale * z - m), rounded to bf16; k-step kk of the value
+                    // product takes positions kh + 16kk + 8g + e, which are sacc[qt][8kk + e]
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
+                    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-            }
-            const float m_neg = m_run == -INFINITY ? 0.f : -m_run;   // nothing visible yet: weights 0
-            // weights exp2(scale * z - m), rounded to bf16; k-step kk of the value
-            // product takes positions 16kk + 8g + e, which are sacc[kk/2][8(kk%2) + e]
-            uint32_t pk[4][4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int j = 8 * (kk & 1) + 2 * e2;
-                    const uint32_t pr =
-                        cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kk >> 1][j], zscale, m_neg)),
-                                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kk >> 1][j + 1], zscale, m_neg)));
-                    pk[kk][e2] = pr;
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
-                                                            bf16x2{(__bf16)1.f, (__bf16)1.f}, l_run, false);
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            const int j = 8 * kk + 2 * e2;
+                            const uint32_t pr =
+                                cvt_pk_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qt][j], zscale, m_neg)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qt][j + 1], zscale, m_neg)));
+                            pk[qt][kk][e2] = pr;
+                            l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr),
+                                                                        bf16x2{(__bf16)1.f, (__bf16)1.f}, l_run[qt],
+                                                                        false);
+                        }
                 }
-            // O^T[d, q] += V^T[d, t] . P^T[t, q]
+                // O^T[d, q] += V^T[d, t] . P^T[t, q]; each value operand serves every query tile
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 pb = as_bf16x8(u32x4{pk[kk][0], pk[kk][1], pk[kk][2], pk[kk][3]});
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const u32x4 a = lds_load<u32x4>(st + v_off + dt * 32 * kVStride + kk * 32);
-                    o[dt] = mfma32(as_bf16x8(a), pb, o[dt]);
-                }
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const u32x4 a = lds_load<u32x4>(st + v_off + dt * 32 * kVStride + (2 * ps + kk) * 32);
+#pragma unroll
+                        for (int qt = 0; qt < kQT; ++qt)
+                            o[qt][dt] = mfma32(
+                                as_bf16x8(a),
+                                as_bf16x8(u32x4{pk[qt][kk][0], pk[qt][kk][1], pk[qt][kk][2], pk[qt][kk][3]}),
+                                o[qt][dt]);
+                    }
             }
         }
         if (more) {
@@ -432,24 +473,11 @@ __global__ __launch_bounds__(512) void prefill_attention_kernel(
         }
         __syncthreads();
     }
-    if (!q_ok) return;
-    const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    // o[dt][j]: dim 32dt + 8(j/4) + 4g + j%4, query s
-    const int64_t orow = ((static_cast<int64_t>(b) * p.Sq + s) * p.H + h) * kDh;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = 32 * dt + 8 * q4 + 4 * g;
-            const f32x4 v = f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
-            if constexpr (kOutBf16) {
-                uint16_t *dst = static_cast<uint16_t *>(out) + orow + d0;
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
-            } else {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + orow + d0) = v;
-            }
-        }
+    for (int qt = 0; qt < kQT; ++qt) {
+        const float l_tot = pair_sum(l_run[qt]);
+        store_out(qt, o[qt], l_tot > 0.f ? 1.f / l_tot : 0.f);
+    }
 }
 
 }  // namespace
@@ -477,16 +505,17 @@ hipError_t launch_prefill_attention(const mla_params_t &p, const void *q_nope, c
                                     const int32_t *block_table, const int32_t *seq_lens, void *out,
                                     hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H * ((p.Sq + kQPerWg - 1) / kQPerWg);
+    static_assert(kQPerWg == 256, "the host's grid check assumes 256 new tokens per workgroup");
     const auto qn = static_cast<const uint16_t *>(q_nope);
     const auto qr = static_cast<const uint16_t *>(q_rope);
     const auto kn = static_cast<const uint16_t *>(k_nope);
     const auto vt = static_cast<const uint16_t *>(v_t);
     const auto kp = static_cast<const uint16_t *>(k_pe);
     if (p.out_dtype == MLA_BF16)
-        hipLaunchKernelGGL(prefill_attention_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+        hipLaunchKernelGGL(prefill_attention_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kAttThreads), 0, stream,
                            p, qn, qr, kn, vt, kp, block_table, seq_lens, out);
     else
-        hipLaunchKernelGGL(prefill_attention_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream,
+        hipLaunchKernelGGL(prefill_attention_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kAttThreads), 0, stream,
                            p, qn, qr, kn, vt, kp, block_table, seq_lens, out);
     return hipGetLastError();
 }

@@ -122,9 +122,9 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
     int64_t P = std::max<int64_t>(1, num_cus / wg_per_part);
     if (!mfma) P = std::max<int64_t>(1, 2ll * num_cus / wg_per_part);
-    // parts of at least 8 pages keep the fp32 partials (d_c*4 bytes per row) small next
-    // to the cache they summarise
-    P = std::min(P, std::max<int64_t>(1, pages_lo / 8));
+    // parts of at least 4 pages keep the fp32 partials (d_c*4 bytes per row) small next
+    // to the cache they summarise (measured at B = 1: 4 pages per part beat 8, 2 and 1)
+    P = std::min(P, std::max<int64_t>(1, pages_lo / 4));
     P = std::max(P, std::min<int64_t>(min_splits, std::max<int64_t>(1, pages_lo)));
     P = std::min<int64_t>(P, kMaxParts);
     // a sequence of n pages touches at most ceil(n / q) + 1 parts of >= q pages, and
