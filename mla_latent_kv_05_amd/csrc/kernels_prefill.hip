@@ -9,11 +9,12 @@
 // of head h at position t is [W_UK[h] c_t ; k_pe_t], its value W_UV[h] c_t, the
 // score scale 1/sqrt(d_h + d_r), and row s attends to positions t <= its own.
 //
-// Decompress: one workgroup (4 waves) per (group of 16 heads, sequence, 128
+// Decompress: one workgroup (8 waves) per (group of 16 heads, sequence, 256
 // positions); wave w holds the latent rows of 32 of the positions as MFMA operands
-// (128 VGPRs) for the whole workgroup.  The weights of each head stream through
-// LDS in chunks of 64 latent dims (double-buffered, shared by the 4 waves), first
-// W_UK[h] then W_UV[h]:
+// (128 VGPRs) for the whole workgroup.  The weights stream through LDS in passes
+// of 64 rows (output dims) of one head, W_UK[h] then W_UV[h], each pass in chunks
+// of 256 latent dims (double-buffered, two chunks ahead in registers, shared by
+// the 8 waves):
 //   keys:   D[d, t] = W_UK[h] . c^T (weight rows as the A operand, latent rows as B),
 //   values: D[t, d] = c . W_UV[h]^T (latent rows as A, weight rows as B),
 // the latent registers serving both roles unchanged (both operands take 8
@@ -26,17 +27,17 @@
 // Attention: one workgroup (8 waves) per (sequence, head, 256 new tokens); wave w
 // takes 32 of them.  Keys and transposed values of 64 positions (one page) at a
 // time are staged in LDS once per workgroup, double-buffered, and read by every
-// wave.  Per staged tile and wave:
-//   S^T[t, q] = K_tile . Q^T over the 192 dims (2 x 12 MFMAs; Q^T in registers).
-//   Tile row r of each 32-row half holds position swap23(r) (bits 2 and 3 of r
-//   exchanged), so that the 16 weights a lane holds for query q are, as the B
-//   operand of the value product, positions 16ks + 8g + e in order;
-//   online softmax per query in the exp2 domain (a lane pair per query); the
+// wave.  Per staged tile, in two halves of 32 positions, each wave forms
+//   S^T[t, q] = K_half . Q^T over the 192 dims (12 MFMAs; Q^T in registers).
+//   Row r of the half holds position swap23(r) (bits 2 and 3 of r exchanged), so
+//   that the 16 weights a lane holds for query q are, as the B operand of the
+//   value product, positions 16k + 8g + e in order;
+//   the online softmax per query in the exp2 domain (a lane pair per query); the
 //   running maximum only moves when exceeded by more than 2^8, so the rescale of
-//   the accumulators is skipped on most tiles;
-//   O^T[d, q] += V^T[d, t] . P^T[t, q] (16 MFMAs).
+//   the accumulators is skipped on most halves;
+//   O^T[d, q] += V^T[d, t] . P^T[t, q] (8 MFMAs).
 // Positions past a query's own or past seq_len are masked in the scores; values
-// past seq_len (never written) are zeroed when staged.
+// past seq_len are zeroed when staged.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -56,7 +57,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecPos = 32 * kDecWaves;        // positions of one decompress workgroup (32 per wave)
 constexpr int kDecRows = 64;                   // weight rows (output dims) of one pass
-constexpr int kWChunk = 128;                   // latent dims of one staged weight chunk
+constexpr int kWChunk = 256;                   // latent dims of one staged weight chunk
 constexpr int kWStride = 2 * kWChunk + 16;     // bytes per staged weight row (padded: no bank conflicts)
 constexpr int kWStage = kDecRows * kWStride;
 static_assert(kDecPos == 256, "prefill_lmax rounds the row stride to whole decompression tiles");
