@@ -336,30 +336,46 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
             sum[i] += wt[i];
             live |= __builtin_amdgcn_ballot_w64(wt[i] != 0.f);
         }
+        // two live splits per round: the loads of all rows and both splits first,
+        // then the sums in split order; a row without weight on a split (or a
+        // missing second split) loads past its buffer's end, which returns zeros
+        // without a memory access
         while (live) {
-            const int k = __builtin_ctzll(live);
+            const int ka = __builtin_ctzll(live);
             live &= live - 1;
-            // the loads of all rows first (one round trip per split), then the sums; a
-            // row without weight on this split loads past its buffer's end, which
-            // returns zeros without a memory access
-            float wk[kCuRowsPerWave];
-            f32x4 v0[kCuRowsPerWave], v1[kCuRowsPerWave];
+            const bool has_b = live != 0;
+            const int kb = has_b ? __builtin_ctzll(live) : ka;
+            if (has_b) live &= live - 1;
+            float wa_[kCuRowsPerWave], wb_[kCuRowsPerWave];
+            f32x4 a0[kCuRowsPerWave], a1[kCuRowsPerWave], b0[kCuRowsPerWave], b1[kCuRowsPerWave];
 #pragma unroll
             for (int i = 0; i < kCuRowsPerWave; ++i) {
-                wk[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), k));
-                const uint32_t off = wk[i] != 0.f ? ((c0 + k) * kDc + lane * 8) * 4u : 0x80000000u;
-                v0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off, 0, 0));
-                v1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off + 16u, 0, 0));
+                wa_[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), ka));
+                wb_[i] = has_b ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), kb)) : 0.f;
+                const uint32_t oa = wa_[i] != 0.f ? ((c0 + ka) * kDc + lane * 8) * 4u : 0x80000000u;
+                const uint32_t ob = wb_[i] != 0.f ? ((c0 + kb) * kDc + lane * 8) * 4u : 0x80000000u;
+                a0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0));
+                a1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa + 16u, 0, 0));
+                b0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0));
+                b1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob + 16u, 0, 0));
             }
 #pragma unroll
-            for (int i = 0; i < kCuRowsPerWave; ++i)
-                if (wk[i] != 0.f) {
+            for (int i = 0; i < kCuRowsPerWave; ++i) {
+                if (wa_[i] != 0.f) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[i][j] += wk[i] * v0[i][j];
-                        acc[i][4 + j] += wk[i] * v1[i][j];
+                        acc[i][j] += wa_[i] * a0[i][j];
+                        acc[i][4 + j] += wa_[i] * a1[i][j];
                     }
                 }
+                if (wb_[i] != 0.f) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] += wb_[i] * b0[i][j];
+                        acc[i][4 + j] += wb_[i] * b1[i][j];
+                    }
+                }
+            }
         }
     }
 #pragma unroll
