@@ -280,13 +280,6 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     const int r0 = rc * kUpRows;
     const int d0 = w * 16;
     const uint32_t sm = lds_addr(smem);
-    // this wave's weights (16 rows d0 ..), in flight during the merge
-    const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
-    bf16x8 wa[kDc / 32];
-#pragma unroll
-    for (int ks = 0; ks < kDc / 32; ++ks)
-        wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
-
     // merge rows rr = 4w + i: lane owns latent columns 8 lane .. 8 lane + 7
     const int S = p.num_splits;
     int64_t row[kCuRowsPerWave];
@@ -317,10 +310,20 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
                                                     ok[i] ? S * kDc * 4 : 0, 0x20000);
     float l0[kCuRowsPerWave];
 #pragma unroll
+    for (int i = 0; i < kCuRowsPerWave; ++i) l0[i] = lse_part[row[i] * S + min(lane, S - 1)];
+#pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i) {
-        l0[i] = lse_of(i, 0);
+        l0[i] = ok[i] && lane < S ? l0[i] : -INFINITY;
         mx[i] = l0[i];
     }
+    // this wave's weights (16 rows d0 ..), issued after the split lse values (loads
+    // complete in order: waiting for the lse values does not wait for the weights),
+    // in flight during the merge
+    const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
+    bf16x8 wa[kDc / 32];
+#pragma unroll
+    for (int ks = 0; ks < kDc / 32; ++ks)
+        wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
     for (int c0 = 64; c0 < S; c0 += 64)
 #pragma unroll
         for (int i = 0; i < kCuRowsPerWave; ++i) mx[i] = fmaxf(mx[i], lse_of(i, c0));
