@@ -77,3 +77,19 @@ def test_fused_step_equals_four_call_step():
     assert torch.equal(f.out, ref_out)
     ref = O.decode(case)[0]
     assert err_rms(f.out.cpu().numpy(), ref) <= TOL["bf16"]
+
+
+def test_fused_step_full_size_bitwise():
+    """At the bench's decode workload (B=64, lengths U[1024, 8192], balanced splits)
+    the fused step reproduces the four-call step bit for bit."""
+    wl = I.workload("v3_b64")
+    case = I.make_case(wl)
+    p = params_for(case, plan=True)
+    dc = DeviceCase(case)
+    note(f"fused vs four-call at full size: S={p.num_splits} parts={p.num_parts}")
+    a = mla.DecodeStep(p)
+    f = mla.DecodeStep(p, fused=True)
+    for st in (a, f):
+        st(dc.q_nope, dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table, dc.seq_lens, dc.W_UK, dc.W_UV)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, f.out) and torch.equal(a.lse, f.lse)

@@ -57,7 +57,8 @@ def run_path(case, p):
     L = mla.lmax(p)
     kn = torch.full((wl.B, L, wl.H, wl.d_h), SENT, dtype=torch.bfloat16, device="cuda")
     vt = torch.full((wl.B, wl.H, wl.d_h, L), SENT, dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((wl.B, wl.Sq, wl.H, wl.d_h), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.B, wl.Sq, wl.H, wl.d_h), dtype=torch.float32 if p.out_dtype == mla.F32 else torch.bfloat16,
+                      device="cuda")
     d = {k: getattr(case, k).cuda() for k in ("c_kv", "k_pe", "block_table", "seq_lens", "W_UK", "W_UV",
                                               "q_nope", "q_rope")}
     mla.decompress_kv(p, d["c_kv"], d["block_table"], d["seq_lens"], d["W_UK"], d["W_UV"], kn, vt)
@@ -66,15 +67,20 @@ def run_path(case, p):
     return kn.cpu(), vt.cpu(), out.cpu()
 
 
-def err_rows(got, ref) -> float:
+def err_rows(got, ref, out_bf16=False) -> float:
     """max over rows (last axis = d_h) of max|got - ref| / RMS(ref row); rows whose
-    reference is 0 (nothing visible) must be 0 exactly."""
+    reference is 0 (nothing visible) must be 0 exactly.  With a bf16 output, each
+    element's own rounding (at most 2^-9 of its value; 2^-8 allowed) is taken off
+    first, so the bound stays that of the computation."""
     got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
     ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
     rms = np.sqrt(np.mean(ref ** 2, axis=1))
     empty = rms == 0
     assert (got[empty] == 0).all()
-    return float((np.abs(got - ref).max(axis=1)[~empty] / rms[~empty]).max())
+    d = np.abs(got - ref)
+    if out_bf16:
+        d = np.maximum(d - 2.0 ** -8 * np.abs(ref), 0.0)
+    return float((d.max(axis=1)[~empty] / rms[~empty]).max())
 
 
 def check_decompressed(case, kn, vt):
@@ -144,3 +150,60 @@ def test_both_paths_agree_where_both_apply():
     assert e_na <= 2e-2 and e_ab <= 2e-2
     # each within 2e-2 of the oracle per row, hence within 4e-2 of each other
     assert err_rows(out_na.double().numpy(), st.out.cpu().double().numpy()) <= 4e-2
+
+
+def test_empty_sequence_and_prefix_only_rows():
+    """A sequence of length 0 next to normal ones: nothing of it is written and all
+    its rows are 0; the others are unaffected."""
+    wl = I.workload("v3_b64", B=3, Sq=40)
+    case = I.make_case(wl, seq_lens=[0, 40, 300])
+    p = params(case)
+    note("prefill with an empty sequence")
+    kn, vt, out = run_path(case, p)
+    check_decompressed(case, kn, vt)
+    assert (out[0] == 0).all()
+    ref = O.decode(case)[0]
+    assert err_rows(out[1:].double().numpy(), ref[1:]) <= 2e-2
+
+
+def test_full_size_sampled():
+    """The bench's workload (4 sequences x 4,096 new tokens, whole-prompt prefill) in
+    its launch configuration, bf16 output; decompressed rows and outputs checked on
+    sampled positions and rows that the oracle computes one by one."""
+    B, x = 4, 4096
+    wl = I.workload("v3_b64", B=B, Sq=x)
+    note("prefill full size: generating")
+    case = I.make_case(wl, seq_lens=[x] * B)
+    p = params(case, out_dtype=mla.BF16)
+    validate(case)
+    L = mla.lmax(p)
+    d = {k: getattr(case, k).cuda() for k in ("c_kv", "k_pe", "block_table", "seq_lens", "W_UK", "W_UV",
+                                              "q_nope", "q_rope")}
+    kn = torch.empty((B, L, wl.H, wl.d_h), dtype=torch.bfloat16, device="cuda")
+    vt = torch.empty((B, wl.H, wl.d_h, L), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, x, wl.H, wl.d_h), dtype=torch.bfloat16, device="cuda")
+    note("prefill full size: running")
+    mla.decompress_kv(p, d["c_kv"], d["block_table"], d["seq_lens"], d["W_UK"], d["W_UV"], kn, vt)
+    mla.prefill_attention(p, d["q_nope"], d["q_rope"], kn, vt, d["k_pe"], d["block_table"], d["seq_lens"], out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    # decompressed rows: first, last and random positions of every sequence
+    c = O.cache_values(case)
+    wuk, wuv = O.decode_values(case.W_UK), O.decode_values(case.W_UV)
+    bt = case.block_table.numpy()
+    for b in range(B):
+        pos = np.unique(np.concatenate([[0, x - 1], rng.integers(0, x, 6)]))
+        lat = c[bt[b, pos // 64], pos % 64]
+        K, V = PF.decompress_kv(lat, wuk, wuv)
+        assert_bf16_rounding(kn[b, pos].double().cpu().numpy(), K, acc_rel=1e-4)
+        assert_bf16_rounding(vt[b][:, :, pos].double().cpu().numpy(), V.transpose(1, 2, 0), acc_rel=1e-4)
+    # outputs: the first and last new tokens and random ones, first/last/random heads
+    toks = np.unique(np.concatenate([[0, 1, x - 1], rng.integers(0, x, 5)]))
+    heads = np.unique(np.concatenate([[0, wl.H - 1], rng.integers(0, wl.H, 2)]))
+    rows = np.array([(b * x + s) * wl.H + h for b in range(B) for s in toks for h in heads], dtype=np.int64)
+    note(f"prefill full size: oracle on {len(rows)} rows")
+    ref = O.decode(case, rows=rows)[0]
+    got = out.float().cpu().numpy().reshape(-1, wl.d_h)[rows]
+    e = err_rows(got, ref, out_bf16=True)
+    note(f"prefill full size err {e:.3e}")
+    assert e <= 2e-2
