@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
 // ---------------------------------------------------------------------------
 // mla_combine_up_v: the split merge and the up-projection in one launch, without
 // the merged latent rows leaving the chip.  One workgroup of 8 waves per (head,
-// 32-row chunk), as for up_v: wave w first merges rows 4w .. 4w+3 of the chunk
+// 32-row chunk), as for up_v: wave w first merges rows w, w+8, w+16, w+24 of the chunk
 // from their split partials (the arithmetic and order of combine_kernel_512, four
 // rows at a time so that their loads overlap), rounds them to bf16 into the
 // swizzled LDS layout of up_v, and then forms output dims 16w .. 16w+15 from its
@@ -280,14 +280,14 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     const int r0 = rc * kUpRows;
     const int d0 = w * 16;
     const uint32_t sm = lds_addr(smem);
-    // merge rows rr = 4w + i: lane owns latent columns 8 lane .. 8 lane + 7
+    // merge rows rr = w + 8i: lane owns latent columns 8 lane .. 8 lane + 7
     const int S = p.num_splits;
     int64_t row[kCuRowsPerWave];
     bool ok[kCuRowsPerWave];
     float mx[kCuRowsPerWave], sum[kCuRowsPerWave], acc[kCuRowsPerWave][8];
 #pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i) {
-        const int r = r0 + kCuRowsPerWave * w + i;
+        const int r = r0 + w + 8 * i;             // strided: few rows still spread over the waves
         ok[i] = r < R;
         row[i] = static_cast<int64_t>(ok[i] ? r : 0) * p.H + h;
         mx[i] = -INFINITY;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     for (int i = 0; i < kCuRowsPerWave; ++i) {
         const float tot = wave_sum_f(sum[i]);
         const float inv = tot > 0.f ? 1.f / tot : 0.f;
-        const int rr = kCuRowsPerWave * w + i;
+        const int rr = w + 8 * i;
         u32x4 o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(acc[i][2 * k] * inv, acc[i][2 * k + 1] * inv);
