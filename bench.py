@@ -170,8 +170,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    peaks = measured_peaks(dev, stream)
     append = append_bench(mla, A, wl, p, reps[0], dev, stream, args)
     prefill = None if args.no_prefill else prefill_bench(mla, A, dev, stream, args)
+    if prefill is not None:
+        for k in ("decompress", "attention", "path"):
+            prefill[k]["frac_of_measured_gemm"] = round(prefill[k]["achieved"] / peaks["bf16_gemm_tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -210,7 +214,9 @@ def main():
             "launch_us": round(dec_avg_ms * 1e3, 2),
             "bytes_per_launch": cost.decode_bytes,
             "mfma_tflops": round(cost.decode_flops / (dec_avg_ms * 1e-3) / 1e12, 1),
+            "frac_of_measured_copy": round(achieved_gbs / peaks["hbm_copy_gbs"], 4),
         },
+        "measured_peaks": peaks,
         "step_roofline": {"bytes": cost.total_bytes, "flops": cost.flops, "t_roof_us": round(roofline_us, 2),
                           "frac": round(roofline_us / (ms_step * 1e3), 4)},
         "steps_timed": {
@@ -227,6 +233,39 @@ def main():
         "wall_s": round(wall, 3),
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_peaks(dev, stream):
+    """Practical peaks on this GPU, as context for the spec peaks: a 1 GiB device copy
+    (bytes read + written per second) and a large bf16 matrix product (torch's
+    library GEMM, contiguous operands)."""
+    import numpy as np
+    import torch
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    src = torch.ones(1 << 28, device=dev)             # 1 GiB of fp32
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device=dev).bfloat16()
+    b = torch.randn((n, n), device=dev).bfloat16()
+    t_mm = timed(lambda: torch.mm(a, b), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "bf16_gemm_tflops": round(2 * n ** 3 / t_mm / 1e12, 1),
+            "how": "1 GiB device copy (read + write); 8192^3 bf16 torch.mm"}
 
 
 def append_bench(mla, A, wl, p, t, dev, stream, args):
