@@ -249,6 +249,25 @@ mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void 
                            void *stream);
 
 /*
+ * mla_expand_kv -- a bf16 copy of an e4m3 latent cache with each token's scale
+ * applied (the cache's value semantics: c = code * kv_scale, "DeepSeek-MLA-
+ * Principle" sec. 3 on the cache footprint; the per-token quantisation is that of
+ * mla_append_kv):
+ *   c_out[page, slot, m] = bf16_rne(float(e4m3(c_kv[page, slot, m])) * kv_scale[page, slot])
+ * (one fp32 product, then rounding to nearest even).  Every page is expanded.  A
+ * decode step bound by the matrix cores (many query rows per cached token) runs
+ * faster as mla_expand_kv followed by mla_decode_splitkv on the bf16 copy
+ * (kv_dtype = bf16) than on the e4m3 cache directly, at the cost of the bf16
+ * workspace, which the caller owns.
+ *
+ *   c_kv     [num_pages,64,d_c]  e4m3 codes  (in; kv_dtype must be MLA_FP8_E4M3)
+ *   kv_scale [num_pages,64]      fp32        (in)
+ *   c_out    [num_pages,64,d_c]  bf16        (out)
+ */
+mla_status_t mla_expand_kv(const mla_params_t *p, const void *c_kv, const float *kv_scale, void *c_out,
+                           void *stream);
+
+/*
  * The non-absorbed path, for many new tokens per sequence (prefill, chunked
  * prefill).  "MLA Matrix Absorption" sec. 6 describes the switch: with x new tokens
  * per sequence at or above a threshold (about 64) the per-head keys and values are

@@ -217,6 +217,19 @@ mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const 
     return hip_status(mla::launch_combine_up_v(*p, o_part, lse_part, W_UV, out, lse_out, st), "mla_combine_up_v launch");
 }
 
+mla_status_t mla_expand_kv(const mla_params_t *p, const void *c_kv, const float *kv_scale, void *c_out,
+                           void *stream) {
+    mla_status_t s = check(p, kMaxPrefill);
+    if (s != MLA_OK) return s;
+    if (!c_kv || !kv_scale || !c_out) return fail(MLA_ERR_NULL, "mla_expand_kv: NULL tensor pointer");
+    if (p->kv_dtype != MLA_FP8_E4M3) return fail(MLA_ERR_DTYPE, "mla_expand_kv: kv_dtype must be e4m3");
+    if (p->d_c % 8 != 0) return fail(MLA_ERR_SHAPE, "mla_expand_kv: d_c must be a multiple of 8 (got %d)", p->d_c);
+    if ((int64_t)p->num_pages * p->page_size * (p->d_c / 8) / 256 > 0x7fffffffll)
+        return fail(MLA_ERR_SHAPE, "mla_expand_kv: cache too large for one launch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_expand(*p, c_kv, kv_scale, c_out, st), "mla_expand_kv launch");
+}
+
 mla_status_t mla_append_kv(const mla_params_t *p, const void *c_new, const void *kpe_new, const void *q_rope_in,
                            void *q_rope_out, const int32_t *block_table, const int32_t *seq_lens, void *c_kv,
                            void *k_pe, float *kv_scale, void *stream) {

@@ -40,6 +40,8 @@ hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const v
 bool up_v_mfma_supported(const mla_params_t &p);
 bool combine_fast_supported(const mla_params_t &p);
 bool combine_up_v_supported(const mla_params_t &p);
+hipError_t launch_expand(const mla_params_t &p, const void *c_kv, const float *kv_scale, void *c_out,
+                         hipStream_t stream);
 hipError_t launch_combine_up_v(const mla_params_t &p, const float *o_part, const float *lse_part, const void *W_UV,
                                void *out, float *lse_out, hipStream_t stream);
 hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,

@@ -26,7 +26,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
-           "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax",
+           "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax", "mla_expand_kv",
            "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
@@ -78,6 +78,7 @@ def lib():
             ("mla_combine_lse", [PP, P, P, P, P, P]),
             ("mla_up_v", [PP, P, P, P, P]),
             ("mla_combine_up_v", [PP, P, P, P, P, P, P]),
+            ("mla_expand_kv", [PP, P, P, P, P]),
             ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
             ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
             ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
@@ -217,6 +218,16 @@ def up_v(p: Params, o_latent, W_UV, out, stream=None) -> None:
                           _stream(stream)))
 
 
+def expand_kv(p: Params, c_kv, kv_scale, c_out, stream=None) -> None:
+    """bf16 copy of an e4m3 cache with each token's scale applied: c_out = bf16(code * scale)."""
+    _check(lib().mla_expand_kv(
+        ctypes.byref(p),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), FP8_E4M3),
+        _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+        _ptr(c_out, "c_out", (p.num_pages, PAGE, p.d_c), BF16),
+        _stream(stream)))
+
+
 def combine_up_v(p: Params, o_part, lse_part, W_UV, out, lse_out=None, stream=None) -> None:
     """combine_lse followed by up_v in one launch (merged latent rows stay on chip)."""
     rows = (p.B, p.Sq, p.H)
@@ -314,9 +325,13 @@ class BoundCalls:
     the parameters on every call).  The tensors must stay alive and in place."""
 
     def __init__(self, p: Params, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
-                 W_UK, W_UV, q_abs, o_part, lse_part, o_latent, lse, out, stream=None, fused=False):
+                 W_UK, W_UV, q_abs, o_part, lse_part, o_latent, lse, out, stream=None, fused=False,
+                 expand=None):
         rows = (p.B, p.Sq, p.H)
         self.fused = fused
+        # expand = (decode parameters with a bf16 cache, the bf16 workspace): the step
+        # expands the e4m3 cache first and attends to the copy
+        pd = p if expand is None else expand[0]
         if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
             raise ValueError("block_table and seq_lens must be int32")
         self.p = p
@@ -327,11 +342,12 @@ class BoundCalls:
             (L.mla_absorb_q, (pp, _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
                               _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
                               _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype), st)),
-            (L.mla_decode_splitkv, (pp, _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype),
+            (L.mla_decode_splitkv, (ctypes.byref(pd), _ptr(q_abs, "q_abs", rows + (p.d_c,), p.latent_dtype),
                                     _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
-                                    _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+                                    _ptr(c_kv if expand is None else expand[1], "c_kv",
+                                         (p.num_pages, PAGE, p.d_c), pd.kv_dtype),
                                     _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
-                                    _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+                                    _ptr(kv_scale if expand is None else None, "kv_scale", (p.num_pages, PAGE), F32),
                                     _ptr(block_table, "block_table", (p.B, p.max_pages)),
                                     _ptr(seq_lens, "seq_lens", (p.B,)),
                                     _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
@@ -350,6 +366,16 @@ class BoundCalls:
                                   _ptr(lse, "lse_out", rows, F32), st)),
         )
         self._step = (self._calls[0], self._calls[1], self._calls[4]) if fused else self._calls[:4]
+        if expand is not None:
+            ex = (L.mla_expand_kv, (pp, _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), FP8_E4M3),
+                                    _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+                                    _ptr(expand[1], "c_out", (p.num_pages, PAGE, p.d_c), BF16), st))
+            self._calls = self._calls + (ex,)
+            self._step = (ex,) + self._step
+
+    def expand_kv(self):
+        f, a = self._calls[5]
+        _check(f(*a))
 
     def absorb_q(self):
         f, a = self._calls[0]
@@ -384,9 +410,16 @@ class DecodeStep:
     runs the four library calls on the current stream (fused=True: absorb, decode
     and the fused merge + up-projection; o_latent is then not written)."""
 
-    def __init__(self, p: Params, device="cuda", fused=False):
+    def __init__(self, p: Params, device="cuda", fused=False, expand=False):
         self.p = p
         self.fused = fused
+        # expand (e4m3 cache only): each step first expands the cache to a bf16 copy
+        # (mla_expand_kv) and attends to it with the bf16 kernel
+        self.expand = bool(expand) and p.kv_dtype == FP8_E4M3
+        if self.expand:
+            self.p_dec = p.copy()
+            self.p_dec.kv_dtype = BF16
+            self.kv_bf16 = torch.empty((p.num_pages, PAGE, p.d_c), dtype=torch.bfloat16, device=device)
         rows = (p.B, p.Sq, p.H)
         self.q_abs = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
         self.o_part = torch.empty(rows + (p.num_splits, p.d_c), dtype=torch.float32, device=device)
@@ -400,14 +433,20 @@ class DecodeStep:
         """The four calls on these inputs, marshalled once (see BoundCalls)."""
         return BoundCalls(self.p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
                           self.q_abs, self.o_part, self.lse_part, self.o_latent, self.lse, self.out, stream,
-                          fused=self.fused)
+                          fused=self.fused, expand=(self.p_dec, self.kv_bf16) if self.expand else None)
 
     def __call__(self, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV,
                  stream=None):
         p = self.p
+        if self.expand:
+            expand_kv(p, c_kv, kv_scale, self.kv_bf16, stream)
         absorb_q(p, q_nope, W_UK, self.q_abs, stream)
-        decode_splitkv(p, self.q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
-                       self.o_part, self.lse_part, stream)
+        if self.expand:
+            decode_splitkv(self.p_dec, self.q_abs, q_rope, self.kv_bf16, k_pe, None, block_table, seq_lens,
+                           self.o_part, self.lse_part, stream)
+        else:
+            decode_splitkv(p, self.q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
+                           self.o_part, self.lse_part, stream)
         if self.fused:
             combine_up_v(p, self.o_part, self.lse_part, W_UV, self.out, self.lse, stream)
         else:

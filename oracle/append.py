@@ -107,6 +107,20 @@ def quantize_e4m3_rows(x: np.ndarray):
     return e4m3_nearest(r), scale.astype(np.float32)
 
 
+def expand_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 bits of code * scale for an e4m3 cache (the value semantics of the
+    per-token quantisation above): the code's value (the oracle's decoder, sign
+    from bit 7) times the token's fp32 scale as one fp32 product, then rounded to
+    bf16, nearest even (torch's conversion).  codes [..., d] uint8, scales [...]
+    float32 -> uint16 [..., d]."""
+    import torch
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = _e4m3_table()[np.minimum(codes & 0x7F, 0x7E)].astype(np.float32)   # 0x7F (NaN) never stored
+    val = np.where(codes & 0x80, -mag, mag).astype(np.float32)
+    prod = (val * np.asarray(scales, dtype=np.float32)[..., None]).astype(np.float32)
+    return torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def append_kv(c_new, kpe_new, block_table, seq_lens, Sq: int, q_rope=None):
     """Expected effect of appending the new tokens.
 

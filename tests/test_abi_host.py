@@ -153,6 +153,14 @@ def test_fused_tail_validates_on_the_host():
     assert L.mla_combine_up_v(ctypes.byref(v3(Sq=17)), d, d, d, d, None, None) == 2
 
 
+def test_expand_validates_on_the_host():
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    q = v3(Sq=1, kv_dtype=mla.FP8_E4M3)
+    assert L.mla_expand_kv(ctypes.byref(q), d, None, d, None) == 1
+    assert L.mla_expand_kv(ctypes.byref(v3(Sq=1)), d, d, d, None) == 3          # bf16 cache: nothing to expand
+
+
 def test_status_strings():
     L = mla.lib()
     for code, name in mla.STATUS.items():

@@ -113,3 +113,21 @@ def test_positions_and_slots():
     # sequence 1: positions 62..65 -> pages 7, 7, 3, 3
     assert page[1].tolist() == [7, 7, 3, 3] and slot[1].tolist() == [62, 63, 0, 1]
     assert A.positions(seq_lens, 4)[1].tolist() == [62, 63, 64, 65]
+
+
+def test_expand_is_decoded_code_times_scale():
+    """The expansion of an e4m3 cache: with a power-of-two scale the product is
+    exact, so the bf16 value equals the code's OCP value times the scale (every
+    e4m3 value has at most 4 significant bits, exact in bf16); with other scales it
+    is the fp32 product rounded to bf16."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F].reshape(1, -1)            # no NaN codes
+    for sc in (1.0, 2.0 ** -9, 16.0):
+        got = A.expand_e4m3(codes, np.array([sc], np.float32))
+        vals = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).double().numpy()[0]
+        ref = torch.from_numpy(codes[0].copy()).view(torch.float8_e4m3fn).double().numpy() * sc
+        assert np.array_equal(vals, ref)
+    sc = np.float32(0.3)
+    got = A.expand_e4m3(codes, np.array([sc], np.float32))
+    ref = (torch.from_numpy(codes[0].copy()).view(torch.float8_e4m3fn).float() * torch.tensor(0.3)).bfloat16()
+    assert np.array_equal(got[0], ref.view(torch.int16).numpy().view(np.uint16))
