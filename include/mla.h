@@ -326,10 +326,11 @@ mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, co
 int64_t mla_prefill_lmax(const mla_params_t *p);
 
 /* The switch of "MLA Matrix Absorption" sec. 6 (host-only): 1 when Sq new tokens
- * per sequence are served by the absorbed path, 0 when by the non-absorbed one;
- * -1 for invalid parameters.  The pages put the crossover near 64; the absorbed
- * kernels here take at most 16 new tokens per sequence, so the switch is at
- * Sq <= 16 (both paths accept 1 <= Sq <= 16 and agree there). */
+ * per sequence are served faster by the absorbed path, 0 when by the non-absorbed
+ * one; -1 for invalid parameters.  The switch is at Sq = 64, as on the pages: the
+ * two paths measure equal there on this hardware (and the absorbed one is faster
+ * below, the non-absorbed one above).  Both paths accept 1 <= Sq <= 256 and agree
+ * there; the non-absorbed path accepts up to 65,536. */
 int32_t mla_prefer_absorbed(const mla_params_t *p);
 
 /* Host-only validation of *p (no GPU needed).  Returns MLA_OK or the first error. */

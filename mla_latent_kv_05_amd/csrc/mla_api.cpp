@@ -33,7 +33,11 @@ bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
 // new tokens per sequence: at most kMaxAbsorbedSq on the absorbed path, kMaxPrefill on
 // the non-absorbed one
-constexpr int kMaxAbsorbedSq = 16;
+constexpr int kMaxAbsorbedSq = 256;
+// the absorbed path below, the non-absorbed one from here on: measured equal at 64 new
+// tokens per sequence (4 x 4,096 and 16 x 2,048 cached positions), the absorbed
+// path faster below and the non-absorbed one faster above
+constexpr int kSwitchSq = 64;
 constexpr int kMaxPrefill = 65536;
 
 mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
@@ -256,7 +260,7 @@ int64_t mla_prefill_lmax(const mla_params_t *p) {
 
 int32_t mla_prefer_absorbed(const mla_params_t *p) {
     if (check(p, kMaxPrefill) != MLA_OK) return -1;
-    return p->Sq <= kMaxAbsorbedSq ? 1 : 0;
+    return p->Sq < kSwitchSq ? 1 : 0;
 }
 
 mla_status_t mla_decompress_kv(const mla_params_t *p, const void *c_kv, const int32_t *block_table,

@@ -21,6 +21,24 @@ def err_rms(got, ref) -> float:
     return float(np.max(np.abs(got - ref))) / rms
 
 
+def err_rows(got, ref, out_bf16=False) -> float:
+    """max over rows (last axis) of max|got - ref| / RMS(ref row); rows whose reference
+    is 0 (nothing visible) must be 0 exactly.  For many new tokens per sequence: the
+    rows see from one position to thousands, and a row that sees few positions
+    returns a few value rows at their full size, while the whole-output RMS is set
+    by the rows that average many positions.  With a bf16 output, each element's own
+    rounding (at most 2^-9 of its value; 2^-8 allowed) is taken off first."""
+    got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
+    rms = np.sqrt(np.mean(ref ** 2, axis=1))
+    empty = rms == 0
+    assert (got[empty] == 0).all()
+    d = np.abs(got - ref)
+    if out_bf16:
+        d = np.maximum(d - 2.0 ** -8 * np.abs(ref), 0.0)
+    return float((d.max(axis=1)[~empty] / rms[~empty]).max())
+
+
 def assert_bf16_rounding(got, ref, acc_rel=1e-3):
     """Every element is within half a bf16 ulp (at most 2^-8 relative) of the exact
     value, plus an accumulation allowance of acc_rel * RMS(ref)."""

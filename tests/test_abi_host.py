@@ -56,7 +56,7 @@ def test_valid_params_pass():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("B", 0, 2), ("Sq", 0, 2), ("Sq", 17, 2), ("H", 0, 2), ("d_h", 0, 2), ("d_c", 2048, 2),
+    ("B", 0, 2), ("Sq", 0, 2), ("Sq", 257, 2), ("H", 0, 2), ("d_h", 0, 2), ("d_c", 2048, 2),
     ("d_r", -1, 2), ("page_size", 32, 2), ("num_pages", 0, 2), ("max_pages", 0, 2),
     ("num_splits", 0, 4), ("num_splits", 5000, 4), ("split_pages", 0, 4), ("scale", 0.0, 2),
     ("scale", float("inf"), 2), ("q_dtype", 2, 3), ("w_dtype", 7, 3), ("kv_dtype", 3, 3),
@@ -128,10 +128,12 @@ def test_prefill_entry_points_validate_on_the_host():
     L = mla.lib()
     d = ctypes.c_void_p(0x1000)
     p = v3(Sq=4096)
-    assert mla.lib().mla_check_params(ctypes.byref(p)) == 2          # too many rows for the absorbed path
+    assert mla.lib().mla_check_params(ctypes.byref(p)) == 2          # too many new tokens for the absorbed path
     assert [mla.lmax(v3(Sq=64, max_pages=n)) for n in (1, 4, 5, 8, 9)] == [256, 256, 512, 512, 768]
-    assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=16))
-    assert not mla.prefer_absorbed(v3(Sq=17)) and not mla.prefer_absorbed(p)
+    assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=63))
+    assert not mla.prefer_absorbed(v3(Sq=64)) and not mla.prefer_absorbed(p)
+    assert mla.lib().mla_check_params(ctypes.byref(v3(Sq=256))) == 0
+    assert mla.lib().mla_check_params(ctypes.byref(v3(Sq=257))) == 2
     assert L.mla_decompress_kv(ctypes.byref(p), d, d, d, d, d, d, None, None) == 1
     assert L.mla_prefill_attention(ctypes.byref(p), d, d, d, d, d, d, d, None, None) == 1
     q = v3(Sq=128, d_c=256)
@@ -150,7 +152,7 @@ def test_fused_tail_validates_on_the_host():
     assert L.mla_combine_up_v(ctypes.byref(q), d, d, d, d, None, None) == 6
     r = v3(Sq=1, latent_dtype=mla.F32)
     assert L.mla_combine_up_v(ctypes.byref(r), d, d, d, d, None, None) == 6
-    assert L.mla_combine_up_v(ctypes.byref(v3(Sq=17)), d, d, d, d, None, None) == 2
+    assert L.mla_combine_up_v(ctypes.byref(v3(Sq=257)), d, d, d, d, None, None) == 2
 
 
 def test_expand_validates_on_the_host():

@@ -16,7 +16,7 @@ import torch
 from mla_latent_kv_05_amd import inputs as I
 from mla_latent_kv_05_amd import mla
 from oracle import oracle as O
-from tests.helpers import (TOL, DeviceCase, assert_bf16_rounding, err_rms, params_for, sample_rows,
+from tests.helpers import (TOL, DeviceCase, assert_bf16_rounding, err_rms, err_rows, params_for, sample_rows,
                            split_page_ranges)
 
 pytestmark = pytest.mark.gpu
@@ -197,6 +197,9 @@ SMALL = [
     ("v3_long", {"B": 2, "seq_lo": 8192, "seq_hi": 8192}, None),
     ("v3_sq4_fp8", {"B": 4, "seq_lo": 300, "seq_hi": 2000}, None),
     ("v3_sq4_fp8", {"B": 3}, [4, 3, 66]),
+    ("v3_b64", {"B": 3, "Sq": 32}, [40, 300, 1000]),          # many new tokens on the absorbed path
+    ("v3_b64", {"B": 2, "Sq": 64}, [64, 700]),                # whole prompt of 64 tokens; a prefix
+    ("v3_sq4_fp8", {"B": 2, "Sq": 32}, [40, 900]),            # the same on the e4m3 cache
 ]
 
 
@@ -210,11 +213,17 @@ def test_step_matches_oracle(wl_name, over, lens):
     st = DeviceCase(case).step(p)
     torch.cuda.synchronize()
     out, ol, lse = O.decode(case)
-    e = err_rms(st.out.float().cpu().numpy(), out)
+    # many new tokens per sequence: rows see from a few positions to thousands, so
+    # the error is taken per row (a few-position row returns values at full size)
+    e = (err_rows if wl.Sq >= 16 else err_rms)(st.out.float().cpu().numpy(), out)
     note(f"  out err {e:.3e}")
     assert e <= tol_of(wl)
     vis = lse > -np.inf
-    assert np.abs(st.lse.cpu().numpy()[vis] - lse[vis]).max() <= (1e-5 if wl.dtype == "f32" else 2e-3)
+    # lse: a row that sees one position returns that one score, whose error from the
+    # bf16 absorbed query is about scale * 2^-9 * |q_abs| / sqrt(3) ~ 4e-4 (one sigma)
+    # at these distributions; with many new tokens such rows exist, so 4e-3 (10 sigma)
+    lse_tol = 1e-5 if wl.dtype == "f32" else (4e-3 if wl.Sq >= 16 else 2e-3)
+    assert np.abs(st.lse.cpu().numpy()[vis] - lse[vis]).max() <= lse_tol
     assert np.all(st.lse.cpu().numpy()[~vis] == -np.inf)
 
 

@@ -22,7 +22,7 @@ from mla_latent_kv_05_amd import inputs as I
 from mla_latent_kv_05_amd import mla
 from oracle import oracle as O
 from oracle import prefill as PF
-from tests.helpers import assert_bf16_rounding
+from tests.helpers import assert_bf16_rounding, err_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -65,22 +65,6 @@ def run_path(case, p):
     mla.prefill_attention(p, d["q_nope"], d["q_rope"], kn, vt, d["k_pe"], d["block_table"], d["seq_lens"], out)
     torch.cuda.synchronize()
     return kn.cpu(), vt.cpu(), out.cpu()
-
-
-def err_rows(got, ref, out_bf16=False) -> float:
-    """max over rows (last axis = d_h) of max|got - ref| / RMS(ref row); rows whose
-    reference is 0 (nothing visible) must be 0 exactly.  With a bf16 output, each
-    element's own rounding (at most 2^-9 of its value; 2^-8 allowed) is taken off
-    first, so the bound stays that of the computation."""
-    got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
-    ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
-    rms = np.sqrt(np.mean(ref ** 2, axis=1))
-    empty = rms == 0
-    assert (got[empty] == 0).all()
-    d = np.abs(got - ref)
-    if out_bf16:
-        d = np.maximum(d - 2.0 ** -8 * np.abs(ref), 0.0)
-    return float((d.max(axis=1)[~empty] / rms[~empty]).max())
 
 
 def check_decompressed(case, kn, vt):
@@ -131,13 +115,14 @@ def test_prefill_rows_with_nothing_visible():
     assert err_rows(out.double().numpy(), ref) <= 2e-2
 
 
-def test_both_paths_agree_where_both_apply():
-    """At Sq = 16 both the absorbed steps and the non-absorbed path serve the same
-    rows: the two GPU results agree with each other and with the oracle."""
-    wl = I.workload("v3_b64", B=3, Sq=16)
-    case = I.make_case(wl, seq_lens=[16, 300, 777])
+@pytest.mark.parametrize("Sq,lens", [(16, [16, 300, 777]), (64, [64, 200, 1000])])
+def test_both_paths_agree_where_both_apply(Sq, lens):
+    """Where both paths take the new tokens, the absorbed steps and the non-absorbed
+    path agree with each other and with the oracle."""
+    wl = I.workload("v3_b64", B=3, Sq=Sq)
+    case = I.make_case(wl, seq_lens=lens)
     p = params(case)
-    note("absorbed vs non-absorbed at Sq=16")
+    note(f"absorbed vs non-absorbed at Sq={Sq}")
     _, _, out_na = run_path(case, p)
     d = {k: getattr(case, k).cuda() for k in ("q_nope", "q_rope", "c_kv", "k_pe", "block_table", "seq_lens",
                                               "W_UK", "W_UV")}
