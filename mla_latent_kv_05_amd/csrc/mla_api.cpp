@@ -34,10 +34,11 @@ bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 // new tokens per sequence: at most kMaxAbsorbedSq on the absorbed path, kMaxPrefill on
 // the non-absorbed one
 constexpr int kMaxAbsorbedSq = 256;
-// the absorbed path below, the non-absorbed one from here on: measured equal at 64 new
-// tokens per sequence (4 x 4,096 and 16 x 2,048 cached positions), the absorbed
-// path faster below and the non-absorbed one faster above
-constexpr int kSwitchSq = 64;
+// the absorbed path below, the non-absorbed one from here on: the two measure equal at
+// 180 to 195 new tokens per sequence (4 x 4,096 and 16 x 2,048 cached positions), the
+// absorbed path faster below (linear in the new tokens) and the non-absorbed one above
+// (dominated by the decompression of every cached position)
+constexpr int kSwitchSq = 192;
 constexpr int kMaxPrefill = 65536;
 
 mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
@@ -126,6 +127,10 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
     int64_t P = std::max<int64_t>(1, num_cus / wg_per_part);
     if (!mfma) P = std::max<int64_t>(1, 2ll * num_cus / wg_per_part);
+    // at least 8 parts even when that takes several rounds of workgroups (many query
+    // rows per token): with 2 or 4 parts every page is read by all row groups at once
+    // (measured at 4 x 4,096 positions: 64 new tokens, 2 parts 1.28 ms, 8 parts 0.44 ms)
+    P = std::max<int64_t>(P, 8);
     // parts of at least 4 pages keep the fp32 partials (d_c*4 bytes per row) small next
     // to the cache they summarise (measured at B = 1: 4 pages per part beat 8, 2 and 1)
     P = std::min(P, std::max<int64_t>(1, pages_lo / 4));
