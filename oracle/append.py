@@ -25,6 +25,9 @@ What it computes, with the passages it follows:
                 both divisions in fp32 (the precision the kernel decides in);
                 the code is the E4M3 value nearest to r_j, ties to the even code,
                 magnitudes above 448 saturating to 448, sign kept.
+  expansion     the values such a cache holds, code * scale, as bf16: the code's
+                E4M3 value times the token's scale in one fp32 product, rounded
+                to bf16 nearest even (what the bf16 route over an e4m3 cache reads).
 """
 from __future__ import annotations
 
