@@ -33,6 +33,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+STEP_BLOCK = 50                # steps per block of the step-time spread
+
+
+def pct(xs):
+    """[p10, p50, p90] of a list of times, rounded to 0.01."""
+    import numpy as np
+    return [round(float(v), 2) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
+
+
 # rocprofv3 counter summary of the attention kernel on this workload (FETCH_SIZE /
 # WRITE_SIZE in KiB per dispatch) and the hash of the kernel source it was taken on
 COUNTERS = os.path.join(ROOT, "profiles", "decode8_bf16_v3_b64_counters.txt")
@@ -146,13 +155,21 @@ def main():
     for i in range(args.warmup):
         bound_f[i % args.replicas]()
     torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
+    # an event at every block boundary (one per STEP_BLOCK steps) gives the spread of
+    # the per-step time over the region without gaps inside the steps
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps // STEP_BLOCK + 2)]
+    nm = 0
+    marks[nm].record(stream)
+    nm += 1
     for i in range(args.steps):
         bound_f[i % args.replicas]()
-    f1.record(stream)
+        if (i + 1) % STEP_BLOCK == 0 or i + 1 == args.steps:
+            marks[nm].record(stream)
+            nm += 1
     torch.cuda.synchronize()
-    ms_fused = f0.elapsed_time(f1) / args.steps
+    ms_fused = marks[0].elapsed_time(marks[nm - 1]) / args.steps
+    blk_us = [marks[k].elapsed_time(marks[k + 1]) * 1e3 / min(STEP_BLOCK, args.steps - (k * STEP_BLOCK))
+              for k in range(nm - 1)]
     assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
 
     # e4m3 cache: also the route that expands the cache to bf16 first (for a step
@@ -235,6 +252,7 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(wl.name),
             "launch_us": round(dec_avg_ms * 1e3, 2),
+            "launch_us_p10_p50_p90": pct([m * 1e3 for m in dec_ms]),
             "bytes_per_launch": cost.decode_bytes,
             "mfma_tflops": round(cost.decode_flops / (dec_avg_ms * 1e-3) / 1e12, 1),
             "frac_of_measured_copy": round(achieved_gbs / peaks["hbm_copy_gbs"], 4),
@@ -248,7 +266,8 @@ def main():
                            "value": round(cost.cache_bytes / (ms_four * 1e-3) / 1e12, 4)},
             "fused_tail": {"calls": "absorb_q, decode_splitkv, combine_up_v",
                            "us_per_step": round(ms_fused * 1e3, 2),
-                           "value": round(cost.cache_bytes / (ms_fused * 1e-3) / 1e12, 4)},
+                           "value": round(cost.cache_bytes / (ms_fused * 1e-3) / 1e12, 4),
+                           "block_us_p10_p50_p90": pct(blk_us), "block_steps": STEP_BLOCK},
             **({"expand_fused_tail": {"calls": "expand_kv, absorb_q, decode_splitkv (bf16 copy), combine_up_v",
                                       "us_per_step": round(ms_expand * 1e3, 2),
                                       "value": round(cost.cache_bytes / (ms_expand * 1e-3) / 1e12, 4)}}

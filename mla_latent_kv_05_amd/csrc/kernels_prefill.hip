@@ -13,8 +13,9 @@
 // positions); wave w holds the latent rows of 32 of the positions as MFMA operands
 // (128 VGPRs) for the whole workgroup.  The weights stream through LDS in passes
 // of 64 rows (output dims) of one head, W_UK[h] then W_UV[h], each pass in chunks
-// of 256 latent dims (double-buffered, two chunks ahead in registers, shared by
-// the 8 waves):
+// of 256 latent dims (direct global->LDS copies into a ring of three buffers, two
+// chunks ahead, shared by the 8 waves; the blocks running together on an XCD start
+// at different passes):
 //   keys:   D[d, t] = W_UK[h] . c^T (weight rows as the A operand, latent rows as B),
 //   values: D[t, d] = c . W_UV[h]^T (latent rows as A, weight rows as B),
 // the latent registers serving both roles unchanged (both operands take 8
@@ -41,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "decode_common.h"
 #include "gfx950.h"
 #include "mla_internal.h"
 
@@ -48,6 +50,19 @@ namespace mla {
 namespace {
 
 using namespace gfx;
+
+// Four 16-byte-per-lane direct copies (buffer_load_dwordx4 ... lds) to consecutive
+// KiB of LDS from l on; copy i reads base + soff + v<i> in each lane (inline asm, as
+// in the attention kernels, so the compiler adds no waits of its own on them).
+__device__ __forceinline__ void dma_rows4_fixed(const void *base, uint32_t bytes, uint32_t l, uint32_t soff,
+                                                uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+    using dec::hi32;
+    using dec::lo32;
+    asm volatile(MLA_DMA_SETUP MLA_DMA_X4(v0) "s_add_u32 m0, m0, 1024\n\t" MLA_DMA_X4(v1)
+                 "s_add_u32 m0, m0, 1024\n\t" MLA_DMA_X4(v2) "s_add_u32 m0, m0, 1024\n\t" MLA_DMA_X4(v3)
+                 :: MLA_DMA_BASE(base, bytes, l, soff), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3)
+                 : MLA_DMA_CLOBBERS);
+}
 
 constexpr int kDh = 128;
 constexpr int kDc = 512;
@@ -58,11 +73,32 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecPos = 32 * kDecWaves;        // positions of one decompress workgroup (32 per wave)
 constexpr int kDecRows = 64;                   // weight rows (output dims) of one pass
 constexpr int kWChunk = 256;                   // latent dims of one staged weight chunk
-constexpr int kWStride = 2 * kWChunk + 16;     // bytes per staged weight row (padded: no bank conflicts)
-constexpr int kWStage = kDecRows * kWStride;
+constexpr int kWStage = kDecRows * kWChunk * 2;  // one staged chunk: 64 rows of 512 bytes (swizzled)
+constexpr int kWBufs = 3;                      // staged chunks: in use, landed, in flight
+// The 32 blocks that run at once on one XCD share a head group; block j of them
+// starts at pass kDecRot * j (mod the pass count), so that they do not all ask
+// the XCD's L2 for the same weight chunk at the same moment (in lockstep they
+// fetched at about 2 TB/s overall and took 1.0-1.1 ms at 4 x 4,096 positions;
+// staggered, 0.66-0.70 ms).
+constexpr int kDecRot = 2;
 static_assert(kDecPos == 256, "prefill_lmax rounds the row stride to whole decompression tiles");
-constexpr int kDecDepth = 2;                   // weight chunks in flight ahead of the one in use
+static_assert(kDecWaves * 4 * 1024 == kWStage, "four 1 KiB copies per wave fill one staged chunk");
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Instruction order of one staged chunk's 32 operand reads and 32 MFMAs: the first
+// kReadAhead reads, then one MFMA and one read in turn, so that each read is issued
+// kReadAhead MFMAs before its product (the default schedule issues it just before).
+constexpr int kReadAhead = 6;
+__device__ __forceinline__ void read_ahead_schedule() {
+    constexpr int kN = 2 * (kWChunk / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);     // DS reads
+#pragma unroll
+    for (int i = 0; i < kN - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
+}
 
 // tile row r holds position swap23(r) of the tile
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -72,7 +108,8 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
     const mla_params_t p, const uint16_t *__restrict__ c_kv, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ W_UK, const uint16_t *__restrict__ W_UV,
     uint16_t *__restrict__ k_nope, uint16_t *__restrict__ v_t) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kWStage];
+    // 1 KiB alignment: the operand addresses XOR bits 5..8 of buffer offsets
+    __shared__ __attribute__((aligned(1024))) char lds[kWBufs * kWStage];
     const int tid = threadIdx.x, lane = tid & 63, t32 = lane & 31, g = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t lmax = prefill_lmax(p);               // a multiple of kDecPos
@@ -80,6 +117,7 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
     const int64_t nblk = gridDim.x;
     int64_t lb = blockIdx.x;
     if ((nblk & 7) == 0) lb = (lb & 7) * (nblk >> 3) + (lb >> 3);
+    const int lb_run = static_cast<int>(lb & 31);           // position among concurrent blocks
     const int pt = static_cast<int>(lb % n_pt);
     lb /= n_pt;
     const int b = static_cast<int>(lb % p.B);
@@ -103,51 +141,52 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
         }
     }
 
-    // staging: thread tid moves 16 bytes (8 latent dims) of kStgPass weight rows
-    constexpr int kPartsPerRow = kWChunk / 8;
-    constexpr int kRowsPerPass = kDecThreads / kPartsPerRow;
-    constexpr int kStgPass = kDecRows / kRowsPerPass;
-    const int sr = tid / kPartsPerRow, sp = tid % kPartsPerRow;
+    // Weight chunks reach LDS by direct copies (buffer_load ... lds), three buffers:
+    // stage st (pass st / kChunks, chunk st % kChunks) in buffer st % 3, copied two
+    // stages ahead.  Row R of a chunk (512 bytes, 32 chunks of 16 bytes) holds
+    // logical chunk c at physical chunk c ^ (R % 32); one copy instruction of wave w
+    // fills rows 8w + 2i and 8w + 2i + 1, lane l taking physical chunk l % 32 of row
+    // 8w + 2i + l / 32.
     const uint32_t lds0 = lds_addr(lds);
-    // kDecDepth register sets: the chunk kDecDepth stages ahead is in flight
-    u32x4 stg[kDecDepth][kStgPass];
-    auto load_w = [&](int set, const uint16_t *Wrows, int kc) {
+    uint32_t voff[4];
 #pragma unroll
-        for (int i = 0; i < kStgPass; ++i)
-            stg[set][i] = *reinterpret_cast<const u32x4 *>(Wrows + static_cast<int64_t>(sr + kRowsPerPass * i) * kDc +
-                                                           kc * kWChunk + sp * 8);
-    };
-    auto settle = [&]() {
-#pragma unroll
-        for (int j = 0; j < kDecDepth; ++j)
-#pragma unroll
-            for (int i = 0; i < kStgPass; ++i) asm volatile("" ::"v"(stg[j][i]));
-    };
-    auto store_w = [&](int set, int buf) {
-#pragma unroll
-        for (int i = 0; i < kStgPass; ++i)
-            lds_store<u32x4>(lds0 + buf * kWStage + (sr + kRowsPerPass * i) * kWStride + sp * 16, stg[set][i]);
-    };
+    for (int i = 0; i < 4; ++i) {
+        const int R = 8 * w + 2 * i + (lane >> 5);
+        voff[i] = static_cast<uint32_t>(R * kDc * 2 + (((lane & 31) ^ (R & 31)) << 4));
+    }
     // passes: (head, keys | values, row half); pass ps covers rows kDecRows*(ps % 2) ..
     constexpr int kHalves = kDh / kDecRows;
     const int h0 = hg * kDecHeads;
     const int n_ps = 2 * kHalves * min(kDecHeads, p.H - h0);
-    constexpr int kChunks = kDc / kWChunk;               // stages per pass; stage s uses LDS buffer s % 2
+    constexpr int kChunks = kDc / kWChunk;               // stages per pass
     const int n_st = n_ps * kChunks;
-    auto wrows = [&](int ps) {
-        const int hk = ps / kHalves;
-        return ((hk & 1) ? W_UV : W_UK) + (static_cast<int64_t>(h0 + (hk >> 1)) * kDh + kDecRows * (ps % kHalves)) * kDc;
+    const int rot = (kDecRot * lb_run) % n_ps;
+    auto pass_of = [&](int i) { const int q = i + rot; return q >= n_ps ? q - n_ps : q; };
+    // copy stage s2 (clamped to the last: the copy past the end refills a buffer no
+    // stage reads, so that every stage issues the same number of copies) into buffer
+    // `buf`; the descriptor covers one head's matrix
+    auto copy_stage = [&](int s2, int buf) {
+        s2 = min(s2, n_st - 1);
+        const int ps2 = pass_of(s2 / kChunks), hk = ps2 / kHalves;
+        const uint16_t *Wh = ((hk & 1) ? W_UV : W_UK) + static_cast<int64_t>(h0 + (hk >> 1)) * kDh * kDc;
+        const uint32_t soff = static_cast<uint32_t>((kDecRows * (ps2 % kHalves) * kDc + (s2 % kChunks) * kWChunk) * 2);
+        dma_rows4_fixed(Wh, kDh * kDc * 2, lds0 + buf * kWStage + w * 4096, soff, voff[0], voff[1], voff[2], voff[3]);
     };
-    const uint32_t a_row = swap23(t32) * kWStride + g * 16;   // weight rows as the A operand (keys)
-    const uint32_t b_row = t32 * kWStride + g * 16;           // weight rows as the B operand (values)
+    // MFMA operand reads: row R = 32dt + x (x = swap23(t32) for the keys' A operand,
+    // t32 for the values' B operand), logical chunk 2ks + g -> physical
+    // (2ks + g) ^ x, at R*512 + physical*16 = (base ^ (ks << 5)) + dt*16384 with
+    // base = x*512 + ((x & 30) << 4) + (((g ^ x) & 1) << 4)
+    auto rbase = [&](int x) -> uint32_t {
+        return static_cast<uint32_t>(x * 512 + ((x & 30) << 4) + (((g ^ x) & 1) << 4));
+    };
+    const uint32_t a_base = rbase(swap23(t32));
+    const uint32_t b_base = rbase(t32);
 
-#pragma unroll
-    for (int i = 0; i < kDecDepth; ++i) load_w(i, wrows(0), i);
-    store_w(0, 0);
-    settle();                                            // nothing in flight on entry, as after every pass
-    __syncthreads();
+    copy_stage(0, 0);
+    copy_stage(1, 1);
     for (int ps = 0; ps < n_ps; ++ps) {
-        const bool is_v = (ps / kHalves) & 1;
+        const int pe = pass_of(ps);
+        const bool is_v = (pe / kHalves) & 1;
         f32x16 acc[kDecRows / 32];
 #pragma unroll
         for (int dt = 0; dt < kDecRows / 32; ++dt)
@@ -156,39 +195,40 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
 #pragma unroll
         for (int kc = 0; kc < kChunks; ++kc) {
             const int st = ps * kChunks + kc;
-            // stage st + kDecDepth into register set st % kDecDepth (its previous
-            // contents, stage st, are already in LDS); unconditional (the last stage is
-            // re-read past the end) so that the wait before the store below counts only
-            // the older loads
-            const int st2 = min(st + kDecDepth, n_st - 1);
-            load_w(kc % kDecDepth, wrows(st2 / kChunks), st2 % kChunks);
-            const uint32_t buf = lds0 + (kc & 1) * kWStage;
+            // this wave's copies of stage st are complete once at most the copies
+            // issued after them are outstanding: those of stage st + 1 (4) and, from
+            // the second pass on, the 4 output stores of the pass before
+            if (ps == 0) wait_vmcnt<4>();
+            else wait_vmcnt<8>();
+            // every wave's copies have landed, and every wave is done with buffer
+            // (st + 2) % 3 = (st - 1) % 3
+            barrier_lds();
+            copy_stage(st + 2, (st + 2) % kWBufs);
+            const uint32_t buf = lds0 + (st % kWBufs) * kWStage;
             if (is_v) {
+                const uint32_t base = buf + b_base;
 #pragma unroll
                 for (int ks = 0; ks < kWChunk / 16; ++ks)
 #pragma unroll
                     for (int dt = 0; dt < kDecRows / 32; ++dt) {
-                        const u32x4 wb = lds_load<u32x4>(buf + b_row + dt * 32 * kWStride + ks * 32);
+                        const u32x4 wb = lds_load<u32x4>((base ^ (ks << 5)) + dt * 32 * 512);
                         acc[dt] = mfma32(cop[kc * (kWChunk / 16) + ks], as_bf16x8(wb), acc[dt]);
                     }
+                read_ahead_schedule();
             } else {
+                const uint32_t base = buf + a_base;
 #pragma unroll
                 for (int ks = 0; ks < kWChunk / 16; ++ks)
 #pragma unroll
                     for (int dt = 0; dt < kDecRows / 32; ++dt) {
-                        const u32x4 wa = lds_load<u32x4>(buf + a_row + dt * 32 * kWStride + ks * 32);
+                        const u32x4 wa = lds_load<u32x4>((base ^ (ks << 5)) + dt * 32 * 512);
                         acc[dt] = mfma32(as_bf16x8(wa), cop[kc * (kWChunk / 16) + ks], acc[dt]);
                     }
+                read_ahead_schedule();
             }
-            if (st + 1 < n_st) store_w((kc + 1) % kDecDepth, (kc + 1) & 1);
-            __syncthreads();
         }
-        // The weight chunk in flight was issued a stage ago: wait for it here, before
-        // the output stores, so that no later wait for it also waits for them (the
-        // empty asm consumes the staging registers, which makes the compiler wait).
-        settle();
-        const int h = h0 + ps / (2 * kHalves);
-        const int d_base = kDecRows * (ps % kHalves);
+        const int h = h0 + pe / (2 * kHalves);
+        const int d_base = kDecRows * (pe % kHalves);
         // acc[dt][8hf + e]: keys: dim d_base + 32dt + 16hf + 8g + e of position pos;
         //                   values: position tw + 16hf + 8g + e of dim d_base + 32dt + t32
 #pragma unroll
@@ -200,9 +240,8 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
                                       cvt_pk_bf16(acc[dt][8 * hf + 4], acc[dt][8 * hf + 5]),
                                       cvt_pk_bf16(acc[dt][8 * hf + 6], acc[dt][8 * hf + 7])};
                 // unconditional (positions past seq_len hold zero latents, so their rows
-                // are written as zeros; the tile ends inside lmax): the compiler then
-                // counts these stores, and the wait for the next weight chunk does not
-                // wait for them
+                // are written as zeros; the tile ends inside lmax): every pass issues
+                // the same 4 stores, which the copy waits above count
                 if (!is_v) {
                     *reinterpret_cast<u32x4 *>(k_nope + ((static_cast<int64_t>(b) * lmax + pos) * p.H + h) * kDh +
                                                d_base + 32 * dt + 16 * hf + 8 * g) = v;
@@ -213,6 +252,9 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kernel(
                 }
             }
     }
+    // the copies past the end are still in flight: no wave may end (and free the
+    // workgroup's LDS) before they have landed
+    wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
