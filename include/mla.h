@@ -328,8 +328,8 @@ int64_t mla_prefill_lmax(const mla_params_t *p);
 /* The switch of "MLA Matrix Absorption" sec. 6 (host-only): 1 when Sq new tokens
  * per sequence are served faster by the absorbed path, 0 when by the non-absorbed
  * one; -1 for invalid parameters.  The pages put the crossover near 64 new tokens;
- * with these kernels the two paths measure equal near 190, so the switch is at
- * Sq = 192 (absorbed below).  Both paths accept 1 <= Sq <= 256 and agree there;
+ * with these kernels the two paths measure equal near 120, so the switch is at
+ * Sq = 120 (absorbed below).  Both paths accept 1 <= Sq <= 256 and agree there;
  * the non-absorbed path accepts up to 65,536. */
 int32_t mla_prefer_absorbed(const mla_params_t *p);
 

@@ -35,10 +35,10 @@ bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 // the non-absorbed one
 constexpr int kMaxAbsorbedSq = 256;
 // the absorbed path below, the non-absorbed one from here on: the two measure equal at
-// 180 to 195 new tokens per sequence (4 x 4,096 and 16 x 2,048 cached positions), the
+// 115 to 125 new tokens per sequence (4 x 4,096 and 16 x 2,048 cached positions), the
 // absorbed path faster below (linear in the new tokens) and the non-absorbed one above
 // (dominated by the decompression of every cached position)
-constexpr int kSwitchSq = 192;
+constexpr int kSwitchSq = 120;
 constexpr int kMaxPrefill = 65536;
 
 mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {

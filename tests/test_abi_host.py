@@ -130,8 +130,8 @@ def test_prefill_entry_points_validate_on_the_host():
     p = v3(Sq=4096)
     assert mla.lib().mla_check_params(ctypes.byref(p)) == 2          # too many new tokens for the absorbed path
     assert [mla.lmax(v3(Sq=64, max_pages=n)) for n in (1, 4, 5, 8, 9)] == [256, 256, 512, 512, 768]
-    assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=191))
-    assert not mla.prefer_absorbed(v3(Sq=192)) and not mla.prefer_absorbed(p)
+    assert mla.prefer_absorbed(v3(Sq=1)) and mla.prefer_absorbed(v3(Sq=119))
+    assert not mla.prefer_absorbed(v3(Sq=120)) and not mla.prefer_absorbed(p)
     assert mla.lib().mla_check_params(ctypes.byref(v3(Sq=256))) == 0
     assert mla.lib().mla_check_params(ctypes.byref(v3(Sq=257))) == 2
     assert L.mla_decompress_kv(ctypes.byref(p), d, d, d, d, d, d, None, None) == 1

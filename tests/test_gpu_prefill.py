@@ -93,7 +93,7 @@ def test_prefill_path_matches_oracle(B, Sq, lens):
     wl = I.workload("v3_b64", B=B, Sq=Sq)
     case = I.make_case(wl, seq_lens=lens)
     p = params(case)
-    assert mla.prefer_absorbed(p) == (Sq < 192)     # the switch (these cases run the non-absorbed path anyway)
+    assert mla.prefer_absorbed(p) == (Sq < 120)     # the switch (these cases run the non-absorbed path anyway)
     note(f"prefill B={B} Sq={Sq} lens={lens}")
     kn, vt, out = run_path(case, p)
     check_decompressed(case, kn, vt)
