@@ -434,11 +434,31 @@ def prefill_bench(mla, A, dev, stream, args, B=4, x=4096):
                 "unit": "TFLOP/s", "frac": round(t / BF16_PEAK_TFLOPS, 4)}
 
     tot = cost.decompress_flops + cost.attention_flops
+    # context for the decompression: a library GEMM of its own shape, the latent rows
+    # [B*x, d_c] times [W_UK; W_UV]^T [d_c, 2*H*d_h] into one contiguous bf16 matrix
+    del kn, vt
+    lat = c_kv.view(-1, d_c)
+    w_t = torch.cat([W_UK, W_UV]).view(2 * H * d_h, d_c).t().contiguous()
+    kv_lib = torch.empty((lat.shape[0], 2 * H * d_h), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.mm(lat, w_t, out=kv_lib)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(n):
+        torch.mm(lat, w_t, out=kv_lib)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    lib_us = g0.elapsed_time(g1) / n * 1e3
+    del kv_lib, w_t
+    dec = roof(cost.decompress_flops, d_us)
+    dec["library_same_shape_us"] = round(lib_us, 1)
+    dec["speedup_vs_library"] = round(lib_us / d_us, 3)
     return {"workload": f"whole-prompt prefill, B={B} sequences x {x} new tokens (seq_len {x}), H={H}, "
                         f"d_h={d_h}, d_c={d_c}, d_r={d_r}, bf16, permuted pages, bf16 out",
             "tokens_per_s": round(B * x / ((d_us + a_us) * 1e-6), 0),
             "bound": "mfma",
-            "decompress": roof(cost.decompress_flops, d_us),
+            "decompress": dec,
             "attention": roof(cost.attention_flops, a_us),
             "path": roof(tot, d_us + a_us)}
 
