@@ -12,14 +12,14 @@ What it computes, with the passages it follows:
   slot          position t lives at page block_table[b, t // 64], slot t % 64
                 (the paged cache with a block table that "DeepSeek-MLA-Principle"
                 lists among FlashMLA's ideas, sec. 3).
-  RoPE          the decode module's rotation of the shared RoPE key (and of the
-                query's RoPE part) at the token's position, rotate-half form with
-                base 10000: with half = d_r / 2 and
-                theta_i = pos * 10000^(-i / half), i < half,
-                    y[i]        = x[i] cos theta_i - x[i + half] sin theta_i
-                    y[i + half] = x[i + half] cos theta_i + x[i] sin theta_i
-                ("DeepSeek-MLA-Principle" sec. 3, why RoPE: the rotation R_pos
-                makes <R_m q, R_n k> depend on n - m only).
+  RoPE          the rotary embedding of the shared RoPE key (and of the query's
+                RoPE part) at the token's position: dimension i < half = d_r / 2
+                is paired with dimension i + half (the rotate-half pairing of the
+                decode module on the "DeepSeek MLA 架构详解" page), and the pair,
+                read as the complex number x_i + j x_{i+half}, is turned by the
+                angle pos * 10000^(-i / half), base 10000 ("DeepSeek-MLA-Principle"
+                sec. 3, why RoPE: a position-dependent rotation R_pos for which
+                <R_m q, R_n k> depends on n - m only).
   e4m3 cache    the pages fix no quantiser.  Per token: amax = max |x| over the
                 latent row, scale = max(amax, 2^-20) / 448 and r_j = x_j / scale,
                 both divisions in fp32 (the precision the kernel decides in);
@@ -54,21 +54,16 @@ def slots(block_table: np.ndarray, seq_lens: np.ndarray, Sq: int):
 
 
 def rope(x: np.ndarray, pos) -> np.ndarray:
-    """Rotate-half RoPE of the last axis of x (float64) at position pos
-    (a scalar or an array broadcasting against x[..., 0])."""
+    """Rotary embedding of the last axis of x (float64) at position pos (a scalar
+    or an array broadcasting against x[..., 0]): pair i, the complex number
+    x_i + j x_{i+half}, times exp(j pos 10000^(-i/half))."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     assert d % 2 == 0, "RoPE needs an even dimension"
     half = d // 2
-    i = np.arange(half, dtype=np.float64)
-    freq = np.exp(-np.log(10000.0) * i / half)             # 10000^(-i/half)
-    theta = np.asarray(pos, dtype=np.float64)[..., None] * freq
-    c, s = np.cos(theta), np.sin(theta)
-    lo, hi = x[..., :half], x[..., half:]
-    y = np.empty_like(x)
-    y[..., :half] = lo * c - hi * s
-    y[..., half:] = hi * c + lo * s
-    return y
+    angle = np.asarray(pos, dtype=np.float64)[..., None] * np.power(10000.0, -np.arange(half) / half)
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * angle)
+    return np.concatenate([z.real, z.imag], axis=-1)
 
 
 def _e4m3_table() -> np.ndarray:

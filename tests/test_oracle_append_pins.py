@@ -1,8 +1,8 @@
 """Pins of the cache-append oracle (oracle/append.py) against what the pages
 and the mathematics fix, not against itself:
 
-  * RoPE: identity at position 0; the complex-number form of a rotation by
-    pos * 10000^(-i/half) (an independent formula); the relative-position
+  * RoPE: identity at position 0; the real 2 x 2 rotation matrix of each pair
+    at angle pos / 10000^(i/half) (an independent form); the relative-position
     property <R_m q, R_n k> = <q, R_{n-m} k> that "DeepSeek-MLA-Principle"
     sec. 3 (why RoPE) states; composition of rotations; hand-computed values
     that fix the frequency schedule;
@@ -26,19 +26,21 @@ def test_rope_identity_at_position_zero():
 
 
 @pytest.mark.parametrize("d", [2, 8, 64])
-def test_rope_is_complex_rotation(d):
-    """Pair (x_i, x_{i+half}) as the complex number x_i + j x_{i+half}, multiplied
-    by exp(j pos 10000^(-i/half))."""
+def test_rope_is_a_plane_rotation_per_pair(d):
+    """Each pair (x_i, x_{i+half}) is multiplied by the 2 x 2 rotation matrix
+    [[cos a, -sin a], [sin a, cos a]] with a = pos * base^(-i/half), the angle
+    taken as pos / base^(i/half) (and the frequencies from math, not numpy)."""
     rng = np.random.default_rng(d)
     x = rng.standard_normal((3, d))
     half = d // 2
     for pos in (1, 7, 4095, 131071):
-        z = x[:, :half] + 1j * x[:, half:]
-        w = np.exp(1j * pos * np.power(10000.0, -np.arange(half) / half))
-        zr = z * w
         y = A.rope(x, pos)
-        np.testing.assert_allclose(y[:, :half], zr.real, rtol=0, atol=1e-9)
-        np.testing.assert_allclose(y[:, half:], zr.imag, rtol=0, atol=1e-9)
+        for i in range(half):
+            a = pos / (10000.0 ** (i / half))
+            rot = np.array([[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]])
+            pair = rot @ np.stack([x[:, i], x[:, i + half]])
+            np.testing.assert_allclose(y[:, i], pair[0], rtol=0, atol=1e-9)
+            np.testing.assert_allclose(y[:, i + half], pair[1], rtol=0, atol=1e-9)
 
 
 def test_rope_relative_position_property():
@@ -131,3 +133,55 @@ def test_expand_is_decoded_code_times_scale():
     got = A.expand_e4m3(codes, np.array([sc], np.float32))
     ref = (torch.from_numpy(codes[0].copy()).view(torch.float8_e4m3fn).float() * torch.tensor(0.3)).bfloat16()
     assert np.array_equal(got[0], ref.view(torch.int16).numpy().view(np.uint16))
+
+
+def _round_sig(x, bits):
+    """x (float64, normal range or 0) rounded to `bits` significant bits, ties to
+    even: frexp gives x = m * 2^e with 0.5 <= |m| < 1, so m * 2^bits is exact and
+    rint rounds it to the nearest integer, halves to even."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.rint(m * 2.0 ** bits), e - bits)
+
+
+def _bf16_bits_value(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_expand_rounds_the_fp32_product_to_bf16():
+    """Expansion = the code's value times the scale as one fp32 product (24
+    significant bits), then bf16 (8 significant bits), each nearest-even, written
+    here from the two formats' significand widths.  The case list includes
+    products for which rounding the exact product straight to bf16 gives another
+    value (the fp32 product lands exactly on a bf16 midpoint), so a single
+    rounding would fail this pin."""
+    rng = np.random.default_rng(31)
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                           # no NaN codes
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    # random scales that are not powers of two
+    scales = (rng.uniform(1e-3, 8.0, size=400)).astype(np.float32)
+    scales = scales[np.frexp(scales.astype(np.float64))[0] != 0.5]
+    # constructed scales: v * s exact lies just above a bf16 midpoint that is an fp32 value
+    built = []
+    for v in (1.125, 1.375, 1.625, 1.875, 3.0, 5.0, 7.0, 0.4375, 13.0):
+        for mant in range(128, 256, 2):                           # even bf16 significands
+            mid = (mant + 0.5) * 2.0 ** -7                        # midpoint above it, in [1, 2)
+            s0 = np.float32(mid / v)
+            for k in range(-4, 5):
+                s = np.nextafter(s0, np.float32(np.inf) if k > 0 else np.float32(0), dtype=np.float32)
+                for _ in range(abs(k) - 1):
+                    s = np.nextafter(s, np.float32(np.inf) if k > 0 else np.float32(0), dtype=np.float32)
+                s = s0 if k == 0 else s
+                p = v * float(s)                                  # exact: 4 x 24 bits
+                if _round_sig(p, 24) == mid and p != mid:
+                    built.append(s)
+    built = np.unique(np.array(built, dtype=np.float32))
+    assert built.size >= 50
+    all_scales = np.concatenate([scales, built])
+    got = A.expand_e4m3(np.broadcast_to(codes, (all_scales.size, codes.size)).copy(), all_scales)
+    exact = vals[None, :] * all_scales.astype(np.float64)[:, None]   # exact products
+    ref = _round_sig(_round_sig(exact, 24), 8)
+    assert np.array_equal(_bf16_bits_value(got), ref)
+    # the constructed cases tell the two roundings apart
+    once = _round_sig(exact, 8)
+    assert int((once != ref).sum()) >= 50

@@ -356,6 +356,89 @@ def test_merge_ignores_empty_split_payload():
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
 
 
+def _range_reference(case, begin, end):
+    """Split partials over explicit page ranges by brute force: for each row and
+    split, the visible positions t with begin*64 <= t < end*64, scores from a
+    numpy absorbed query, a direct softmax; lse = -inf for an empty range."""
+    wl = case.wl
+    c = O.cache_values(case)
+    r = O.decode_values(case.k_pe)
+    qa = np.einsum("bshd,hdm->bshm", O.decode_values(case.q_nope), O.decode_values(case.W_UK))
+    qr = O.decode_values(case.q_rope)
+    bt = case.block_table.numpy()
+    S = begin.shape[1]
+    o = np.full((wl.B, wl.Sq, wl.H, S, wl.d_c), np.nan)
+    lse = np.full((wl.B, wl.Sq, wl.H, S), -np.inf)
+    for b in range(wl.B):
+        L = int(case.seq_lens[b])
+        for s in range(wl.Sq):
+            n = L - wl.Sq + 1 + s
+            for cc in range(S):
+                ts = [t for t in range(int(begin[b, cc]) * I.PAGE, int(end[b, cc]) * I.PAGE) if t < n]
+                if not ts:
+                    continue
+                rows_c = np.stack([c[bt[b, t // I.PAGE], t % I.PAGE] for t in ts])
+                rows_r = np.stack([r[bt[b, t // I.PAGE], t % I.PAGE] for t in ts])
+                for h in range(wl.H):
+                    z = (rows_c @ qa[b, s, h] + rows_r @ qr[b, s, h]) * wl.scale
+                    m = z.max()
+                    e = np.exp(z - m)
+                    lse[b, s, h, cc] = m + math.log(e.sum())
+                    o[b, s, h, cc] = (e / e.sum()) @ rows_c
+    return o, lse
+
+
+def test_page_range_partials_brute_force():
+    """Explicit page ranges per (sequence, split), each sequence its own plan: one
+    page, empty (begin = end), reversed (begin > end), several pages, a last page
+    that is partly past the sequence end, a range past the last page, and the
+    causal rule cutting into a range (Sq = 2)."""
+    wl = small(B=3, Sq=2, H=2, d_h=4, d_c=8, d_r=4, paging="permuted", seed=21)
+    case = I.make_case(wl, seq_lens=[300, 130, 65])       # 5, 3 and 2 pages
+    D = O.dims_of(case)
+    begin = np.array([[0, 1, 1, 4], [2, 0, 3, 2], [1, 0, 1, 0]], dtype=np.int32)
+    end = np.array([[1, 1, 4, 5], [3, 2, 4, 1], [2, 1, 1, 2]], dtype=np.int32)
+    q_abs = torch.from_numpy(O.absorb_q(D, case.q_nope, case.W_UK))
+    o, lse = O.decode_page_ranges(D, q_abs, case.q_rope, case.c_kv, None, case.k_pe,
+                                  case.block_table, case.seq_lens, begin, end)
+    o_ref, lse_ref = _range_reference(case, begin, end)
+    empty = lse_ref == -np.inf
+    assert np.array_equal(lse == -np.inf, empty)
+    np.testing.assert_allclose(lse[~empty], lse_ref[~empty], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o[~empty], o_ref[~empty], rtol=1e-11, atol=1e-12)
+    # the cases the plan was built to hold
+    assert np.all(empty[0, :, :, 1]) and np.all(empty[1, :, :, 3])      # begin = end, begin > end
+    assert np.all(empty[1, :, :, 2])                                     # past the last page
+    # sequence 2 (65 tokens) split [1, 2) holds position 64 only, which row 0 (sees 64) misses
+    assert np.all(empty[2, 0, :, 0]) and not np.any(empty[2, 1, :, 0])
+
+
+def test_page_ranges_equal_fixed_splits_and_merge_to_full_softmax():
+    """Ranges equal to the fixed plan give the fixed plan's partials bit for bit;
+    per-sequence ranges that cover each sequence's pages merge to the unsplit result."""
+    wl = small(B=3, Sq=2, H=2, d_h=4, d_c=8, d_r=4, paging="permuted", seed=22)
+    case = I.make_case(wl, seq_lens=[300, 1, 129])
+    D = O.dims_of(case)
+    q_abs = torch.from_numpy(O.absorb_q(D, case.q_nope, case.W_UK))
+    sp, S = 2, 3
+    pages = [(int(n) + I.PAGE - 1) // I.PAGE for n in case.seq_lens]
+    begin = np.array([[c * sp for c in range(S)] for _ in pages], dtype=np.int32)
+    end = np.array([[min((c + 1) * sp, P) for c in range(S)] for P in pages], dtype=np.int32)
+    args = (D, q_abs, case.q_rope, case.c_kv, None, case.k_pe, case.block_table, case.seq_lens)
+    o1, l1 = O.decode_page_ranges(*args, begin, end)
+    o2, l2 = O.decode_splitkv(*args, S, sp)
+    live = l2 != -np.inf
+    assert np.array_equal(l1, l2) and np.array_equal(o1[live], o2[live])
+    # a different cut per sequence (sequence 0: 1 + 4 pages, sequence 2: 0 + 3, empty first)
+    begin = np.array([[0, 1], [0, 1], [0, 0]], dtype=np.int32)
+    end = np.array([[1, 5], [1, 1], [0, 3]], dtype=np.int32)
+    o3, l3 = O.decode_page_ranges(*args, begin, end)
+    ol, lse = O.combine_lse(D, o3, l3)
+    _, ol_ref, lse_ref = O.decode(case)
+    np.testing.assert_allclose(ol, ol_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-13, atol=1e-13)
+
+
 def test_absorb_and_up_projection_against_einsum():
     """Key absorption contracts d_h; the up-projection contracts d_c (weight layout
     [n_heads, d_head, d_latent])."""
