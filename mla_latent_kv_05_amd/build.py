@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["mla_api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
-           "kernels_decode8.hip", "kernels_append.hip", "kernels_prefill.hip", "kernels_expand.hip"]
+           "kernels_decode8.hip", "kernels_decode128.hip", "kernels_append.hip", "kernels_prefill.hip", "kernels_expand.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -124,7 +124,7 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     // on the MFMA path (one per (row, split) on the generic path)
     const bool mfma = mla::decode_mfma_supported(*p);
     const int64_t rows = (int64_t)p->Sq * p->H;
-    const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::kDecodeRowsPerBlock) : rows;
+    const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::decode_rows_per_workgroup(*p)) : rows;
     int64_t P = std::max<int64_t>(1, num_cus / wg_per_part);
     if (!mfma) P = std::max<int64_t>(1, 2ll * num_cus / wg_per_part);
     // at least 8 parts even when that takes several rounds of workgroups (many query
@@ -176,9 +176,13 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
     const int64_t rows = (int64_t)p->B * p->Sq * p->H;
     const int64_t parts = p->num_parts > 0 ? p->num_parts : (int64_t)p->B * p->num_splits;
     const int64_t grid = mla::decode_mfma_supported(*p)
-                             ? (parts + 7) / 8 * 8 * (rows / p->B / mla::kDecodeRowsPerBlock)
+                             ? (parts + 7) / 8 * 8 * (rows / p->B / mla::decode_rows_per_workgroup(*p))
                              : rows * p->num_splits;
     if (grid > 0x7fffffffll) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: grid of %lld workgroups too large", (long long)grid);
+    if (mla::decode128_supported(*p))
+        return hip_status(mla::launch_decode128(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
+                                                lse_part, st),
+                          "mla_decode_splitkv launch");
     if (mla::decode8_supported(*p))
         return hip_status(mla::launch_decode8(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
                                               lse_part, st),

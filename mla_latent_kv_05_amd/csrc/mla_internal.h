@@ -67,7 +67,16 @@ hipError_t launch_prefill_attention(const mla_params_t &p, const void *q_nope, c
                                     const int32_t *block_table, const int32_t *seq_lens, void *out,
                                     hipStream_t stream);
 
-// Heads x query rows handled by one attention workgroup of the MFMA kernel.
+// Heads x query rows handled by one attention workgroup of the e4m3 kernel
+// (kernels_decode.hip) and of the eight-wave bf16 kernel (kernels_decode8.hip).
 constexpr int kDecodeRowsPerBlock = 64;
+// ... of the four-wave bf16 kernel (kernels_decode128.hip).
+constexpr int kDecodeRowsPerGroup = 128;
+bool decode128_supported(const mla_params_t &p);
+hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
+                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                            float *lse_part, hipStream_t stream);
+// query rows per attention workgroup for the kernel mla_decode_splitkv picks
+int decode_rows_per_workgroup(const mla_params_t &p);
 
 }  // namespace mla

@@ -200,7 +200,7 @@ def test_balanced_plan(B, lo, hi, Sq, min_splits, seed):
     q = mla.plan_splits(p, int(lens.max()), int(lens.sum()), num_cus=256, min_splits=min_splits)
     assert status_of(q) == 0
     assert q.num_parts >= 1
-    n_rg = Sq * 128 // 64                           # workgroups per part
+    n_rg = Sq * 128 // 128                          # workgroups per part (128 query rows each)
     assert q.num_parts * n_rg <= 256 or q.num_parts <= min_splits
     assert max(1, int(touched_parts(lens, q.num_parts).max())) <= q.num_splits
     beg, end = split_page_ranges(lens, q)          # asserts the slot bound as it goes
