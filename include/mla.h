@@ -78,17 +78,20 @@ typedef enum {
  *               sequence b covers its pages [c*split_pages, (c+1)*split_pages).
  *               Requires num_splits * split_pages >= max_pages.
  *   num_parts   0 for fixed splits; P >= 1 for balanced splits, which give
- *               every part of the work the same number of pages whatever the
- *               length mix.  With n_b = ceil(seq_lens[b] / 64) pages for
- *               sequence b, off_b = n_0 + ... + n_{b-1} and T = sum_b n_b, the
- *               batch's pages taken in order are cut into P parts, part j
- *               holding pages [floor(j*T/P), floor((j+1)*T/P)).  Split c of
- *               sequence b is its pages in part j0(b) + c, where j0(b) is the
- *               part holding its first page (a sequence touches one part per
- *               split, consecutively).  split_pages is ignored.  Requires
- *               num_splits >= the largest number of parts any sequence touches,
- *               which mla_plan_splits guarantees; a split index at or past
- *               num_splits is not computed.
+ *               every part the same amount of work whatever the length mix.
+ *               Work is counted in units: sequence b with n_b = ceil(seq_lens[b]
+ *               / 64) > 0 pages costs u_b = 6 + n_b units (a start cost of 6,
+ *               for its query loads, first copies and partial output, then one
+ *               unit per page); an empty sequence costs 0.  With U = sum_b u_b and
+ *               off_b = u_0 + ... + u_{b-1}, the batch's units taken in order are
+ *               cut into P parts, part j holding units [floor(j*U/P),
+ *               floor((j+1)*U/P)); page i of sequence b is unit off_b + 6 + i.
+ *               Split c of sequence b is its pages in part j0(b) + c, where j0(b)
+ *               is the part holding its first page (a sequence's pages lie in
+ *               consecutive parts, one split each).  split_pages is ignored.
+ *               Requires num_splits >= the largest number of parts holding pages
+ *               of one sequence, which mla_plan_splits guarantees; a split index
+ *               at or past num_splits is not computed.
  *   scale       softmax scale, 1/sqrt(d_h + d_r) ("DeepSeek-MLA-Principle"
  *               sec. 2; the decode module's self.scale)
  *   q_dtype     q_nope, q_rope            F32 | BF16

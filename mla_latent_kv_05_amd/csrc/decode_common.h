@@ -175,26 +175,28 @@ __device__ __forceinline__ void for_each_segment(const mla_params_t &p, const in
         else fill(b, c, c + 1);
         return;
     }
+    auto cost = [](int pages) { return pages > 0 ? pages + kSeqStartCost : 0; };
     const int64_t P = p.num_parts;
-    int64_t T = 0;                                     // pages of the whole batch
+    int64_t T = 0;                                     // units of the whole batch
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
-        T += wave_sum(b < p.B ? (seq_lens[b] + kPage - 1) / kPage : 0);
+        T += wave_sum(b < p.B ? cost((seq_lens[b] + kPage - 1) / kPage) : 0);
     }
-    const int64_t pg0 = part * T / P, pg1 = (part + 1) * T / P;   // this part's flattened pages
-    int64_t base = 0;                                  // flattened index of sequence b0's first page
+    const int64_t pg0 = part * T / P, pg1 = (part + 1) * T / P;   // this part's units
+    int64_t base = 0;                                  // units before sequence b0
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
         const int pages = b < p.B ? (seq_lens[b] + kPage - 1) / kPage : 0;
-        const int incl = wave_inclusive_scan(pages);
+        const int units = cost(pages);
+        const int incl = wave_inclusive_scan(units);
         const int chunk = __builtin_amdgcn_readlane(incl, 63);
         if (base > pg1) break;                         // every later sequence starts past this part
         if (base + chunk >= pg0) {
-            const int64_t off = base + incl - pages;
-            // sequences with pages that intersect the part; empty sequences are
-            // owned by the part whose range holds their position (the last part
-            // owns those at the very end)
-            const bool mine = b < p.B && (pages > 0 ? (off < pg1 && off + pages > pg0)
+            const int64_t off = base + incl - units;   // the sequence's first unit
+            const int64_t first = off + kSeqStartCost; // ... and the unit of its first page
+            // sequences with pages in the part; empty sequences are owned by the part
+            // whose range holds their position (the last part owns those at the very end)
+            const bool mine = b < p.B && (pages > 0 ? (first < pg1 && first + pages > pg0)
                                                     : ((off >= pg0 && off < pg1) || (part == P - 1 && off >= T)));
             uint64_t m = __builtin_amdgcn_ballot_w64(mine);
             while (m) {
@@ -202,16 +204,17 @@ __device__ __forceinline__ void for_each_segment(const mla_params_t &p, const in
                 m &= m - 1;
                 const int bb = b0 + k;
                 const int pg_b = __builtin_amdgcn_readlane(pages, k);
-                const int64_t off_b = base + __builtin_amdgcn_readlane(incl, k) - pg_b;
+                const int64_t off_b = base + __builtin_amdgcn_readlane(incl, k) - cost(pg_b);
                 if (pg_b == 0) {
                     fill(bb, 0, p.num_splits);
                     continue;
                 }
-                const int64_t j0 = ((off_b + 1) * P - 1) / T;          // part holding the first page
-                const int64_t jl = ((off_b + pg_b) * P - 1) / T;       // part holding the last page
+                const int64_t f_b = off_b + kSeqStartCost;
+                const int64_t j0 = ((f_b + 1) * P - 1) / T;             // part holding the first page
+                const int64_t jl = ((f_b + pg_b) * P - 1) / T;          // part holding the last page
                 const int c = static_cast<int>(part - j0);
-                const int pa = static_cast<int>(max<int64_t>(pg0 - off_b, 0));
-                const int pb = static_cast<int>(min<int64_t>(pg1 - off_b, pg_b));
+                const int pa = static_cast<int>(max<int64_t>(pg0 - f_b, 0));
+                const int pb = static_cast<int>(min<int64_t>(pg1 - f_b, pg_b));
                 f(Segment{bb, c, pa, pb, part == jl});
             }
         }

@@ -54,9 +54,10 @@ __device__ __forceinline__ int64_t block_reduce_sum_i64(int64_t v, int64_t *red)
 
 // Pages [*pa, *pb) of sequence b that split c covers (empty when *pa >= *pb).
 // Fixed splits: [c*split_pages, (c+1)*split_pages).  Balanced splits: the
-// batch's pages in sequence order are cut into num_parts parts, part j holding
-// flattened pages [floor(j*T/P), floor((j+1)*T/P)); split c of b is its pages
-// in part j0 + c, j0 being the part that holds b's first page.
+// batch's work units (kSeqStartCost + n for a sequence of n > 0 pages, start cost
+// first) in sequence order are cut into num_parts parts, part j holding units
+// [floor(j*T/P), floor((j+1)*T/P)); split c of b is its pages in part j0 + c, j0
+// being the part that holds b's first page.
 __device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict__ seq_lens, int b, int c,
                                int64_t *pa, int64_t *pb, int64_t *red) {
     const int64_t pages = (seq_lens[b] + p.page_size - 1) / p.page_size;
@@ -69,11 +70,12 @@ __device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict_
     int64_t tot = 0, before = 0;
     for (int i = threadIdx.x; i < p.B; i += kThreads) {
         const int64_t n = (seq_lens[i] + p.page_size - 1) / p.page_size;
-        tot += n;
-        if (i < b) before += n;
+        const int64_t units = n > 0 ? n + kSeqStartCost : 0;
+        tot += units;
+        if (i < b) before += units;
     }
     const int64_t T = block_reduce_sum_i64(tot, red);
-    const int64_t off = block_reduce_sum_i64(before, red);
+    const int64_t off = block_reduce_sum_i64(before, red) + kSeqStartCost;   // unit of b's first page
     *pa = 0;
     *pb = 0;
     if (pages == 0) return;

@@ -76,6 +76,12 @@ bool decode128_supported(const mla_params_t &p);
 hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
                             const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
                             float *lse_part, hipStream_t stream);
+// Balanced parts are cut in units of work: a sequence with n > 0 pages costs
+// kSeqStartCost + n units, its start cost first, then one unit per page; an empty
+// sequence costs nothing.  The batch's units, taken in sequence order, are cut into
+// num_parts equal parts, so a part that also starts a sequence (one more segment:
+// its query loads, its first copies and its partial output) streams fewer pages.
+constexpr int kSeqStartCost = 6;
 // query rows per attention workgroup for the kernel mla_decode_splitkv picks
 int decode_rows_per_workgroup(const mla_params_t &p);
 

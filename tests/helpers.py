@@ -51,13 +51,19 @@ def assert_bf16_rounding(got, ref, acc_rel=1e-3):
         f"{float(np.max(np.abs(got - ref) - bound)):.3e}"
 
 
+# start cost of a sequence in the balanced plan's work units (the C header's num_parts)
+SEQ_START_COST = 6
+
+
 def split_page_ranges(seq_lens, p: mla.Params):
     """Pages [begin, end) of sequence b that split slot c covers under p's split plan,
     as two [B, num_splits] int32 arrays (end <= begin: empty).  Written from the
     plan's definition in the C header, independently of the kernels: fixed splits
-    cover [c*split_pages, (c+1)*split_pages); balanced splits cut the batch's pages,
-    taken in sequence order, into num_parts parts at floor(j*T/P), and slot c of
-    sequence b is its share of the (c+1)-th part it touches."""
+    cover [c*split_pages, (c+1)*split_pages); balanced splits give a sequence of
+    n > 0 pages SEQ_START_COST + n work units (start cost first, then one per page),
+    cut the batch's units, taken in sequence order, into num_parts parts at
+    floor(j*U/P), and slot c of sequence b is its share of the pages of the (c+1)-th
+    part that holds any of them."""
     lens = np.asarray(seq_lens, dtype=np.int64)
     n = (lens + 63) // 64
     B, S = len(lens), p.num_splits
@@ -69,20 +75,22 @@ def split_page_ranges(seq_lens, p: mla.Params):
                 beg[b, c] = c * p.split_pages
                 end[b, c] = min((c + 1) * p.split_pages, n[b])
         return beg.astype(np.int32), np.maximum(end, beg).astype(np.int32)
-    P, T = p.num_parts, int(n.sum())
-    starts = [j * T // P for j in range(P + 1)]
+    cost = np.where(n > 0, n + SEQ_START_COST, 0)
+    P, U = p.num_parts, int(cost.sum())
+    starts = [j * U // P for j in range(P + 1)]
     off = 0
     for b in range(B):
         if n[b] > 0:
+            first = off + SEQ_START_COST           # unit of the sequence's first page
             # the parts holding the sequence's first and last pages
-            j0 = bisect.bisect_right(starts[:P], off) - 1
-            jl = bisect.bisect_right(starts[:P], off + n[b] - 1) - 1
+            j0 = bisect.bisect_right(starts[:P], first) - 1
+            jl = bisect.bisect_right(starts[:P], first + n[b] - 1) - 1
             for j in range(j0, jl + 1):
                 c = j - j0
                 assert c < S, f"sequence {b} touches more than num_splits={S} parts"
-                beg[b, c] = max(starts[j] - off, 0)
-                end[b, c] = min(starts[j + 1] - off, n[b])
-        off += n[b]
+                beg[b, c] = max(starts[j] - first, 0)
+                end[b, c] = min(starts[j + 1] - first, n[b])
+        off += cost[b]
     return beg.astype(np.int32), np.maximum(end, beg).astype(np.int32)
 
 
@@ -145,14 +153,16 @@ def sample_rows(case: I.Case, n_seq: int, heads_per_seq: int, seed: int = 0) -> 
 
 
 def touched_parts(seq_lens, num_parts: int) -> np.ndarray:
-    """Number of balanced-split parts each sequence touches (0 for an empty one)."""
+    """Number of balanced-split parts holding pages of each sequence (0 for an empty one)."""
     lens = np.asarray(seq_lens, dtype=np.int64)
     n = (lens + 63) // 64
-    T, P = int(n.sum()), num_parts
-    starts = [j * T // P for j in range(P)]
-    off = np.concatenate([[0], np.cumsum(n)[:-1]])
+    cost = np.where(n > 0, n + SEQ_START_COST, 0)
+    U, P = int(cost.sum()), num_parts
+    starts = [j * U // P for j in range(P)]
+    off = np.concatenate([[0], np.cumsum(cost)[:-1]])
     out = np.zeros(len(n), np.int64)
     for b in range(len(n)):
         if n[b]:
-            out[b] = (bisect.bisect_right(starts, off[b] + n[b] - 1) - bisect.bisect_right(starts, off[b])) + 1
+            first = off[b] + SEQ_START_COST
+            out[b] = (bisect.bisect_right(starts, first + n[b] - 1) - bisect.bisect_right(starts, first)) + 1
     return out

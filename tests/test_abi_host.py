@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from mla_latent_kv_05_amd import mla
-from tests.helpers import split_page_ranges, touched_parts
+from tests.helpers import SEQ_START_COST, split_page_ranges, touched_parts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -213,9 +213,11 @@ def test_balanced_plan(B, lo, hi, Sq, min_splits, seed):
                 assert beg[b, c] == covered, "splits of a sequence must tile its pages in order"
                 covered = int(end[b, c])
         assert covered == n[b]
-    parts = [(j + 1) * T // q.num_parts - j * T // q.num_parts for j in range(q.num_parts)]
+    # the parts are equal in work units (pages plus a start cost per sequence)
+    U = int(np.where(n > 0, n + SEQ_START_COST, 0).sum())
+    parts = [(j + 1) * U // q.num_parts - j * U // q.num_parts for j in range(q.num_parts)]
     assert max(parts) - min(parts) <= 1
-    if T >= 8:
+    if U >= 8:
         assert min(parts) >= 1
     if min_splits > 1:
         assert (touched_parts(lens, q.num_parts) >= min_splits).all()
