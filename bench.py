@@ -7,16 +7,24 @@ the same output) is timed as well, and `value` is the faster of the two.  Defaul
 DeepSeek-V3 head shapes (H=128, d_h=128, d_c=512, d_r=64), bf16, pages of 64
 tokens in a randomly permuted block table, Sq=1.
 
-The inputs are replicated R times in HBM and the steps rotate over the
-replicas, so the 256 MB last-level cache cannot serve one step from the
-previous one.
+The inputs are replicated in HBM (by default enough replicas to hold at least
+1 GiB, at least 4) and the steps rotate over the replicas, so the 256 MB
+last-level cache cannot serve one step from the previous one.
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by a synchronize
-and one event pair on each side, then the same K steps again with an event pair
-around each attention launch, which gives that kernel's average launch duration
-for the roofline object.  After a synchronize the GPU takes some tens of steps
-to return to its sustained step rate; the default K = 1000 (~0.15 s) keeps that
-to a few percent of the timed region.
+Timing, in this order:
+  1. the step with the fused tail: max(W, STEP_WARMUP) untimed warm-up steps,
+     then exactly K timed steps bracketed by a synchronize and events (events
+     only at block boundaries);
+  2. the same for the four-call step;
+  3. the attention kernel alone (the roofline object): a fixed warm-up of
+     KERNEL_WARMUP launches, then max(KERNEL_LAUNCHES, K) launches back to back
+     on the launch stream inside one event pair, whatever --steps is.
+The GPU reaches its sustained step rate only after some hundreds of steps of
+load (measured at 64 x 4,096 positions: 5 warm-up steps then 20 timed ones read
+~10% slower than after 300 more), so each route gets at least STEP_WARMUP
+warm-up steps whatever W is; the JSON gives W and the warm-up steps run.
+The oracle leg (cpu_baseline) also compares the step's output for the sequences
+it computed with the GPU step's output (max and RMS error over the output RMS).
 
 Prints one JSON line.  value = latent-cache TB/s = (tokens x 1152 B) / step time.
 """
@@ -34,6 +42,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 STEP_BLOCK = 50                # steps per block of the step-time spread
+STEP_WARMUP = 300              # warm-up steps of each route at least (more when W is larger)
+KERNEL_WARMUP = 300            # untimed attention launches before the kernel leg
+KERNEL_LAUNCHES = 600          # timed attention launches (at least; more when K is larger)
+REPLICA_BYTES = 1 << 30        # inputs replicated until the replicas hold this many bytes
 
 
 def pct(xs):
@@ -44,22 +56,19 @@ def pct(xs):
 
 # rocprofv3 counter summary of the attention kernel on this workload (FETCH_SIZE /
 # WRITE_SIZE in KiB per dispatch) and the hash of the kernel source it was taken on
-COUNTERS = os.path.join(ROOT, "profiles", "decode8_bf16_v3_b64_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "decode128_bf16_v3_b64_counters.txt")
 # the sources of the attention kernel the counters were taken on
 KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc", f)
-               for f in ("kernels_decode8.hip", "decode_common.h", "gfx950.h")]
+               for f in ("kernels_decode128.hip", "decode_common.h", "gfx950.h", "mla_internal.h")]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # after the synchronize that opens the timed region the first ~50 steps run up to
-    # 20% slower while the GPU returns to its sustained clocks: the default timed
-    # region (~0.15 s) keeps that start-up to a few percent of it
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="v3_b64")
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=10)
@@ -99,6 +108,9 @@ def main():
 
     names = ("q_nope", "q_rope", "c_kv", "k_pe", "kv_scale", "block_table", "seq_lens", "W_UK", "W_UV")
     base = {k: (None if getattr(case, k) is None else getattr(case, k).to(dev)) for k in names}
+    rep_bytes = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    if args.replicas < 1:
+        args.replicas = max(4, min(256, -(-REPLICA_BYTES // rep_bytes)))
     reps = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
                      for _ in range(args.replicas - 1)]
     step = mla.DecodeStep(p, device=dev)
@@ -109,68 +121,71 @@ def main():
     bound = [step.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                        t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
 
-    def run(r, ev=None):
+    def run(r):
         b = bound[r]
         b.absorb_q()
-        if ev is not None:
-            ev[0].record(stream)
         b.decode_splitkv()
-        if ev is not None:
-            ev[1].record(stream)
         b.combine_lse()
         b.up_v()
 
-    for i in range(args.warmup):
-        run(i % args.replicas)
-    torch.cuda.synchronize()
-    assert torch.isfinite(step.out).all(), "non-finite output"
+    # the step with the fused tail (merge + up-projection in one launch): same output
+    step_f = mla.DecodeStep(p, device=dev, fused=True)
+    bound_f = [step_f.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
+                           t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
+    n_warm = max(args.warmup, STEP_WARMUP)
 
-    # the timed steps: events around the whole loop only (an event pair inside each
-    # step adds several microseconds of stream gaps to it)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # 1. the fused step: warm-up steps, then exactly K timed steps bracketed by a
+    # synchronize and events; an event at every block boundary (one per STEP_BLOCK
+    # steps) gives the spread of the per-step time without gaps inside the steps
+    for i in range(n_warm):
+        bound_f[i % args.replicas]()
+    torch.cuda.synchronize()
+    assert torch.isfinite(step_f.out).all(), "non-finite output"
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-args.steps // STEP_BLOCK) + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    marks[0].record(stream)
+    for i in range(args.steps):
+        bound_f[i % args.replicas]()
+        if (i + 1) % STEP_BLOCK == 0 or i + 1 == args.steps:
+            marks[-(-(i + 1) // STEP_BLOCK)].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_fused = marks[0].elapsed_time(marks[-1]) / args.steps
+    blk_us = [marks[k].elapsed_time(marks[k + 1]) * 1e3 / min(STEP_BLOCK, args.steps - k * STEP_BLOCK)
+              for k in range(len(marks) - 1)]
+
+    # 2. the four-call step, the same way (events around the whole loop only)
+    for i in range(n_warm):
+        run(i % args.replicas)
+    torch.cuda.synchronize()
+    assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
         run(i % args.replicas)
     t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    # the attention launch's own duration: the same steps again, with an event pair
-    # around each attention launch on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        run(i % args.replicas, evs[i])
-    torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = float(np.mean(dec_ms))
 
-    # the same step with the fused tail (merge + up-projection in one launch)
-    step_f = mla.DecodeStep(p, device=dev, fused=True)
-    bound_f = [step_f.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
-                           t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
-    for i in range(args.warmup):
-        bound_f[i % args.replicas]()
+    # 3. the attention kernel alone: fixed warm-up, then back-to-back launches inside
+    # one event pair on the launch stream (no per-launch events, whose stream gaps
+    # would be timed too); events at block boundaries give the spread
+    n_dec = max(KERNEL_LAUNCHES, args.steps)
+    for i in range(KERNEL_WARMUP):
+        bound[i % args.replicas].decode_splitkv()
+    kmarks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-n_dec // STEP_BLOCK) + 1)]
     torch.cuda.synchronize()
-    # an event at every block boundary (one per STEP_BLOCK steps) gives the spread of
-    # the per-step time over the region without gaps inside the steps
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps // STEP_BLOCK + 2)]
-    nm = 0
-    marks[nm].record(stream)
-    nm += 1
-    for i in range(args.steps):
-        bound_f[i % args.replicas]()
-        if (i + 1) % STEP_BLOCK == 0 or i + 1 == args.steps:
-            marks[nm].record(stream)
-            nm += 1
+    kmarks[0].record(stream)
+    for i in range(n_dec):
+        bound[i % args.replicas].decode_splitkv()
+        if (i + 1) % STEP_BLOCK == 0 or i + 1 == n_dec:
+            kmarks[-(-(i + 1) // STEP_BLOCK)].record(stream)
     torch.cuda.synchronize()
-    ms_fused = marks[0].elapsed_time(marks[nm - 1]) / args.steps
-    blk_us = [marks[k].elapsed_time(marks[k + 1]) * 1e3 / min(STEP_BLOCK, args.steps - (k * STEP_BLOCK))
-              for k in range(nm - 1)]
-    assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
+    dec_avg_ms = kmarks[0].elapsed_time(kmarks[-1]) / n_dec
+    dec_blk_us = [kmarks[k].elapsed_time(kmarks[k + 1]) * 1e3 / min(STEP_BLOCK, n_dec - k * STEP_BLOCK)
+                  for k in range(len(kmarks) - 1)]
 
     # e4m3 cache: also the route that expands the cache to bf16 first (for a step
     # bound by the matrix cores); same result within the e4m3 bound
@@ -179,7 +194,7 @@ def main():
         step_e = mla.DecodeStep(p, device=dev, fused=True, expand=True)
         bound_e = [step_e.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                                t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
-        for i in range(args.warmup):
+        for i in range(n_warm):
             bound_e[i % args.replicas]()
         torch.cuda.synchronize()
         x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -198,6 +213,8 @@ def main():
     ms_step = min(ms_step, ms_fused)               # the headline step: the fastest route (same result)
     if ms_expand is not None:
         ms_step = min(ms_step, ms_expand)
+    assert dec_avg_ms <= ms_step, (f"attention launch {dec_avg_ms * 1e3:.2f} us exceeds the step "
+                                   f"{ms_step * 1e3:.2f} us it is part of")
     tb_s = cost.cache_bytes / (ms_step * 1e-3) / 1e12
     achieved_gbs = cost.decode_bytes / (dec_avg_ms * 1e-3) / 1e9
     roofline_us = max(cost.total_bytes / (HBM_PEAK_GBS * 1e9), cost.flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
@@ -217,9 +234,9 @@ def main():
         for k in ("decompress", "attention", "path"):
             prefill[k]["frac_of_measured_gemm"] = round(prefill[k]["achieved"] / peaks["bf16_gemm_tflops"], 4)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, args.cpu_budget_s)
+        cpu, parity = cpu_baseline(case, args.cpu_budget_s, step_f.out.float().cpu().numpy())
 
     result = {
         "metric": "MLA absorbed decode µs/step + latent-cache TB/s at B=64, L=4096, bf16",
@@ -228,6 +245,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "higher_is_better": True,
@@ -252,7 +270,8 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(wl.name),
             "launch_us": round(dec_avg_ms * 1e3, 2),
-            "launch_us_p10_p50_p90": pct([m * 1e3 for m in dec_ms]),
+            "launches_timed": n_dec,
+            "block_us_p10_p50_p90": pct(dec_blk_us), "block_launches": STEP_BLOCK,
             "bytes_per_launch": cost.decode_bytes,
             "mfma_tflops": round(cost.decode_flops / (dec_avg_ms * 1e-3) / 1e12, 1),
             "frac_of_measured_copy": round(achieved_gbs / peaks["hbm_copy_gbs"], 4),
@@ -276,6 +295,7 @@ def main():
         "append": append,
         "prefill": prefill,
         "cpu_baseline": cpu,
+        "parity": parity,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(result), flush=True)
@@ -495,30 +515,41 @@ def code_hash(paths):
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
-def cpu_baseline(case, budget_s):
+def cpu_baseline(case, budget_s, gpu_out):
     """The oracle, untuned, on a bounded sample: whole sequences (every head) until
-    about `budget_s` seconds of CPU work; reported in the metric's unit."""
+    about `budget_s` seconds of CPU work; reported in the metric's unit.  Also the
+    step output of the sampled rows against the GPU step's output `gpu_out`
+    [B, Sq, H, d_h]: max and RMS of the error, each over the oracle output's RMS."""
     import numpy as np
     from oracle import oracle as O
 
     wl = case.wl
     lens = case.seq_lens.numpy()
     order = np.argsort(lens)[len(lens) // 2:]          # median-length and longer first
-    t_used, toks, seqs = 0.0, 0, []
+    t_used, toks, seqs, refs = 0.0, 0, [], []
     for b in order:
         rows = np.arange(b * wl.Sq * wl.H, (b + 1) * wl.Sq * wl.H, dtype=np.int64)
         t0 = time.perf_counter()
-        O.decode(case, rows=rows)
+        out, _, _ = O.decode(case, rows=rows)
         dt = time.perf_counter() - t0
         t_used += dt
         toks += int(lens[b])
         seqs.append(int(b))
+        refs.append(out)
         if t_used + dt > budget_s:
             break
     value = toks * 1152 / t_used / 1e12
-    return {"value": value, "unit": "TB/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{len(seqs)} whole sequences ({toks} tokens, all {wl.H} heads) of the "
-                      f"same workload, fp64 oracle, {t_used:.1f} s"}
+    ref = np.concatenate(refs)
+    got = np.concatenate([gpu_out[b].reshape(-1, wl.d_h) for b in seqs]).astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    tol = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}[wl.dtype]
+    parity = {"rows": int(ref.shape[0]), "sequences": seqs,
+              "max_abs_err_over_rms": float(err.max() / rms), "rms_err_over_rms": float(np.sqrt(np.mean(err ** 2)) / rms),
+              "tol_max_abs_over_rms": tol, "pass": bool(err.max() / rms <= tol)}
+    return ({"value": value, "unit": "TB/s", "cores": O.num_threads(), "kind": "oracle",
+             "sample": f"{len(seqs)} whole sequences ({toks} tokens, all {wl.H} heads) of the "
+                       f"same workload, fp64 oracle, {t_used:.1f} s"}, parity)
 
 
 if __name__ == "__main__":

@@ -65,7 +65,9 @@ typedef enum {
  * Problem description shared by the four calls.
  *
  *   B           sequences in the batch                          >= 1
- *   Sq          new query tokens per sequence (causal among them) 1..16
+ *   Sq          new query tokens per sequence (causal among them) 1..256
+ *               (1..65,536 for mla_append_kv, mla_decompress_kv and
+ *               mla_prefill_attention)
  *   H           attention heads n_h (DeepSeek-V3: 128)           >= 1
  *   d_h         per-head non-RoPE query/key dim = value dim (128)  1..256
  *   d_c         latent dim kv_lora_rank (512)                    1..1024
@@ -342,14 +344,29 @@ mla_status_t mla_check_params(const mla_params_t *p);
 /*
  * Host-only split planner.  Given the longest sequence (tokens), the total
  * tokens of the batch and the number of compute units to fill, chooses
- * balanced splits: sets p->num_parts (one workgroup per compute unit, parts of
- * at least 8 pages, at least `min_splits` parts when the batch has that many
- * pages) and p->num_splits, the bound on the parts one sequence can touch.
- * max_seq_len must not be below, and total_tokens not above, the true values.
+ * balanced splits: sets p->num_parts (P: one attention workgroup per compute
+ * unit, at least 8 parts, parts of at least 4 pages on average, at least
+ * `min_splits` parts when the batch has that many pages) and p->num_splits, the
+ * bound on the parts one sequence can touch.  It extends mla_default_num_splits
+ * (uniform lengths, fixed splits) to any mix of lengths.  max_seq_len must not be
+ * below, and total_tokens not above, the true values; the plan depends on
+ * seq_lens through them, so it must be recomputed whenever a sequence grows past
+ * max_seq_len (a split index at or past num_splits is not computed).
  * Reads B, Sq, H, max_pages, the dtypes and flags.  Returns MLA_OK or an error.
  */
 mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total_tokens,
                              int32_t num_cus, int32_t min_splits);
+
+/*
+ * Host-only default split count for fixed splits (num_parts == 0): the number of
+ * KV chunks per sequence that fills the 256 compute units of an MI355X when all
+ * B sequences hold max_seq_len tokens, i.e. ceil(P / B) for the part count P that
+ * mla_plan_splits picks for that batch, clamped to [1, ceil(max_seq_len / 64)].
+ * Use it with split_pages = ceil(ceil(max_seq_len / 64) / S).  Reads the same
+ * fields as mla_plan_splits.  Returns S >= 1, or -1 (mla_last_error says why) for
+ * a NULL or invalid p or max_seq_len < 1.
+ */
+int32_t mla_default_num_splits(const mla_params_t *p, int32_t max_seq_len);
 
 /* Name of the kernel family mla_decode_splitkv would use for *p:
  * "mfma_bf16", "mfma_fp8" or "generic_f32" (host-only). */

@@ -150,6 +150,25 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     return MLA_OK;
 }
 
+int32_t mla_default_num_splits(const mla_params_t *p, int32_t max_seq_len) {
+    if (!p) {
+        fail(MLA_ERR_NULL, "params is NULL");
+        return -1;
+    }
+    if (max_seq_len < 1) {
+        fail(MLA_ERR_SHAPE, "need max_seq_len >= 1 (got %d)", max_seq_len);
+        return -1;
+    }
+    // the planner's part count for a batch of B sequences of max_seq_len tokens each,
+    // on the 256 compute units of an MI355X; equal sequences share it evenly
+    mla_params_t q = *p;
+    if (mla_plan_splits(&q, max_seq_len, (int64_t)p->B * max_seq_len, 256, 1) != MLA_OK) return -1;
+    const int64_t pages = (max_seq_len + 63) / 64;
+    int64_t S = (q.num_parts + p->B - 1) / p->B;
+    S = std::min<int64_t>(std::max<int64_t>(S, 1), std::min<int64_t>(pages, kMaxSplits));
+    return (int32_t)S;
+}
+
 mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void *W_UK, void *q_abs,
                           void *stream) {
     mla_status_t s = check(p);

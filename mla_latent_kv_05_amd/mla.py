@@ -27,7 +27,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
            "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax", "mla_expand_kv",
-           "mla_check_params", "mla_plan_splits", "mla_decode_kernel_name",
+           "mla_check_params", "mla_plan_splits", "mla_default_num_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
 
@@ -98,6 +98,8 @@ def lib():
         L.mla_prefill_lmax.restype = ctypes.c_int64
         L.mla_prefer_absorbed.argtypes = [PP]
         L.mla_prefer_absorbed.restype = ctypes.c_int32
+        L.mla_default_num_splits.argtypes = [PP, ctypes.c_int32]
+        L.mla_default_num_splits.restype = ctypes.c_int32
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = ctypes.c_int32
         if L.mla_abi_version() != 2:
@@ -270,6 +272,15 @@ def prefer_absorbed(p: Params) -> bool:
     if r < 0:
         raise MLAError(2, lib().mla_last_error().decode())
     return bool(r)
+
+
+def default_num_splits(p: Params, max_seq_len: int) -> int:
+    """Fixed-split count per sequence that fills an MI355X for B sequences of
+    max_seq_len tokens (use with split_pages = ceil(ceil(max_seq_len / 64) / S))."""
+    r = lib().mla_default_num_splits(ctypes.byref(p), int(max_seq_len))
+    if r < 0:
+        raise MLAError(2, lib().mla_last_error().decode())
+    return int(r)
 
 
 def lmax(p: Params) -> int:

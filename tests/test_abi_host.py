@@ -223,6 +223,35 @@ def test_balanced_plan(B, lo, hi, Sq, min_splits, seed):
         assert (touched_parts(lens, q.num_parts) >= min_splits).all()
 
 
+@pytest.mark.parametrize("B,L", [(64, 4096), (1, 4096), (4, 131072), (128, 16384), (3, 70), (1, 1)])
+def test_default_num_splits(B, L):
+    """The fixed-split default: the planner's parts for B equal sequences, shared
+    evenly; the resulting fixed plan covers every page and is accepted."""
+    pages = (L + 63) // 64
+    p = mla.make_params(B, 1, 128, 128, 512, 64, num_pages=B * pages, max_pages=pages)
+    S = mla.default_num_splits(p, L)
+    q = mla.plan_splits(p, L, B * L, num_cus=256, min_splits=1)
+    assert S == min(max(1, -(-q.num_parts // B)), pages)
+    assert 1 <= S <= pages
+    f = mla.make_params(B, 1, 128, 128, 512, 64, num_pages=B * pages, max_pages=pages,
+                        num_splits=S, split_pages=-(-pages // S))
+    assert status_of(f) == 0
+    assert S * f.split_pages >= pages
+
+
+def test_default_num_splits_values_and_errors():
+    p = mla.make_params(64, 1, 128, 128, 512, 64, num_pages=64 * 64, max_pages=64)
+    assert mla.default_num_splits(p, 4096) == 4          # 256 parts over 64 sequences
+    b1 = mla.make_params(1, 1, 128, 128, 512, 64, num_pages=64, max_pages=64)
+    assert mla.default_num_splits(b1, 4096) == 16        # 64 pages, parts of 4 pages
+    L = mla.lib()
+    assert L.mla_default_num_splits(None, 4096) == -1
+    assert L.mla_default_num_splits(ctypes.byref(p), 0) == -1
+    bad = mla.make_params(64, 1, 128, 128, 512, 64, num_pages=64 * 64, max_pages=64)
+    bad.B = 0
+    assert L.mla_default_num_splits(ctypes.byref(bad), 4096) == -1
+
+
 def test_generic_split_count_invariance_of_checks():
     for S in (1, 2, 8, 32, 64):
         p = v3(max_pages=64, num_splits=S)
