@@ -216,6 +216,33 @@ mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const 
                               void *out, float *lse_out, void *stream);
 
 /*
+ * mla_decode_step -- the whole absorbed decode step in one call: mla_absorb_q,
+ * mla_decode_splitkv, then mla_combine_up_v where it applies (else mla_combine_lse
+ * and mla_up_v), all on `stream`, with the intermediates (q_abs, the partials, and
+ * o_latent when the merge and the up-projection are two launches) in a workspace
+ * the caller owns ("DeepSeek-MLA-Principle", matrix absorption 3): the query is
+ * absorbed once, attention runs in latent space, the output is up-projected once).
+ * The output equals that of the separate calls bit for bit.
+ *
+ *   q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV
+ *                as for the separate calls (in)
+ *   out        [B,Sq,H,d_h] out_dtype (out)
+ *   lse_out    [B,Sq,H] fp32 (out; may be NULL)
+ *   workspace  device memory of at least mla_decode_step_workspace(p) bytes,
+ *              256-byte aligned (scratch: its contents on entry do not matter and
+ *              are overwritten; two calls in flight at once need two workspaces)
+ * Returns MLA_ERR_NULL / MLA_ERR_SHAPE (workspace NULL, misaligned or too small)
+ * without launching anything, else the first failing call's status.
+ */
+mla_status_t mla_decode_step(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
+                             const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                             const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out, float *lse_out,
+                             void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes mla_decode_step needs for *p (host-only; -1 for invalid p). */
+int64_t mla_decode_step_workspace(const mla_params_t *p);
+
+/*
  * mla_append_kv -- write the Sq new tokens of every sequence into the paged
  * cache, rotating the shared RoPE key at each token's position; optionally
  * rotate the query's RoPE part at the same positions.  The decode module of

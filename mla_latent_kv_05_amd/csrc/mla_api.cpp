@@ -82,6 +82,29 @@ mla_status_t hip_status(hipError_t e, const char *what) {
     return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+size_t elem_bytes(int dt) { return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
+
+int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Intermediates of the one-call decode step, at 256-byte aligned offsets of one
+// workspace: q_abs, lse_part, o_part, then o_latent when the merge and the
+// up-projection run as two launches.
+struct StepLayout {
+    int64_t q_abs, lse_part, o_part, o_latent, bytes;
+};
+
+StepLayout step_layout(const mla_params_t &p) {
+    const int64_t rows = (int64_t)p.B * p.Sq * p.H;
+    StepLayout l{};
+    l.q_abs = 0;
+    l.lse_part = align256(rows * p.d_c * (int64_t)elem_bytes(p.latent_dtype));
+    l.o_part = l.lse_part + align256(rows * p.num_splits * 4);
+    l.o_latent = l.o_part + align256(rows * p.num_splits * (int64_t)p.d_c * 4);
+    l.bytes = mla::combine_up_v_supported(p) ? l.o_latent
+                                             : l.o_latent + align256(rows * p.d_c * (int64_t)elem_bytes(p.latent_dtype));
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,6 +348,65 @@ mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, co
     return hip_status(mla::launch_prefill_attention(*p, q_nope, q_rope, k_nope, v_t, k_pe, block_table, seq_lens,
                                                     out, st),
                       "mla_prefill_attention launch");
+}
+
+int64_t mla_decode_step_workspace(const mla_params_t *p) {
+    if (check(p) != MLA_OK) return -1;
+    return step_layout(*p).bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// absorb, attention, then the merge and up-projection (one launch where the fused
+// tail applies) on the intermediates at ws
+mla_status_t run_step(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
+                      const void *k_pe, const float *kv_scale, const int32_t *block_table, const int32_t *seq_lens,
+                      const void *W_UK, const void *W_UV, void *out, float *lse_out, char *ws, void *stream) {
+    const StepLayout l = step_layout(*p);
+    void *q_abs = ws + l.q_abs;
+    float *lse_part = reinterpret_cast<float *>(ws + l.lse_part);
+    float *o_part = reinterpret_cast<float *>(ws + l.o_part);
+    mla_status_t s = mla_absorb_q(p, q_nope, W_UK, q_abs, stream);
+    if (s != MLA_OK) return s;
+    s = mla_decode_splitkv(p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, o_part, lse_part, stream);
+    if (s != MLA_OK) return s;
+    if (mla::combine_up_v_supported(*p)) return mla_combine_up_v(p, o_part, lse_part, W_UV, out, lse_out, stream);
+    void *o_latent = ws + l.o_latent;
+    s = mla_combine_lse(p, o_part, lse_part, o_latent, lse_out, stream);
+    if (s != MLA_OK) return s;
+    return mla_up_v(p, o_latent, W_UV, out, stream);
+}
+
+mla_status_t check_step(const mla_params_t *p, const void *q_nope, const void *c_kv, const int32_t *block_table,
+                        const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out, const char *who) {
+    mla_status_t s = check(p);
+    if (s != MLA_OK) return s;
+    if (!q_nope || !c_kv || !block_table || !seq_lens || !W_UK || !W_UV || !out)
+        return fail(MLA_ERR_NULL, "%s: NULL tensor pointer", who);
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode_step(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
+                             const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                             const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out, float *lse_out,
+                             void *workspace, int64_t workspace_bytes, void *stream) {
+    mla_status_t s = check_step(p, q_nope, c_kv, block_table, seq_lens, W_UK, W_UV, out, "mla_decode_step");
+    if (s != MLA_OK) return s;
+    if (!workspace) return fail(MLA_ERR_NULL, "mla_decode_step: NULL workspace");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(MLA_ERR_SHAPE, "mla_decode_step: workspace must be 256-byte aligned");
+    const int64_t need = step_layout(*p).bytes;
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_SHAPE, "mla_decode_step: workspace of %lld bytes, need %lld (mla_decode_step_workspace)",
+                    (long long)workspace_bytes, (long long)need);
+    return run_step(p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV, out, lse_out,
+                    static_cast<char *>(workspace), stream);
 }
 
 }  // extern "C"

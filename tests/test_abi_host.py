@@ -256,3 +256,31 @@ def test_generic_split_count_invariance_of_checks():
     for S in (1, 2, 8, 32, 64):
         p = v3(max_pages=64, num_splits=S)
         assert status_of(p) == 0
+
+
+def test_decode_step_workspace_layout():
+    """Workspace of the one-call step: q_abs, lse_part, o_part (and o_latent when
+    the merge and the up-projection are two launches), each 256-byte aligned."""
+    def a(n):
+        return (n + 255) // 256 * 256
+    p = v3(B=3, Sq=2, num_splits=5)
+    rows = 3 * 2 * 128
+    want = a(rows * 512 * 2) + a(rows * 5 * 4) + a(rows * 5 * 512 * 4)
+    assert mla.decode_step_workspace(p) == want                 # fused tail: no o_latent
+    q = v3(B=3, Sq=2, num_splits=5, latent_dtype=mla.F32)       # two-launch tail
+    assert mla.decode_step_workspace(q) == a(rows * 512 * 4) + a(rows * 5 * 4) + a(rows * 5 * 512 * 4) + a(rows * 512 * 4)
+    assert mla.lib().mla_decode_step_workspace(None) == -1
+
+
+def test_decode_step_validates_on_the_host():
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    p = v3(Sq=1)
+    n = mla.decode_step_workspace(p)
+    args = [d] * 10
+    # NULL q_nope, NULL workspace, misaligned workspace, small workspace: no launch
+    assert L.mla_decode_step(ctypes.byref(p), None, *args[1:], None, d, n, None) == 1
+    assert L.mla_decode_step(ctypes.byref(p), *args, None, None, n, None) == 1
+    assert L.mla_decode_step(ctypes.byref(p), *args, None, ctypes.c_void_p(0x1008), n, None) == 2
+    assert L.mla_decode_step(ctypes.byref(p), *args, None, d, n - 1, None) == 2
+    assert L.mla_decode_step(ctypes.byref(v3(Sq=257)), *args, None, d, n, None) == 2
