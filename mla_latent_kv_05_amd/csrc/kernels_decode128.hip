@@ -71,6 +71,9 @@ constexpr int kSmem = kSmemStages + 8 * 1024;           // + one buffer of the w
 constexpr int kSteps = 36;                              // score k-steps: 576 / 16
 constexpr int kCopies = 9;                              // copy instructions per wave per tile
 constexpr float kSlack = 64.f;                          // log2 units a score may exceed the reference by
+constexpr int kORow = 256 * 4 + 16;                     // LDS stride of an output row (fp32, padded)
+constexpr int kOutArea = 32 * kORow;                    // a wave's output area: one head block
+static_assert(4 * kOutArea <= kSmemStages, "output areas inside the stages");
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 static_assert(kRows == 128, "four waves of 32 rows");
 
@@ -507,27 +510,39 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     }
 
     // ---- output: lse of the wave's head block; O of its 64 heads x 256 columns,
-    // normalised by the sums the score waves published
+    // normalised by the sums the score waves published.  A lane holds 16 columns of
+    // one row in groups of four, so O goes out through LDS: each head block is
+    // written to a wave-private area of 32 rows and read back a row at a time, and
+    // every store then writes 1 KiB of one row (a whole-row store instead of 32
+    // rows x 32 bytes).
+    const float inv0 = lds_load<float>(cell(xb, 2 * pr, n));
+    const float inv1 = lds_load<float>(cell(xb, 2 * pr + 1, n));
+    wait_vmcnt<0>();           // the copies of tiles past the end (zero-length) are done too
+    barrier_lds();             // every wave has its sums: the stage area is free
     {
         const float l_tot = pair_sum(l_run);
         if (g == 0)
             lse_part[(row_w + n) * S + seg.c] = l_tot == 0.f ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
+    const uint32_t ob = sm + w * kOutArea;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int hb = 2 * pr + j;
-        const float inv = lds_load<float>(cell(xb, hb, n));
+        const float inv = j ? inv1 : inv0;
         // oacc[j][cb][4i + e]: latent column 256kh + 32cb + 8i + 4g + e of head n of block hb
-        float *dst = o_part + ((static_cast<int64_t>(seg.b) * p.Sq * p.H + rg * kRows + 32 * hb + n) * S + seg.c) * kDc +
-                     256 * kh + 4 * g;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 o = f32x4{oacc[j][cb][4 * i], oacc[j][cb][4 * i + 1], oacc[j][cb][4 * i + 2],
-                                      oacc[j][cb][4 * i + 3]} * inv;
-                *reinterpret_cast<f32x4 *>(dst + 32 * cb + 8 * i) = o;
-            }
+            for (int i = 0; i < 4; ++i)
+                lds_store<f32x4>(ob + n * kORow + (32 * cb + 8 * i + 4 * g) * 4,
+                                 f32x4{oacc[j][cb][4 * i], oacc[j][cb][4 * i + 1], oacc[j][cb][4 * i + 2],
+                                       oacc[j][cb][4 * i + 3]} * inv);
+        // row x of the block: lane l stores columns 4l .. 4l + 3 of the wave's half
+        float *dst = o_part + ((static_cast<int64_t>(seg.b) * p.Sq * p.H + rg * kRows + 32 * hb) * S + seg.c) * kDc +
+                     256 * kh + 4 * lane;
+#pragma unroll
+        for (int x = 0; x < 32; ++x)
+            *reinterpret_cast<f32x4 *>(dst + static_cast<int64_t>(x) * S * kDc) = lds_load<f32x4>(ob + x * kORow + 16 * lane);
     }
 }
 
