@@ -243,6 +243,30 @@ mla_status_t mla_decode_step(const mla_params_t *p, const void *q_nope, const vo
 int64_t mla_decode_step_workspace(const mla_params_t *p);
 
 /*
+ * mla_decode_step_noalloc -- mla_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same calls and the same output bit for bit, with
+ * the intermediates in a static scratch array of the library instead of a
+ * caller's workspace.  It allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).
+ *   - The scratch holds 160 MiB (167,772,160 bytes) per GPU, reserved when the
+ *     library's code is loaded on that GPU and held until the process ends.
+ *     Parameters whose mla_decode_step_workspace exceeds it return MLA_ERR_SHAPE
+ *     without launching anything (B = 64, Sq = 1, num_splits = 8 at the
+ *     DeepSeek-V3 shapes needs 143 MB).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that overlap
+ *     on one GPU (other streams, other threads) race on it: serialise them.
+ *   - The scratch's device address is looked up on the first call on each device
+ *     (the device current at the call); a failure returns MLA_ERR_HIP.
+ * Arguments as for mla_decode_step, without the workspace.
+ */
+mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
+                                     const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                                     const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out,
+                                     float *lse_out, void *stream);
+
+/*
  * mla_append_kv -- write the Sq new tokens of every sequence into the paged
  * cache, rotating the shared RoPE key at each token's position; optionally
  * rotate the query's RoPE part at the same positions.  The decode module of

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "mla.h"
@@ -390,6 +391,38 @@ mla_status_t check_step(const mla_params_t *p, const void *q_nope, const void *c
 
 }  // namespace
 
+// The no-allocation step's intermediates live in this file-scope device array (one
+// copy per GPU, alive until the process ends).  Host code never passes the array's
+// name to a kernel or a copy: it uses the device address hipGetSymbolAddress gives,
+// looked up once per device with that device current.
+constexpr int64_t kScratchBytes = 160ll << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+mla_status_t scratch_of_current_device(char **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_decode_step_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_HIP, "mla_decode_step_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !a)
+            return fail(MLA_ERR_HIP, "mla_decode_step_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = a;
+    }
+    *ptr = static_cast<char *>(g_scratch_ptr[dev]);
+    return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 mla_status_t mla_decode_step(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
@@ -407,6 +440,25 @@ mla_status_t mla_decode_step(const mla_params_t *p, const void *q_nope, const vo
                     (long long)workspace_bytes, (long long)need);
     return run_step(p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV, out, lse_out,
                     static_cast<char *>(workspace), stream);
+}
+
+mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, const void *q_rope, const void *c_kv,
+                                     const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                                     const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out,
+                                     float *lse_out, void *stream) {
+    mla_status_t s = check_step(p, q_nope, c_kv, block_table, seq_lens, W_UK, W_UV, out, "mla_decode_step_noalloc");
+    if (s != MLA_OK) return s;
+    const int64_t need = step_layout(*p).bytes;
+    if (need > kScratchBytes)
+        return fail(MLA_ERR_SHAPE,
+                    "mla_decode_step_noalloc: the step needs %lld bytes of scratch, the static scratch holds %lld "
+                    "(use mla_decode_step with a workspace)",
+                    (long long)need, (long long)kScratchBytes);
+    char *ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s != MLA_OK) return s;
+    return run_step(p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV, out, lse_out, ws,
+                    stream);
 }
 
 }  // extern "C"

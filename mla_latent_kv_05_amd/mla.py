@@ -27,7 +27,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 # every symbol include/mla.h declares
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
            "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax", "mla_expand_kv",
-           "mla_decode_step", "mla_decode_step_workspace",
+           "mla_decode_step", "mla_decode_step_workspace", "mla_decode_step_noalloc",
            "mla_check_params", "mla_plan_splits", "mla_default_num_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
@@ -84,6 +84,7 @@ def lib():
             ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
             ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
             ("mla_decode_step", [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]),
+            ("mla_decode_step_noalloc", [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
             ("mla_check_params", [PP]),
             ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
         ):
@@ -280,6 +281,29 @@ def decode_step(p: Params, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, se
         _ptr(lse_out, "lse_out", rows, F32),
         _ptr(workspace, "workspace"),
         ctypes.c_int64(workspace.numel()),
+        _stream(stream)))
+
+
+def decode_step_noalloc(p: Params, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV, out,
+                        lse_out=None, stream=None) -> None:
+    """decode_step with its intermediates in the library's static scratch (no
+    allocation; calls on one GPU must not overlap)."""
+    rows = (p.B, p.Sq, p.H)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    _check(lib().mla_decode_step_noalloc(
+        ctypes.byref(p),
+        _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
+        _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+        _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+        _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
+        _ptr(lse_out, "lse_out", rows, F32),
         _stream(stream)))
 
 

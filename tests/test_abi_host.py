@@ -284,3 +284,15 @@ def test_decode_step_validates_on_the_host():
     assert L.mla_decode_step(ctypes.byref(p), *args, None, ctypes.c_void_p(0x1008), n, None) == 2
     assert L.mla_decode_step(ctypes.byref(p), *args, None, d, n - 1, None) == 2
     assert L.mla_decode_step(ctypes.byref(v3(Sq=257)), *args, None, d, n, None) == 2
+
+
+def test_decode_step_noalloc_rejects_large_steps_on_the_host():
+    """Parameters whose step needs more than the 160 MiB static scratch are
+    refused before any HIP call (so this runs without a GPU)."""
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    big = v3(B=64, num_splits=16, max_pages=16)           # o_part alone: 64*128*16*512*4 = 268 MB
+    assert mla.decode_step_workspace(big) > 160 << 20
+    assert L.mla_decode_step_noalloc(ctypes.byref(big), *([d] * 10), None, None) == 2
+    assert "static scratch" in L.mla_last_error().decode()
+    assert L.mla_decode_step_noalloc(ctypes.byref(v3()), None, *([d] * 9), None, None) == 1
