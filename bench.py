@@ -105,6 +105,9 @@ def main():
                         latent_dtype=fl, out_dtype=mla.F32)
     p = mla.plan_splits(p, max(lens), case.total_tokens, num_cus=props.multi_processor_count,
                         min_splits=wl.min_splits)
+    # bf16 partials with a bf16 latent: half the bytes the attention writes and the
+    # merge reads (each partial row rounded once, as o_latent is)
+    p.part_dtype = mla.F32 if wl.dtype == "f32" else mla.BF16
 
     names = ("q_nope", "q_rope", "c_kv", "k_pe", "kv_scale", "block_table", "seq_lens", "W_UK", "W_UV")
     base = {k: (None if getattr(case, k) is None else getattr(case, k).to(dev)) for k in names}
@@ -259,6 +262,7 @@ def main():
                         f"(sum {case.total_tokens}), page 64, permuted pages, {wl.dtype} cache",
             "name": wl.name, "B": wl.B, "Sq": wl.Sq, "tokens": case.total_tokens,
             "num_splits": p.num_splits, "num_parts": p.num_parts,
+            "partials": "bf16" if p.part_dtype == mla.BF16 else "f32",
             "decode_kernel": mla.decode_kernel_name(p), "replicas": args.replicas,
         },
         "roofline": {

@@ -103,6 +103,9 @@ typedef enum {
  *   latent_dtype q_abs and o_latent       F32 | BF16
  *   out_dtype   out                       F32 | BF16
  *   flags       MLA_FLAG_* bits
+ *   part_dtype  o_part (the split partials)  F32 | BF16 (0 = F32).  BF16 halves
+ *               the bytes the attention writes and the merge reads; each partial
+ *               row is rounded once (to nearest even) after its normalisation.
  */
 typedef struct {
     int32_t B, Sq, H, d_h, d_c, d_r;
@@ -115,6 +118,7 @@ typedef struct {
     int32_t q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype;
     uint32_t flags;
     int32_t num_parts;
+    int32_t part_dtype;
 } mla_params_t;
 
 /*
@@ -156,7 +160,7 @@ mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void 
  *   kv_scale  [num_pages,64] fp32   (in; required iff kv_dtype == FP8_E4M3, else ignored)
  *   block_table [B,max_pages] int32 (in; entries past a sequence's last page unread)
  *   seq_lens  [B] int32             (in; tokens per sequence incl. the Sq new ones)
- *   o_part    [B,Sq,H,num_splits,d_c] fp32 (out)
+ *   o_part    [B,Sq,H,num_splits,d_c] part_dtype (out)
  *   lse_part  [B,Sq,H,num_splits]     fp32 (out)
  * Cache slots at or beyond seq_lens[b] in a sequence's last page are read but
  * contribute exactly zero, whatever they hold (non-finite values included).
@@ -164,7 +168,7 @@ mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void 
 mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const void *q_rope,
                                 const void *c_kv, const void *k_pe, const float *kv_scale,
                                 const int32_t *block_table, const int32_t *seq_lens,
-                                float *o_part, float *lse_part, void *stream);
+                                void *o_part, float *lse_part, void *stream);
 
 /*
  * mla_combine_lse -- log-sum-exp merge of split partials (the merge that
@@ -174,12 +178,12 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
  * Splits with lse_c = -inf carry no weight and their o_part is not read.  A
  * row whose splits are all empty gets o_latent = 0 and lse = -inf.
  *
- *   o_part   [B,Sq,H,num_splits,d_c] fp32 (in)
+ *   o_part   [B,Sq,H,num_splits,d_c] part_dtype (in)
  *   lse_part [B,Sq,H,num_splits]     fp32 (in)
  *   o_latent [B,Sq,H,d_c]  latent_dtype  (out)
  *   lse_out  [B,Sq,H] fp32 (out; may be NULL)
  */
-mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const float *lse_part,
+mla_status_t mla_combine_lse(const mla_params_t *p, const void *o_part, const float *lse_part,
                              void *o_latent, float *lse_out, void *stream);
 
 /*
@@ -206,13 +210,13 @@ mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W
  * Kernels exist for d_h = 128, d_c = 512, bf16 weights and latent_dtype = bf16;
  * other parameters return MLA_ERR_UNSUPPORTED.
  *
- *   o_part   [B,Sq,H,num_splits,d_c] fp32 (in)
+ *   o_part   [B,Sq,H,num_splits,d_c] part_dtype (in)
  *   lse_part [B,Sq,H,num_splits]     fp32 (in)
  *   W_UV     [H,d_h,d_c]   w_dtype      (in)
  *   out      [B,Sq,H,d_h]  out_dtype    (out)
  *   lse_out  [B,Sq,H] fp32 (out; may be NULL)
  */
-mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const float *lse_part, const void *W_UV,
+mla_status_t mla_combine_up_v(const mla_params_t *p, const void *o_part, const float *lse_part, const void *W_UV,
                               void *out, float *lse_out, void *stream);
 
 /*

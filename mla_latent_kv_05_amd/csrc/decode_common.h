@@ -124,6 +124,15 @@ __device__ __forceinline__ int perm_tok(int x) {
 // issued, and LDS operations written as inline asm elsewhere only make those waits
 // stricter) and keeps each value in its registers until it has landed.
 __device__ __forceinline__ u32x4 ld128(uint32_t addr) { return lds_load<u32x4>(addr); }
+
+// four consecutive elements of a split partial (element index e) in the partials'
+// storage type: fp32, or bf16 rounded to nearest even
+__device__ __forceinline__ void store_part4(void *o_part, int part_dtype, int64_t e, const f32x4 &v) {
+    if (part_dtype == MLA_BF16)
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(o_part) + e) = u32x2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
+    else
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(o_part) + e) = v;
+}
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // receives element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3.
 __device__ __forceinline__ v4i16 ld_tr16(uint32_t addr) {

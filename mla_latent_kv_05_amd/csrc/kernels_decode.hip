@@ -267,7 +267,7 @@ __device__ __forceinline__ void attend_segment(
     char *smem, const mla_params_t &p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
     const void *__restrict__ c_kv, const uint16_t *__restrict__ k_pe,
     const float *__restrict__ kv_scale, const int32_t *__restrict__ bt, int seq_len,
-    const Segment &seg, int rg, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    const Segment &seg, int rg, void *__restrict__ o_part, float *__restrict__ lse_part) {
     constexpr int kNst = kFp8 ? kStagesFp8 : kStagesBf16;     // raw ring depth
     constexpr int kAhead = kNst - 1;                          // tiles copied ahead of the one finishing
     constexpr int kLoads = kFp8 ? kLoadsFp8 : kLoadsBf16;
@@ -664,7 +664,7 @@ __device__ __forceinline__ void attend_segment(
     }
     const float norm = kFp8 ? l_tot : pair_sum(lw_run);
     const float inv = 1.f / norm;
-    float *dst = o_part + out_row * kDc + kh * 256;
+    const int64_t dst = out_row * kDc + kh * 256;
     // oacc[blk][j]: head t32, latent 256kh + 32*blk + 8*(j/4) + 4*g2 + j%4
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk)
@@ -672,7 +672,7 @@ __device__ __forceinline__ void attend_segment(
         for (int jq = 0; jq < 4; ++jq) {
             const f32x4 v = f32x4{oacc[blk][jq * 4], oacc[blk][jq * 4 + 1], oacc[blk][jq * 4 + 2],
                                   oacc[blk][jq * 4 + 3]} * inv;
-            *reinterpret_cast<f32x4 *>(dst + blk * 32 + jq * 8 + g2 * 4) = v;
+            store_part4(o_part, p.part_dtype, dst + blk * 32 + jq * 8 + g2 * 4, v);
         }
     if (kh == 0 && g2 == 0) lse_part[out_row] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
@@ -682,7 +682,7 @@ __device__ __forceinline__ void decode_wave(
     char *smem, const mla_params_t &p, int part, int rg, const uint16_t *__restrict__ q_abs,
     const uint16_t *__restrict__ q_rope, const void *__restrict__ c_kv, const uint16_t *__restrict__ k_pe,
     const float *__restrict__ kv_scale, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = p.num_splits;
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
     const void *__restrict__ c_kv, const uint16_t *__restrict__ k_pe,
     const float *__restrict__ kv_scale, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) char smem[kFp8 ? kSmemFp8 : kSmemBf16];
     // workgroup -> (part, row group rg); parts are spread over the 8 XCDs, the row
     // groups of one part share an XCD
@@ -744,7 +744,7 @@ bool decode_mfma_supported(const mla_params_t &p) {
 hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const void *q_rope,
                               const void *c_kv, const void *k_pe, const float *kv_scale,
                               const int32_t *block_table, const int32_t *seq_lens,
-                              float *o_part, float *lse_part, hipStream_t stream) {
+                              void *o_part, float *lse_part, hipStream_t stream) {
     const int64_t parts = p.num_parts > 0 ? p.num_parts : static_cast<int64_t>(p.B) * p.num_splits;
     const int64_t n_rg = (static_cast<int64_t>(p.Sq) * p.H) / kRows;
     const int64_t blocks = ((parts + 7) / 8) * 8 * n_rg;

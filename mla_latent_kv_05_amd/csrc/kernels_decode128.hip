@@ -72,6 +72,7 @@ constexpr int kSteps = 36;                              // score k-steps: 576 / 
 constexpr int kCopies = 9;                              // copy instructions per wave per tile
 constexpr float kSlack = 64.f;                          // log2 units a score may exceed the reference by
 constexpr int kORow = 256 * 4 + 16;                     // LDS stride of an output row (fp32, padded)
+constexpr int kORowBf16 = 256 * 2 + 16;                 // ... bf16
 constexpr int kOutArea = 32 * kORow;                    // a wave's output area: one head block
 static_assert(4 * kOutArea <= kSmemStages, "output areas inside the stages");
 static_assert(kSmem <= 160 * 1024, "LDS budget");
@@ -133,7 +134,7 @@ __device__ __forceinline__ bf16x8 tr_op(const v4i16 &lo, const v4i16 &hi) {
 __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p, const uint16_t *__restrict__ q_abs,
                                                const uint16_t *__restrict__ q_rope, const char *__restrict__ c_kv,
                                                const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ seg_bt,
-                                               const Segment &seg, int seq_len, int rg, float *__restrict__ o_part,
+                                               const Segment &seg, int seq_len, int rg, void *__restrict__ o_part,
                                                float *__restrict__ lse_part) {
     // lane-dependent values are recomputed per segment (opaque to code motion, so
     // that they do not stay live across the segment loop)
@@ -513,8 +514,8 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     // normalised by the sums the score waves published.  A lane holds 16 columns of
     // one row in groups of four, so O goes out through LDS: each head block is
     // written to a wave-private area of 32 rows and read back a row at a time, and
-    // every store then writes 1 KiB of one row (a whole-row store instead of 32
-    // rows x 32 bytes).
+    // every store then writes 1 KiB (bf16: 512 bytes) of one row, instead of 32
+    // rows x 32 bytes.
     const float inv0 = lds_load<float>(cell(xb, 2 * pr, n));
     const float inv1 = lds_load<float>(cell(xb, 2 * pr + 1, n));
     wait_vmcnt<0>();           // the copies of tiles past the end (zero-length) are done too
@@ -525,31 +526,49 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
             lse_part[(row_w + n) * S + seg.c] = l_tot == 0.f ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     const uint32_t ob = sm + w * kOutArea;
+    const bool part_bf16 = p.part_dtype == MLA_BF16;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int hb = 2 * pr + j;
         const float inv = j ? inv1 : inv0;
+        const int64_t dst = ((static_cast<int64_t>(seg.b) * p.Sq * p.H + rg * kRows + 32 * hb) * S + seg.c) * kDc +
+                            256 * kh;
         // oacc[j][cb][4i + e]: latent column 256kh + 32cb + 8i + 4g + e of head n of block hb
+        if (part_bf16) {
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
+            for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                lds_store<f32x4>(ob + n * kORow + (32 * cb + 8 * i + 4 * g) * 4,
-                                 f32x4{oacc[j][cb][4 * i], oacc[j][cb][4 * i + 1], oacc[j][cb][4 * i + 2],
-                                       oacc[j][cb][4 * i + 3]} * inv);
-        // row x of the block: lane l stores columns 4l .. 4l + 3 of the wave's half
-        float *dst = o_part + ((static_cast<int64_t>(seg.b) * p.Sq * p.H + rg * kRows + 32 * hb) * S + seg.c) * kDc +
-                     256 * kh + 4 * lane;
+                for (int i = 0; i < 4; ++i)
+                    lds_store<u32x2>(ob + n * kORowBf16 + (32 * cb + 8 * i + 4 * g) * 2,
+                                     u32x2{cvt_pk_bf16(oacc[j][cb][4 * i] * inv, oacc[j][cb][4 * i + 1] * inv),
+                                           cvt_pk_bf16(oacc[j][cb][4 * i + 2] * inv, oacc[j][cb][4 * i + 3] * inv)});
+            // row x of the block: lane l stores columns 4l .. 4l + 3 of the wave's half
+            uint16_t *d = static_cast<uint16_t *>(o_part) + dst + 4 * lane;
 #pragma unroll
-        for (int x = 0; x < 32; ++x)
-            *reinterpret_cast<f32x4 *>(dst + static_cast<int64_t>(x) * S * kDc) = lds_load<f32x4>(ob + x * kORow + 16 * lane);
+            for (int x = 0; x < 32; ++x)
+                *reinterpret_cast<u32x2 *>(d + static_cast<int64_t>(x) * S * kDc) =
+                    lds_load<u32x2>(ob + x * kORowBf16 + 8 * lane);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_store<f32x4>(ob + n * kORow + (32 * cb + 8 * i + 4 * g) * 4,
+                                     f32x4{oacc[j][cb][4 * i], oacc[j][cb][4 * i + 1], oacc[j][cb][4 * i + 2],
+                                           oacc[j][cb][4 * i + 3]} * inv);
+            float *d = static_cast<float *>(o_part) + dst + 4 * lane;
+#pragma unroll
+            for (int x = 0; x < 32; ++x)
+                *reinterpret_cast<f32x4 *>(d + static_cast<int64_t>(x) * S * kDc) =
+                    lds_load<f32x4>(ob + x * kORow + 16 * lane);
+        }
     }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
     const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     // workgroup -> (part, row group rg): parts spread over the 8 XCDs, the row groups
     // of one part on the same XCD
@@ -593,7 +612,7 @@ bool decode128_supported(const mla_params_t &p) {
 }
 
 hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                             float *lse_part, hipStream_t stream) {
     const int64_t parts = p.num_parts > 0 ? p.num_parts : static_cast<int64_t>(p.B) * p.num_splits;
     const int64_t n_rg = (static_cast<int64_t>(p.Sq) * p.H) / kRows;

@@ -305,7 +305,7 @@ __device__ __forceinline__ void score_role(char *smem, const mla_params_t &p, co
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, const char *__restrict__ c_kv,
                                             const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ bt,
-                                            const Segment &seg, const SegInfo &si, float *__restrict__ o_part) {
+                                            const Segment &seg, const SegInfo &si, void *__restrict__ o_part) {
     int lane = threadIdx.x & 63;                       // opaque, as in score_role
     asm volatile("" : "+v"(lane));
     const int v = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) - 4);   // 0..3
@@ -475,14 +475,14 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const float sc = __uint_as_float(inv[hb]);
-        float *dst = o_part + ((si.row_wg + 32 * hb + t32) * S + seg.c) * kDc + 128 * v + 4 * g2;
+        const int64_t dst = ((si.row_wg + 32 * hb + t32) * S + seg.c) * kDc + 128 * v + 4 * g2;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 o = f32x4{oacc[hb][cb][4 * q], oacc[hb][cb][4 * q + 1], oacc[hb][cb][4 * q + 2],
                                       oacc[hb][cb][4 * q + 3]} * sc;
-                *reinterpret_cast<f32x4 *>(dst + 32 * cb + 8 * q) = o;
+                store_part4(o_part, p.part_dtype, dst + 32 * cb + 8 * q, o);
             }
     }
 }
@@ -490,7 +490,7 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
 __global__ __launch_bounds__(kThreads) void decode8_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
     const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     // workgroup -> (part, row group rg); parts are spread over the 8 XCDs, the row
     // groups of one part share an XCD (the second read of a page hits its L2)
@@ -539,7 +539,7 @@ bool decode8_supported(const mla_params_t &p) {
 }
 
 hipError_t launch_decode8(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                          const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                          const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                           float *lse_part, hipStream_t stream) {
     const int64_t parts = p.num_parts > 0 ? p.num_parts : static_cast<int64_t>(p.B) * p.num_splits;
     const int64_t n_rg = (static_cast<int64_t>(p.Sq) * p.H) / kRows;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
     mla_params_t p, const void *__restrict__ q_abs, const void *__restrict__ q_rope,
     const void *__restrict__ c_kv, const void *__restrict__ k_pe,
     const float *__restrict__ kv_scale, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ o_part,
+    const int32_t *__restrict__ seq_lens, void *__restrict__ o_part,
     float *__restrict__ lse_part) {
     __shared__ float qa[kMaxDc];
     __shared__ float qr[kMaxDr];
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
 #pragma unroll
     for (int k = 0; k < kColsPerThread; ++k) {
         const int m = threadIdx.x + k * kThreads;
-        if (m < p.d_c) o_part[out_idx * p.d_c + m] = acc[k] * inv;
+        if (m < p.d_c) store_elem(o_part, p.part_dtype, out_idx * p.d_c + m, acc[k] * inv);
     }
     if (threadIdx.x == 0) lse_part[out_idx] = m_run + logf(l_run);
 }
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void up_v_generic_kernel(
 constexpr int kMaxSplits = 4096;
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(
-    mla_params_t p, const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    mla_params_t p, const void *__restrict__ o_part, const float *__restrict__ lse_part,
     void *__restrict__ o_latent, float *__restrict__ lse_out) {
     __shared__ float w[kMaxSplits];
     __shared__ float red[kThreads / 64];
@@ -237,11 +237,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     }
     sum = block_reduce_sum(sum, red);                        // also orders the w[] writes
     const float inv = 1.f / sum;
-    const float *op = o_part + row * static_cast<int64_t>(S) * p.d_c;
+    const int64_t op = row * static_cast<int64_t>(S) * p.d_c;
     for (int m = threadIdx.x; m < p.d_c; m += kThreads) {
         float acc = 0.f;
         for (int c = 0; c < S; ++c)
-            if (w[c] != 0.f) acc += w[c] * op[static_cast<int64_t>(c) * p.d_c + m];
+            if (w[c] != 0.f) acc += w[c] * load_elem(o_part, p.part_dtype, op + static_cast<int64_t>(c) * p.d_c + m);
         store_elem(o_latent, p.latent_dtype, row * p.d_c + m, acc * inv);
     }
     if (lse_out && threadIdx.x == 0) lse_out[row] = mx + logf(sum);
@@ -262,7 +262,7 @@ hipError_t launch_absorb_generic(const mla_params_t &p, const void *q_nope, cons
 hipError_t launch_decode_generic(const mla_params_t &p, const void *q_abs, const void *q_rope,
                                  const void *c_kv, const void *k_pe, const float *kv_scale,
                                  const int32_t *block_table, const int32_t *seq_lens,
-                                 float *o_part, float *lse_part, hipStream_t stream) {
+                                 void *o_part, float *lse_part, hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.Sq * p.H * p.num_splits;
     hipLaunchKernelGGL(decode_generic_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                        p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, o_part, lse_part);
@@ -277,7 +277,7 @@ hipError_t launch_up_v_generic(const mla_params_t &p, const void *o_latent, cons
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const mla_params_t &p, const float *o_part, const float *lse_part,
+hipError_t launch_combine(const mla_params_t &p, const void *o_part, const float *lse_part,
                           void *o_latent, float *lse_out, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(p.B) * p.Sq * p.H;
     hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, stream,

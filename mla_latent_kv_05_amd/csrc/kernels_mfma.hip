@@ -18,6 +18,13 @@ using namespace gfx;
 constexpr int kDc = 512;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return cvt_pk_bf16(a, b); }
+// eight bf16 (16 bytes) -> two f32x4 (elements 0..3, 4..7)
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 &v, f32x4 &lo, f32x4 &hi) {
+    lo = f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+               __uint_as_float(v[1] & 0xffff0000u)};
+    hi = f32x4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xffff0000u), __uint_as_float(v[3] << 16),
+               __uint_as_float(v[3] & 0xffff0000u)};
+}
 
 // ---------------------------------------------------------------------------
 // mla_absorb_q: q_abs[r, h, m] = sum_d q_nope[r, h, d] W_UK[h, d, m]
@@ -201,9 +208,9 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
-template <bool kBf16Out>
+template <bool kBf16Out, bool kPartBf16>
 __global__ __launch_bounds__(256) void combine_kernel_512(
-    const mla_params_t p, const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    const mla_params_t p, const void *__restrict__ o_part, const float *__restrict__ lse_part,
     void *__restrict__ o_latent, float *__restrict__ lse_out) {
     const int lane = threadIdx.x & 63;
     const int64_t rows = static_cast<int64_t>(p.B) * p.Sq * p.H;
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float sum = 0.f;
     if (mx != -INFINITY) {
-        const float *op = o_part + row * static_cast<int64_t>(S) * kDc + lane * 8;
+        const int64_t op = row * static_cast<int64_t>(S) * kDc + lane * 8;     // element index
         for (int c0 = 0; c0 < S; c0 += 64) {
             const float lc = c0 + lane < S ? l[c0 + lane] : -INFINITY;
             const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);
@@ -227,8 +234,15 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
                 const int k = __builtin_ctzll(live);
                 live &= live - 1;
                 const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), k));
-                const f32x4 *src = reinterpret_cast<const f32x4 *>(op + static_cast<int64_t>(c0 + k) * kDc);
-                const f32x4 v0 = src[0], v1 = src[1];
+                const int64_t e = op + static_cast<int64_t>(c0 + k) * kDc;
+                f32x4 v0, v1;
+                if constexpr (kPartBf16) {
+                    unpack_bf16x8(*reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(o_part) + e), v0, v1);
+                } else {
+                    const f32x4 *src = reinterpret_cast<const f32x4 *>(static_cast<const float *>(o_part) + e);
+                    v0 = src[0];
+                    v1 = src[1];
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     acc[j] += wk * v0[j];
@@ -263,9 +277,9 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
 // ---------------------------------------------------------------------------
 constexpr int kCuRowsPerWave = kUpRows / 8;
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kPartBf16>
 __global__ __launch_bounds__(512) void combine_up_v_kernel(
-    const mla_params_t p, const float *__restrict__ o_part, const float *__restrict__ lse_part,
+    const mla_params_t p, const void *__restrict__ o_part, const float *__restrict__ lse_part,
     const uint16_t *__restrict__ W_UV, void *__restrict__ out, float *__restrict__ lse_out) {
     constexpr int kDh = 128;
     __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2];
@@ -302,12 +316,14 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         const float v = lse_part[row[i] * S + min(c0 + lane, S - 1)];
         return ok[i] && c0 + lane < S ? v : -INFINITY;
     };
-    // each row's partials as a raw buffer of S * d_c floats
+    // each row's partials as a raw buffer of S * d_c elements
+    constexpr int kEb = kPartBf16 ? 2 : 4;
     __amdgpu_buffer_rsrc_t prow[kCuRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i)
-        prow[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o_part) + row[i] * S * kDc, 0,
-                                                    ok[i] ? S * kDc * 4 : 0, 0x20000);
+        prow[i] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(static_cast<const char *>(o_part)) + row[i] * S * kDc * kEb, 0,
+            ok[i] ? S * kDc * kEb : 0, 0x20000);
     float l0[kCuRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i) l0[i] = lse_part[row[i] * S + min(lane, S - 1)];
@@ -355,12 +371,19 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
             for (int i = 0; i < kCuRowsPerWave; ++i) {
                 wa_[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), ka));
                 wb_[i] = has_b ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), kb)) : 0.f;
-                const uint32_t oa = wa_[i] != 0.f ? ((c0 + ka) * kDc + lane * 8) * 4u : 0x80000000u;
-                const uint32_t ob = wb_[i] != 0.f ? ((c0 + kb) * kDc + lane * 8) * 4u : 0x80000000u;
-                a0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0));
-                a1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa + 16u, 0, 0));
-                b0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0));
-                b1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob + 16u, 0, 0));
+                const uint32_t oa = wa_[i] != 0.f ? ((c0 + ka) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
+                const uint32_t ob = wb_[i] != 0.f ? ((c0 + kb) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
+                if constexpr (kPartBf16) {
+                    unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0)),
+                                  a0[i], a1[i]);
+                    unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0)),
+                                  b0[i], b1[i]);
+                } else {
+                    a0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0));
+                    a1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa + 16u, 0, 0));
+                    b0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0));
+                    b1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob + 16u, 0, 0));
+                }
             }
 #pragma unroll
             for (int i = 0; i < kCuRowsPerWave; ++i) {
@@ -428,17 +451,20 @@ bool combine_up_v_supported(const mla_params_t &p) {
     return p.d_c == kDc && p.d_h == 128 && p.latent_dtype == MLA_BF16 && p.w_dtype == MLA_BF16;
 }
 
-hipError_t launch_combine_up_v(const mla_params_t &p, const float *o_part, const float *lse_part, const void *W_UV,
+hipError_t launch_combine_up_v(const mla_params_t &p, const void *o_part, const float *lse_part, const void *W_UV,
                                void *out, float *lse_out, hipStream_t stream) {
     const int64_t R = static_cast<int64_t>(p.B) * p.Sq;
-    const int64_t blocks = (static_cast<int64_t>(p.H) + 7) / 8 * 8 * ((R + kUpRows - 1) / kUpRows);
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(p.H) + 7) / 8 * 8 * ((R + kUpRows - 1) / kUpRows)));
     const auto w = static_cast<const uint16_t *>(W_UV);
-    if (p.out_dtype == MLA_BF16)
-        hipLaunchKernelGGL(combine_up_v_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, p,
-                           o_part, lse_part, w, out, lse_out);
+    const bool ob = p.out_dtype == MLA_BF16, pb = p.part_dtype == MLA_BF16;
+    if (ob && pb)
+        hipLaunchKernelGGL((combine_up_v_kernel<true, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
+    else if (ob)
+        hipLaunchKernelGGL((combine_up_v_kernel<true, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
+    else if (pb)
+        hipLaunchKernelGGL((combine_up_v_kernel<false, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
     else
-        hipLaunchKernelGGL(combine_up_v_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, p,
-                           o_part, lse_part, w, out, lse_out);
+        hipLaunchKernelGGL((combine_up_v_kernel<false, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
     return hipGetLastError();
 }
 
@@ -482,16 +508,19 @@ bool combine_fast_supported(const mla_params_t &p) {
     return p.d_c == kDc && (p.latent_dtype == MLA_BF16 || p.latent_dtype == MLA_F32);
 }
 
-hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,
+hipError_t launch_combine_fast(const mla_params_t &p, const void *o_part, const float *lse_part,
                                void *o_latent, float *lse_out, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(p.B) * p.Sq * p.H;
-    const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
-    if (p.latent_dtype == MLA_BF16)
-        hipLaunchKernelGGL(combine_kernel_512<true>, dim3(blocks), dim3(256), 0, stream, p, o_part, lse_part,
-                           o_latent, lse_out);
+    const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+    const bool lb = p.latent_dtype == MLA_BF16, pb = p.part_dtype == MLA_BF16;
+    if (lb && pb)
+        hipLaunchKernelGGL((combine_kernel_512<true, true>), grid, dim3(256), 0, stream, p, o_part, lse_part, o_latent, lse_out);
+    else if (lb)
+        hipLaunchKernelGGL((combine_kernel_512<true, false>), grid, dim3(256), 0, stream, p, o_part, lse_part, o_latent, lse_out);
+    else if (pb)
+        hipLaunchKernelGGL((combine_kernel_512<false, true>), grid, dim3(256), 0, stream, p, o_part, lse_part, o_latent, lse_out);
     else
-        hipLaunchKernelGGL(combine_kernel_512<false>, dim3(blocks), dim3(256), 0, stream, p, o_part, lse_part,
-                           o_latent, lse_out);
+        hipLaunchKernelGGL((combine_kernel_512<false, false>), grid, dim3(256), 0, stream, p, o_part, lse_part, o_latent, lse_out);
     return hipGetLastError();
 }
 

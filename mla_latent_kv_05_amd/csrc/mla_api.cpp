@@ -74,6 +74,7 @@ mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
     if (!is_float_dtype(p->pe_dtype)) return fail(MLA_ERR_DTYPE, "pe_dtype must be F32 or BF16");
     if (!is_float_dtype(p->latent_dtype)) return fail(MLA_ERR_DTYPE, "latent_dtype must be F32 or BF16");
     if (!is_float_dtype(p->out_dtype)) return fail(MLA_ERR_DTYPE, "out_dtype must be F32 or BF16");
+    if (!is_float_dtype(p->part_dtype)) return fail(MLA_ERR_DTYPE, "part_dtype must be F32 or BF16");
     if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC)) return fail(MLA_ERR_SHAPE, "unknown flag bits 0x%x", p->flags);
     return MLA_OK;
 }
@@ -100,7 +101,7 @@ StepLayout step_layout(const mla_params_t &p) {
     l.q_abs = 0;
     l.lse_part = align256(rows * p.d_c * (int64_t)elem_bytes(p.latent_dtype));
     l.o_part = l.lse_part + align256(rows * p.num_splits * 4);
-    l.o_latent = l.o_part + align256(rows * p.num_splits * (int64_t)p.d_c * 4);
+    l.o_latent = l.o_part + align256(rows * p.num_splits * (int64_t)p.d_c * (int64_t)elem_bytes(p.part_dtype));
     l.bytes = mla::combine_up_v_supported(p) ? l.o_latent
                                              : l.o_latent + align256(rows * p.d_c * (int64_t)elem_bytes(p.latent_dtype));
     return l;
@@ -110,7 +111,7 @@ StepLayout step_layout(const mla_params_t &p) {
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 2; }
+int32_t mla_abi_version(void) { return 3; }
 
 const char *mla_status_string(mla_status_t s) {
     switch (s) {
@@ -206,7 +207,7 @@ mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void 
 
 mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const void *q_rope,
                                 const void *c_kv, const void *k_pe, const float *kv_scale,
-                                const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                                const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                                 float *lse_part, void *stream) {
     mla_status_t s = check(p);
     if (s != MLA_OK) return s;
@@ -239,7 +240,7 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
                       "mla_decode_splitkv launch");
 }
 
-mla_status_t mla_combine_lse(const mla_params_t *p, const float *o_part, const float *lse_part,
+mla_status_t mla_combine_lse(const mla_params_t *p, const void *o_part, const float *lse_part,
                              void *o_latent, float *lse_out, void *stream) {
     mla_status_t s = check(p);
     if (s != MLA_OK) return s;
@@ -261,7 +262,7 @@ mla_status_t mla_up_v(const mla_params_t *p, const void *o_latent, const void *W
     return hip_status(mla::launch_up_v_generic(*p, o_latent, W_UV, out, st), "mla_up_v launch");
 }
 
-mla_status_t mla_combine_up_v(const mla_params_t *p, const float *o_part, const float *lse_part, const void *W_UV,
+mla_status_t mla_combine_up_v(const mla_params_t *p, const void *o_part, const float *lse_part, const void *W_UV,
                               void *out, float *lse_out, void *stream) {
     mla_status_t s = check(p);
     if (s != MLA_OK) return s;
@@ -368,7 +369,7 @@ mla_status_t run_step(const mla_params_t *p, const void *q_nope, const void *q_r
     const StepLayout l = step_layout(*p);
     void *q_abs = ws + l.q_abs;
     float *lse_part = reinterpret_cast<float *>(ws + l.lse_part);
-    float *o_part = reinterpret_cast<float *>(ws + l.o_part);
+    void *o_part = ws + l.o_part;
     mla_status_t s = mla_absorb_q(p, q_nope, W_UK, q_abs, stream);
     if (s != MLA_OK) return s;
     s = mla_decode_splitkv(p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, o_part, lse_part, stream);

@@ -16,10 +16,10 @@ hipError_t launch_absorb_generic(const mla_params_t &p, const void *q_nope, cons
 hipError_t launch_decode_generic(const mla_params_t &p, const void *q_abs, const void *q_rope,
                                  const void *c_kv, const void *k_pe, const float *kv_scale,
                                  const int32_t *block_table, const int32_t *seq_lens,
-                                 float *o_part, float *lse_part, hipStream_t stream);
+                                 void *o_part, float *lse_part, hipStream_t stream);
 hipError_t launch_up_v_generic(const mla_params_t &p, const void *o_latent, const void *W_UV,
                                void *out, hipStream_t stream);
-hipError_t launch_combine(const mla_params_t &p, const float *o_part, const float *lse_part,
+hipError_t launch_combine(const mla_params_t &p, const void *o_part, const float *lse_part,
                           void *o_latent, float *lse_out, hipStream_t stream);
 
 // kernels for the DeepSeek-V3 head shapes (kernels_mfma.hip, kernels_decode.hip: both cache
@@ -28,11 +28,11 @@ bool decode_mfma_supported(const mla_params_t &p);
 hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const void *q_rope,
                               const void *c_kv, const void *k_pe, const float *kv_scale,
                               const int32_t *block_table, const int32_t *seq_lens,
-                              float *o_part, float *lse_part, hipStream_t stream);
+                              void *o_part, float *lse_part, hipStream_t stream);
 // bf16 cache: eight-wave attention kernel (kernels_decode8.hip)
 bool decode8_supported(const mla_params_t &p);
 hipError_t launch_decode8(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                          const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                          const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                           float *lse_part, hipStream_t stream);
 bool absorb_mfma_supported(const mla_params_t &p);
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
@@ -42,9 +42,9 @@ bool combine_fast_supported(const mla_params_t &p);
 bool combine_up_v_supported(const mla_params_t &p);
 hipError_t launch_expand(const mla_params_t &p, const void *c_kv, const float *kv_scale, void *c_out,
                          hipStream_t stream);
-hipError_t launch_combine_up_v(const mla_params_t &p, const float *o_part, const float *lse_part, const void *W_UV,
+hipError_t launch_combine_up_v(const mla_params_t &p, const void *o_part, const float *lse_part, const void *W_UV,
                                void *out, float *lse_out, hipStream_t stream);
-hipError_t launch_combine_fast(const mla_params_t &p, const float *o_part, const float *lse_part,
+hipError_t launch_combine_fast(const mla_params_t &p, const void *o_part, const float *lse_part,
                                void *o_latent, float *lse_out, hipStream_t stream);
 hipError_t launch_up_v_mfma(const mla_params_t &p, const void *o_latent, const void *W_UV,
                             void *out, hipStream_t stream);
@@ -74,7 +74,7 @@ constexpr int kDecodeRowsPerBlock = 64;
 constexpr int kDecodeRowsPerGroup = 128;
 bool decode128_supported(const mla_params_t &p);
 hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, float *o_part,
+                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                             float *lse_part, hipStream_t stream);
 // Balanced parts are cut in units of work: a sequence with n > 0 pages costs
 // kSeqStartCost + n units, its start cost first, then one unit per page; an empty

@@ -48,7 +48,7 @@ class Params(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("pe_dtype", ctypes.c_int32),
                 ("latent_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("num_parts", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("num_parts", ctypes.c_int32), ("part_dtype", ctypes.c_int32)]
 
     def copy(self) -> "Params":
         q = Params()
@@ -107,7 +107,7 @@ def lib():
         L.mla_decode_step_workspace.restype = ctypes.c_int64
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = ctypes.c_int32
-        if L.mla_abi_version() != 2:
+        if L.mla_abi_version() != 3:
             raise RuntimeError("libmla.so ABI version mismatch")
         _lib = L
     return _lib
@@ -132,13 +132,13 @@ def make_params(B: int, Sq: int, H: int, d_h: int, d_c: int, d_r: int, num_pages
                 max_pages: int, num_splits: int = 1, split_pages: Optional[int] = None,
                 scale: Optional[float] = None, q_dtype: int = BF16, w_dtype: int = BF16,
                 kv_dtype: int = BF16, pe_dtype: int = BF16, latent_dtype: int = BF16,
-                out_dtype: int = F32, flags: int = 0, num_parts: int = 0) -> Params:
+                out_dtype: int = F32, flags: int = 0, num_parts: int = 0, part_dtype: int = F32) -> Params:
     if split_pages is None:
         split_pages = -(-max_pages // num_splits)
     if scale is None:
         scale = 1.0 / math.sqrt(d_h + d_r)
     return Params(B, Sq, H, d_h, d_c, d_r, PAGE, num_pages, max_pages, num_splits, split_pages,
-                  scale, q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype, flags, num_parts)
+                  scale, q_dtype, w_dtype, kv_dtype, pe_dtype, latent_dtype, out_dtype, flags, num_parts, part_dtype)
 
 
 def check_params(p: Params) -> None:
@@ -201,7 +201,7 @@ def decode_splitkv(p: Params, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, 
         _ptr(kv_scale, "kv_scale", (p.num_pages, PAGE), F32),
         _ptr(block_table, "block_table", (p.B, p.max_pages)),
         _ptr(seq_lens, "seq_lens", (p.B,)),
-        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
         _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
         _stream(stream)))
 
@@ -209,7 +209,7 @@ def decode_splitkv(p: Params, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, 
 def combine_lse(p: Params, o_part, lse_part, o_latent, lse_out=None, stream=None) -> None:
     rows = (p.B, p.Sq, p.H)
     _check(lib().mla_combine_lse(ctypes.byref(p),
-                                 _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                 _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
                                  _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
                                  _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
                                  _ptr(lse_out, "lse_out", rows, F32),
@@ -240,7 +240,7 @@ def combine_up_v(p: Params, o_part, lse_part, W_UV, out, lse_out=None, stream=No
     rows = (p.B, p.Sq, p.H)
     _check(lib().mla_combine_up_v(
         ctypes.byref(p),
-        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+        _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
         _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
         _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
         _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
@@ -425,16 +425,16 @@ class BoundCalls:
                                     _ptr(kv_scale if expand is None else None, "kv_scale", (p.num_pages, PAGE), F32),
                                     _ptr(block_table, "block_table", (p.B, p.max_pages)),
                                     _ptr(seq_lens, "seq_lens", (p.B,)),
-                                    _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+                                    _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
                                     _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32), st)),
-            (L.mla_combine_lse, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+            (L.mla_combine_lse, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
                                  _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
                                  _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
                                  _ptr(lse, "lse_out", rows, F32), st)),
             (L.mla_up_v, (pp, _ptr(o_latent, "o_latent", rows + (p.d_c,), p.latent_dtype),
                           _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
                           _ptr(out, "out", rows + (p.d_h,), p.out_dtype), st)),
-            (L.mla_combine_up_v, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), F32),
+            (L.mla_combine_up_v, (pp, _ptr(o_part, "o_part", rows + (p.num_splits, p.d_c), p.part_dtype),
                                   _ptr(lse_part, "lse_part", rows + (p.num_splits,), F32),
                                   _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
                                   _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
@@ -497,7 +497,7 @@ class DecodeStep:
             self.kv_bf16 = torch.empty((p.num_pages, PAGE, p.d_c), dtype=torch.bfloat16, device=device)
         rows = (p.B, p.Sq, p.H)
         self.q_abs = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
-        self.o_part = torch.empty(rows + (p.num_splits, p.d_c), dtype=torch.float32, device=device)
+        self.o_part = torch.empty(rows + (p.num_splits, p.d_c), dtype=_TORCH[p.part_dtype], device=device)
         self.lse_part = torch.empty(rows + (p.num_splits,), dtype=torch.float32, device=device)
         self.o_latent = torch.empty(rows + (p.d_c,), dtype=_TORCH[p.latent_dtype], device=device)
         self.lse = torch.empty(rows, dtype=torch.float32, device=device)

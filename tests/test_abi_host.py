@@ -34,8 +34,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_layout_matches_header():
-    # 18 int32/float fields, one uint32 flags field, num_parts; no padding
-    assert ctypes.sizeof(mla.Params) == 20 * 4
+    # 18 int32/float fields, one uint32 flags field, num_parts, part_dtype; no padding
+    assert ctypes.sizeof(mla.Params) == 21 * 4
 
 
 def v3(**kw):
@@ -56,7 +56,7 @@ def test_valid_params_pass():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("B", 0, 2), ("Sq", 0, 2), ("Sq", 257, 2), ("H", 0, 2), ("d_h", 0, 2), ("d_c", 2048, 2),
+    ("B", 0, 2), ("Sq", 0, 2), ("Sq", 257, 2), ("part_dtype", 2, 3), ("part_dtype", -1, 3), ("H", 0, 2), ("d_h", 0, 2), ("d_c", 2048, 2),
     ("d_r", -1, 2), ("page_size", 32, 2), ("num_pages", 0, 2), ("max_pages", 0, 2),
     ("num_splits", 0, 4), ("num_splits", 5000, 4), ("split_pages", 0, 4), ("scale", 0.0, 2),
     ("scale", float("inf"), 2), ("q_dtype", 2, 3), ("w_dtype", 7, 3), ("kv_dtype", 3, 3),
@@ -270,6 +270,8 @@ def test_decode_step_workspace_layout():
     q = v3(B=3, Sq=2, num_splits=5, latent_dtype=mla.F32)       # two-launch tail
     assert mla.decode_step_workspace(q) == a(rows * 512 * 4) + a(rows * 5 * 4) + a(rows * 5 * 512 * 4) + a(rows * 512 * 4)
     assert mla.lib().mla_decode_step_workspace(None) == -1
+    b = v3(B=3, Sq=2, num_splits=5, part_dtype=mla.BF16)       # bf16 partials: half the bytes
+    assert mla.decode_step_workspace(b) == a(rows * 512 * 2) + a(rows * 5 * 4) + a(rows * 5 * 512 * 2)
 
 
 def test_decode_step_validates_on_the_host():

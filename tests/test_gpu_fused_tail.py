@@ -21,18 +21,22 @@ def note(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("B,Sq,S,out_dtype,with_lse", [
-    (64, 1, 3, mla.F32, True),       # two 32-row chunks per head
-    (37, 4, 7, mla.BF16, True),      # 148 rows: a ragged last chunk
-    (5, 1, 70, mla.F32, False),      # more splits than lanes
-    (1, 1, 1, mla.F32, True),        # one row, one split
+@pytest.mark.parametrize("B,Sq,S,out_dtype,with_lse,part", [
+    (64, 1, 3, mla.F32, True, mla.F32),       # two 32-row chunks per head
+    (37, 4, 7, mla.BF16, True, mla.F32),      # 148 rows: a ragged last chunk
+    (5, 1, 70, mla.F32, False, mla.F32),      # more splits than lanes
+    (1, 1, 1, mla.F32, True, mla.F32),        # one row, one split
+    (64, 1, 3, mla.F32, True, mla.BF16),      # bf16 partials
+    (37, 4, 70, mla.F32, True, mla.BF16),
 ])
-def test_combine_up_v_equals_two_calls(B, Sq, S, out_dtype, with_lse):
+def test_combine_up_v_equals_two_calls(B, Sq, S, out_dtype, with_lse, part):
     wl = I.workload("v3_b64", B=B, Sq=Sq)
     o, l = I.random_partials(wl, S, seed=11)
+    if part == mla.BF16:
+        o = o.bfloat16()
     W_UV = I.make_case(I.workload("v3_b64", B=1), seq_lens=[64]).W_UV
     p = mla.make_params(B, Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, 1, S, num_splits=S, split_pages=1,
-                        out_dtype=out_dtype)
+                        out_dtype=out_dtype, part_dtype=part)
     td = torch.float32 if out_dtype == mla.F32 else torch.bfloat16
     od, ld, wd = o.cuda(), l.cuda(), W_UV.cuda()
     ol = torch.empty((B, Sq, wl.H, wl.d_c), dtype=torch.bfloat16, device="cuda")
@@ -40,7 +44,7 @@ def test_combine_up_v_equals_two_calls(B, Sq, S, out_dtype, with_lse):
     lse_ref = torch.empty((B, Sq, wl.H), device="cuda")
     out = torch.full_like(out_ref, 7.0)
     lse = torch.full_like(lse_ref, 7.0) if with_lse else None
-    note(f"combine_up_v B={B} Sq={Sq} S={S} out={out_dtype} lse={with_lse}")
+    note(f"combine_up_v B={B} Sq={Sq} S={S} out={out_dtype} lse={with_lse} part={part}")
     mla.combine_lse(p, od, ld, ol, lse_ref)
     mla.up_v(p, ol, wd, out_ref)
     mla.combine_up_v(p, od, ld, wd, out, lse)

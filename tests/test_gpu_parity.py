@@ -73,7 +73,8 @@ def run_decode(case, p):
     q_abs = I.random_q_abs(case.wl, seed=123)
     S = p.num_splits
     rows = (case.wl.B, case.wl.Sq, case.wl.H)
-    o_part = torch.full(rows + (S, case.wl.d_c), float("nan"), device="cuda")
+    pdt = torch.bfloat16 if p.part_dtype == mla.BF16 else torch.float32
+    o_part = torch.full(rows + (S, case.wl.d_c), float("nan"), dtype=pdt, device="cuda")
     lse_part = torch.full(rows + (S,), float("nan"), device="cuda")
     mla.decode_splitkv(p, q_abs.cuda(), dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table,
                        dc.seq_lens, o_part, lse_part)
@@ -81,7 +82,7 @@ def run_decode(case, p):
     beg, end = split_page_ranges(case.seq_lens.numpy(), p)
     ref_o, ref_l = O.decode_page_ranges(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
                                         case.k_pe, case.block_table, case.seq_lens, beg, end)
-    return o_part.cpu().numpy(), lse_part.cpu().numpy(), ref_o, ref_l
+    return o_part.float().cpu().numpy(), lse_part.cpu().numpy(), ref_o, ref_l
 
 
 def check_partials(wl, o, l, ref_o, ref_l):
@@ -141,18 +142,48 @@ def test_decode_balanced_splits(wl_name, lens, num_parts, extra_slots, flags):
     check_partials(wl, o, l, ref_o, ref_l)
 
 
-@pytest.mark.parametrize("wl_name,S", [("v3_b64", 7), ("tiny", 3), ("v3_sq4_fp8", 40)])
-def test_combine_lse(wl_name, S):
+@pytest.mark.parametrize("wl_name,over,lens,num_parts,flags", [
+    ("v3_b64", {}, [1, 63, 64, 65, 200, 700], 5, 0),                  # four-wave kernel, 128 rows
+    ("v3_b64", {"H": 64}, [1, 63, 64, 65, 200, 700], 5, 0),           # eight-wave kernel, 64 rows
+    ("v3_sq4_fp8", {}, [4, 129, 700, 0], 3, 0),                        # e4m3 cache
+    ("v3_b64", {}, [130, 5, 1000], 2, mla.FLAG_GENERIC),              # fp32 VALU kernel
+])
+def test_decode_bf16_partials(wl_name, over, lens, num_parts, flags):
+    """part_dtype = BF16: the partials are the fp32 partials (checked against the
+    oracle) rounded to nearest even, bit for bit, with the same lse values.  (Rounded
+    partials are not held to the max-error bound itself: a split of a few tokens
+    has values ~10x the RMS of all partials, where bf16's half ulp alone is 2%.)"""
+    wl = I.workload(wl_name, B=len(lens), **over)
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, num_parts=num_parts, flags=flags)
+    note(f"bf16 partials {wl_name} {over} lens={lens} P={num_parts} kernel={mla.decode_kernel_name(p)}")
+    o32, l32, ref_o, ref_l = run_decode(case, p)
+    pb = p.copy()
+    pb.part_dtype = mla.BF16
+    o16, l16, _, _ = run_decode(case, pb)
+    check_partials(wl, o32, l32, ref_o, ref_l)
+    assert np.array_equal(l16, l32)
+    full = ref_l != -np.inf
+    want = torch.from_numpy(o32[full]).bfloat16().float().numpy()
+    assert np.array_equal(o16[full], want)
+
+
+@pytest.mark.parametrize("wl_name,S,part", [("v3_b64", 7, mla.F32), ("tiny", 3, mla.F32), ("v3_sq4_fp8", 40, mla.F32),
+                                             ("v3_b64", 7, mla.BF16), ("tiny", 3, mla.BF16), ("v3_b64", 70, mla.BF16)])
+def test_combine_lse(wl_name, S, part):
     wl = I.workload(wl_name, B=3)
     o, l = I.random_partials(wl, S, seed=9)
+    if part == mla.BF16:
+        o = o.bfloat16()
     D = O.dims(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, S, wl.scale)
     ref_o, ref_l = O.combine_lse(D, o, l)
     latent = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, 1, S, num_splits=S,
-                        split_pages=1, latent_dtype=mla.dtype_code(latent))
+                        split_pages=1, latent_dtype=mla.dtype_code(latent), part_dtype=part)
     ol = torch.empty((wl.B, wl.Sq, wl.H, wl.d_c), dtype=latent, device="cuda")
     lse = torch.empty((wl.B, wl.Sq, wl.H), device="cuda")
-    note(f"combine {wl_name} S={S}")
+    note(f"combine {wl_name} S={S} part={part}")
     mla.combine_lse(p, o.cuda(), l.cuda(), ol, lse)
     torch.cuda.synchronize()
     e = err_rms(ol.float().cpu().numpy(), ref_o)
