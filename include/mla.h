@@ -58,6 +58,12 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 6  /* a valid request no kernel here implements */
 } mla_status_t;
 
+/* Bits of the device error word (mla_device_errors). */
+#define MLA_DEVERR_SPLITS 1u  /* a sequence had pages in more parts than num_splits (stale plan): pages skipped */
+#define MLA_DEVERR_SYNC 2u    /* a bounded wait between the waves of a workgroup gave up */
+#define MLA_DEVERR_PAGE 4u    /* (MLA_DEBUG_BOUNDS build) block_table entry outside [0, num_pages) */
+#define MLA_DEVERR_SEQLEN 8u  /* (MLA_DEBUG_BOUNDS build) seq_lens entry outside [0, max_pages * 64] */
+
 /* Flags (mla_params_t.flags). */
 #define MLA_FLAG_GENERIC 1u  /* use the fp32 VALU kernels even where MFMA kernels apply */
 
@@ -422,6 +428,21 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
  * a NULL or invalid p or max_seq_len < 1.
  */
 int32_t mla_default_num_splits(const mla_params_t *p, int32_t max_seq_len);
+
+/*
+ * mla_device_errors -- synchronises `stream`, then returns in *bits the OR of the
+ * MLA_DEVERR_* bits the attention kernels of this process raised on the current
+ * device since the previous call, and clears them.  The kernels never stop or
+ * fault on these conditions: a stale plan's extra pages are skipped (their rows'
+ * results are then wrong), a wait that gives up continues with the data at hand,
+ * and (MLA_DEBUG_BOUNDS build, libmla_debug.so) an out-of-range page or length is
+ * replaced by page 0 or clamped.  The one entry point that synchronises.
+ * Returns MLA_OK, MLA_ERR_NULL or MLA_ERR_HIP.
+ */
+mla_status_t mla_device_errors(uint32_t *bits, void *stream);
+
+/* 1 when this library was built with the MLA_DEBUG_BOUNDS device checks, else 0. */
+int32_t mla_debug_bounds(void);
 
 /* Name of the kernel family mla_decode_splitkv would use for *p:
  * "mfma_bf16", "mfma_fp8" or "generic_f32" (host-only). */

@@ -1,4 +1,5 @@
-"""Build libmla.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+"""Build libmla.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc, and
+libmla_debug.so, the same sources with the MLA_DEBUG_BOUNDS device checks.
 
     python -m mla_latent_kv_05_amd.build
 """
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
+DEBUG_LIB = os.path.join(PKG, "libmla_debug.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["mla_api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
            "kernels_decode8.hip", "kernels_decode128.hip", "kernels_append.hip", "kernels_prefill.hip", "kernels_expand.hip"]
@@ -27,27 +29,35 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool) -> str:
+    obj = os.path.join(OBJDIR, ("debug_" if debug else "") + os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + (["-DMLA_DEBUG_BOUNDS"] if debug else []) + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                                       "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = [(src, dbg) for dbg in (False, True) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

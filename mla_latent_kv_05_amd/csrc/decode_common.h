@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "dev_errors.h"
 #include "gfx950.h"
 #include "mla_internal.h"
 
@@ -177,7 +178,7 @@ __device__ __forceinline__ void for_each_segment(const mla_params_t &p, const in
     if (p.num_parts == 0) {                            // fixed splits: part = b * S + c
         const int b = part / p.num_splits;
         const int c = part % p.num_splits;
-        const int pages = (seq_lens[b] + kPage - 1) / kPage;
+        const int pages = seq_pages(p, seq_lens[b]);
         const int pa = c * p.split_pages;
         const int pb = min(pa + p.split_pages, pages);
         if (pa < pb) f(Segment{b, c, pa, pb, false});
@@ -189,13 +190,13 @@ __device__ __forceinline__ void for_each_segment(const mla_params_t &p, const in
     int64_t T = 0;                                     // units of the whole batch
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
-        T += wave_sum(b < p.B ? cost((seq_lens[b] + kPage - 1) / kPage) : 0);
+        T += wave_sum(b < p.B ? cost(seq_pages(p, seq_lens[b])) : 0);
     }
     const int64_t pg0 = part * T / P, pg1 = (part + 1) * T / P;   // this part's units
     int64_t base = 0;                                  // units before sequence b0
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int b = b0 + lane;
-        const int pages = b < p.B ? (seq_lens[b] + kPage - 1) / kPage : 0;
+        const int pages = b < p.B ? seq_pages(p, seq_lens[b]) : 0;
         const int units = cost(pages);
         const int incl = wave_inclusive_scan(units);
         const int chunk = __builtin_amdgcn_readlane(incl, 63);

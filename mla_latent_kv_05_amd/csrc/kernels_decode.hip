@@ -309,7 +309,7 @@ __device__ __forceinline__ void attend_segment(
     const int n_pages = __builtin_amdgcn_readfirstlane(seg.pb - seg.pa);
     const int32_t *seg_bt = bt + __builtin_amdgcn_readfirstlane(seg.pa);
     int pl_base = 0;
-    int plist = seg_bt[min(lane, n_pages - 1)];
+    int plist = checked_page(p, seg_bt[min(lane, n_pages - 1)]);
     // Consume the loads here: otherwise the compiler places their vmcnt
     // waits at the first use inside the tile loop, where (re-executed every
     // iteration) they would also wait for the tile copies in flight.
@@ -362,6 +362,7 @@ __device__ __forceinline__ void attend_segment(
             pl_base = k & ~63;
             const int32_t *src = seg_bt + min(pl_base + lane, n_pages - 1);
             asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(plist) : "v"(src) : "memory");
+            plist = checked_page(p, plist);
         }
         return __builtin_amdgcn_readlane(plist, k - pl_base);
     };
@@ -695,12 +696,14 @@ __device__ __forceinline__ void decode_wave(
     auto run = [&](const Segment &seg) {
         if (seg.pa >= seg.pb) {                        // an empty part inside the sequence's range
             if (seg.c < S) fill(seg.b, seg.c, seg.c + 1);
-        } else if (seg.c < S) {                        // else: num_splits too small (precondition)
+        } else if (seg.c < S) {
             if (!first) barrier_lds();                 // the previous segment's LDS reads are done
             first = false;
             attend_segment<kFp8, KH>(smem, p, q_abs, q_rope, c_kv, k_pe, kv_scale,
                                      block_table + static_cast<int64_t>(seg.b) * p.max_pages,
                                      seq_lens[seg.b], seg, rg, o_part, lse_part);
+        } else if (threadIdx.x == 0) {
+            raise_error(MLA_DEVERR_SPLITS);            // num_splits below the plan's bound
         }
         if (seg.last) fill(seg.b, seg.c + 1, S);       // slots after the last split carry no weight
     };
@@ -758,5 +761,7 @@ hipError_t launch_decode_mfma(const mla_params_t &p, const void *q_abs, const vo
                        p, qa, qr, c_kv, kp, kv_scale, block_table, seq_lens, o_part, lse_part);
     return hipGetLastError();
 }
+
+hipError_t take_errors_decode_mfma(uint32_t *bits) { return take_unit_errors(bits); }
 
 }  // namespace mla

@@ -158,7 +158,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     // ---- copies: latent rows 8w .. 8w+7 and RoPE rows 8w .. 8w+7 of a tile
     // page list of the segment: lanes hold pages pl_base .. pl_base + 63
     int pl_base = 0;
-    int plist = seg_bt[min(lane, n_pages - 1)];
+    int plist = checked_page(p, seg_bt[min(lane, n_pages - 1)]);
     asm volatile("" : "+v"(plist));
     auto tile_page = [&](int t) -> int64_t {
         if ((t >> 1) - pl_base >= 64) {
@@ -167,6 +167,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
             pl_base = t >> 1;
             const int32_t *src = seg_bt + min(pl_base + lane, n_pages - 1);
             asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(plist) : "v"(src) : "memory");
+            plist = checked_page(p, plist);
         }
         return __builtin_amdgcn_readlane(plist, (t >> 1) - pl_base);
     };
@@ -505,7 +506,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
         // maximum as the reference
         m_ref = m_all;
         pl_base = 0;
-        plist = seg_bt[min(lane, n_pages - 1)];
+        plist = checked_page(p, seg_bt[min(lane, n_pages - 1)]);
         wait_vmcnt<0>();
         barrier_lds();
     }
@@ -590,13 +591,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
     auto run = [&](const Segment &seg) {
         if (seg.pa >= seg.pb) {                        // an empty part inside the sequence's range
             if (seg.c < S) fill(seg.b, seg.c, seg.c + 1);
-        } else if (seg.c < S) {                        // else: num_splits too small (precondition)
+        } else if (seg.c < S) {
             if (!first) barrier_lds();                 // the previous segment's LDS reads are done
             first = false;
             wait_vmcnt<0>();                           // its stores too (the copy waits count from here)
             attend_segment(smem, p, q_abs, q_rope, c_kv, k_pe,
                            block_table + static_cast<int64_t>(seg.b) * p.max_pages + seg.pa, seg,
                            seq_lens[seg.b], rg, o_part, lse_part);
+        } else if (threadIdx.x == 0) {
+            raise_error(MLA_DEVERR_SPLITS);            // num_splits below the plan's bound
         }
         if (seg.last) fill(seg.b, seg.c + 1, S);       // slots after the last split carry no weight
     };
@@ -623,5 +626,7 @@ hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void
                        o_part, lse_part);
     return hipGetLastError();
 }
+
+hipError_t take_errors_decode128(uint32_t *bits) { return take_unit_errors(bits); }
 
 }  // namespace mla

@@ -233,12 +233,14 @@ __device__ __forceinline__ void score_role(char *smem, const mla_params_t &p, co
         asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(sm + kOffFlag + s * 4), "v"(gen) : "memory");
         // wait for the other half's partial of this tile (bounded: the partner always
         // publishes, the bound only keeps a wave from spinning forever)
-        for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+        uint32_t spin = 0;
+        for (; spin < kSpinLimit; ++spin) {
             uint32_t f;
             asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(sm + kOffFlag + (s ^ 1) * 4) : "memory");
             if (__builtin_amdgcn_readfirstlane(f) == gen) break;
             __builtin_amdgcn_s_sleep(1);
         }
+        if (spin == kSpinLimit && lane == 0) raise_error(MLA_DEVERR_SYNC);   // gave up: flagged, never a hang
         // both partials of the owned heads, in the owner layout
         const u32x4 x0 = ld128(pr_addr), x1 = ld128(pr_addr + 1024);
         const u32x4 y0 = ld128(pr_addr + kPartWave), y1 = ld128(pr_addr + kPartWave + 1024);
@@ -318,7 +320,7 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
     const int n_pages = __builtin_amdgcn_readfirstlane(seg.pb - seg.pa);
     const int32_t *seg_bt = bt + __builtin_amdgcn_readfirstlane(seg.pa);
     int pl_base = 0;                                   // pages pl_base .. pl_base+63 of the segment, one per lane
-    int plist = seg_bt[min(lane, n_pages - 1)];
+    int plist = checked_page(p, seg_bt[min(lane, n_pages - 1)]);
     asm volatile("" : "+v"(plist));
 
     const uint32_t sm = lds_addr(smem);
@@ -369,6 +371,7 @@ __device__ __forceinline__ void latent_role(char *smem, const mla_params_t &p, c
             pl_base = t >> 1;
             const int32_t *src = seg_bt + min(pl_base + lane, n_pages - 1);
             asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(plist) : "v"(src) : "memory");
+            plist = checked_page(p, plist);
         }
         const int64_t phys = real ? page_of(t) : 0;
         const int64_t crow0 = phys * kPage + (t & 1) * kTile;   // first cache row of the tile
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void decode8_kernel(
     auto run = [&](const Segment &seg) {
         if (seg.pa >= seg.pb) {                        // an empty part inside the sequence's range
             if (seg.c < S) fill(seg.b, seg.c, seg.c + 1);
-        } else if (seg.c < S) {                        // else: num_splits too small (precondition)
+        } else if (seg.c < S) {
             if (!first) barrier_lds();                 // the previous segment's LDS traffic is done
             first = false;
             const SegInfo si = seg_info(p, seg, rg, seq_lens[seg.b]);
@@ -526,6 +529,8 @@ __global__ __launch_bounds__(kThreads) void decode8_kernel(
                 score_role<1>(smem, p, q_abs, q_rope, seg, si, rg, lse_part, gen);
             else
                 score_role<0>(smem, p, q_abs, q_rope, seg, si, rg, lse_part, gen);
+        } else if (threadIdx.x == 0) {
+            raise_error(MLA_DEVERR_SPLITS);            // num_splits below the plan's bound
         }
         if (seg.last) fill(seg.b, seg.c + 1, S);       // slots after the last split carry no weight
     };
@@ -550,5 +555,7 @@ hipError_t launch_decode8(const mla_params_t &p, const void *q_abs, const void *
                        o_part, lse_part);
     return hipGetLastError();
 }
+
+hipError_t take_errors_decode8(uint32_t *bits) { return take_unit_errors(bits); }
 
 }  // namespace mla

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "dev_errors.h"
 #include "dtype.h"
 #include "mla_internal.h"
 
@@ -60,7 +61,7 @@ __device__ __forceinline__ int64_t block_reduce_sum_i64(int64_t v, int64_t *red)
 // being the part that holds b's first page.
 __device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict__ seq_lens, int b, int c,
                                int64_t *pa, int64_t *pb, int64_t *red) {
-    const int64_t pages = (seq_lens[b] + p.page_size - 1) / p.page_size;
+    const int64_t pages = seq_pages(p, seq_lens[b]);
     if (p.num_parts == 0) {
         *pa = static_cast<int64_t>(c) * p.split_pages;
         *pb = *pa + p.split_pages;
@@ -69,7 +70,7 @@ __device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict_
     }
     int64_t tot = 0, before = 0;
     for (int i = threadIdx.x; i < p.B; i += kThreads) {
-        const int64_t n = (seq_lens[i] + p.page_size - 1) / p.page_size;
+        const int64_t n = seq_pages(p, seq_lens[i]);
         const int64_t units = n > 0 ? n + kSeqStartCost : 0;
         tot += units;
         if (i < b) before += units;
@@ -80,7 +81,10 @@ __device__ void split_pages_of(const mla_params_t &p, const int32_t *__restrict_
     *pb = 0;
     if (pages == 0) return;
     const int64_t P = p.num_parts;
-    const int64_t j = ((off + 1) * P - 1) / T + c;      // part holding b's first page, plus c
+    const int64_t j0 = ((off + 1) * P - 1) / T;           // part holding b's first page
+    if (c == p.num_splits - 1 && threadIdx.x == 0 && ((off + pages) * P - 1) / T - j0 >= p.num_splits)
+        raise_error(MLA_DEVERR_SPLITS);                   // pages in more parts than num_splits
+    const int64_t j = j0 + c;
     if (j >= P) return;
     const int64_t lo = j * T / P - off, hi = (j + 1) * T / P - off;
     *pa = lo > 0 ? lo : 0;
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
         float z = -INFINITY;
         int64_t crow = 0;
         if (t < t1) {
-            crow = static_cast<int64_t>(bt[t / p.page_size]) * p.page_size + t % p.page_size;
+            crow = static_cast<int64_t>(checked_page(p, bt[t / p.page_size])) * p.page_size + t % p.page_size;
             float content = 0.f, rope = 0.f;
             for (int m = 0; m < p.d_c; ++m) content += qa[m] * load_elem(c_kv, p.kv_dtype, crow * p.d_c + m);
             if (p.kv_dtype == MLA_FP8_E4M3) content *= kv_scale[crow];
@@ -284,5 +288,7 @@ hipError_t launch_combine(const mla_params_t &p, const void *o_part, const float
                        p, o_part, lse_part, o_latent, lse_out);
     return hipGetLastError();
 }
+
+hipError_t take_errors_generic(uint32_t *bits) { return take_unit_errors(bits); }
 
 }  // namespace mla

@@ -352,6 +352,25 @@ mla_status_t mla_prefill_attention(const mla_params_t *p, const void *q_nope, co
                       "mla_prefill_attention launch");
 }
 
+mla_status_t mla_device_errors(uint32_t *bits, void *stream) {
+    if (!bits) return fail(MLA_ERR_NULL, "mla_device_errors: bits is NULL");
+    *bits = 0;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = mla::take_errors_generic(bits);
+    if (e == hipSuccess) e = mla::take_errors_decode_mfma(bits);
+    if (e == hipSuccess) e = mla::take_errors_decode8(bits);
+    if (e == hipSuccess) e = mla::take_errors_decode128(bits);
+    return hip_status(e, "mla_device_errors");
+}
+
+int32_t mla_debug_bounds(void) {
+#ifdef MLA_DEBUG_BOUNDS
+    return 1;
+#else
+    return 0;
+#endif
+}
+
 int64_t mla_decode_step_workspace(const mla_params_t *p) {
     if (check(p) != MLA_OK) return -1;
     return step_layout(*p).bytes;

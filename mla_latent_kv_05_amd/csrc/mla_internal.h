@@ -82,6 +82,11 @@ hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void
 // num_parts equal parts, so a part that also starts a sequence (one more segment:
 // its query loads, its first copies and its partial output) streams fewer pages.
 constexpr int kSeqStartCost = 6;
+// each attention unit's device error word: OR it into *bits, then clear it
+hipError_t take_errors_generic(uint32_t *bits);
+hipError_t take_errors_decode_mfma(uint32_t *bits);
+hipError_t take_errors_decode8(uint32_t *bits);
+hipError_t take_errors_decode128(uint32_t *bits);
 // query rows per attention workgroup for the kernel mla_decode_splitkv picks
 int decode_rows_per_workgroup(const mla_params_t &p);
 

@@ -16,6 +16,7 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla.so")
+DEBUG_LIB_PATH = os.path.join(PKG, "libmla_debug.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 FLAG_GENERIC = 1
@@ -28,6 +29,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
            "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax", "mla_expand_kv",
            "mla_decode_step", "mla_decode_step_workspace", "mla_decode_step_noalloc",
+           "mla_device_errors", "mla_debug_bounds",
            "mla_check_params", "mla_plan_splits", "mla_default_num_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
 
@@ -60,57 +62,75 @@ class Params(ctypes.Structure):
 
 
 _lib = None
+_debug_lib = None
 
 
 def lib():
     """Load libmla.so once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "or python -m mla_latent_kv_05_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        PP = ctypes.POINTER(Params)
-        st = ctypes.c_int
-        for name, args in (
-            ("mla_absorb_q", [PP, P, P, P, P]),
-            ("mla_decode_splitkv", [PP, P, P, P, P, P, P, P, P, P, P]),
-            ("mla_combine_lse", [PP, P, P, P, P, P]),
-            ("mla_up_v", [PP, P, P, P, P]),
-            ("mla_combine_up_v", [PP, P, P, P, P, P, P]),
-            ("mla_expand_kv", [PP, P, P, P, P]),
-            ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
-            ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
-            ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
-            ("mla_decode_step", [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]),
-            ("mla_decode_step_noalloc", [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
-            ("mla_check_params", [PP]),
-            ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
-        ):
-            f = getattr(L, name)
-            f.argtypes = args
-            f.restype = st
-        L.mla_decode_kernel_name.argtypes = [PP]
-        L.mla_decode_kernel_name.restype = ctypes.c_char_p
-        L.mla_status_string.argtypes = [st]
-        L.mla_status_string.restype = ctypes.c_char_p
-        L.mla_last_error.argtypes = []
-        L.mla_last_error.restype = ctypes.c_char_p
-        L.mla_prefill_lmax.argtypes = [PP]
-        L.mla_prefill_lmax.restype = ctypes.c_int64
-        L.mla_prefer_absorbed.argtypes = [PP]
-        L.mla_prefer_absorbed.restype = ctypes.c_int32
-        L.mla_default_num_splits.argtypes = [PP, ctypes.c_int32]
-        L.mla_default_num_splits.restype = ctypes.c_int32
-        L.mla_decode_step_workspace.argtypes = [PP]
-        L.mla_decode_step_workspace.restype = ctypes.c_int64
-        L.mla_abi_version.argtypes = []
-        L.mla_abi_version.restype = ctypes.c_int32
-        if L.mla_abi_version() != 3:
-            raise RuntimeError("libmla.so ABI version mismatch")
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def debug_lib():
+    """libmla_debug.so (built with the MLA_DEBUG_BOUNDS device checks), loaded once
+    beside libmla.so; the same C ABI."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "or python -m mla_latent_kv_05_amd.build")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(Params)
+    st = ctypes.c_int
+    for name, args in (
+        ("mla_absorb_q", [PP, P, P, P, P]),
+        ("mla_decode_splitkv", [PP, P, P, P, P, P, P, P, P, P, P]),
+        ("mla_combine_lse", [PP, P, P, P, P, P]),
+        ("mla_up_v", [PP, P, P, P, P]),
+        ("mla_combine_up_v", [PP, P, P, P, P, P, P]),
+        ("mla_expand_kv", [PP, P, P, P, P]),
+        ("mla_append_kv", [PP, P, P, P, P, P, P, P, P, P, P]),
+        ("mla_decompress_kv", [PP, P, P, P, P, P, P, P, P]),
+        ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
+        ("mla_decode_step", [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]),
+        ("mla_decode_step_noalloc", [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
+        ("mla_check_params", [PP]),
+        ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    ):
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = st
+    L.mla_decode_kernel_name.argtypes = [PP]
+    L.mla_decode_kernel_name.restype = ctypes.c_char_p
+    L.mla_status_string.argtypes = [st]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    L.mla_prefill_lmax.argtypes = [PP]
+    L.mla_prefill_lmax.restype = ctypes.c_int64
+    L.mla_prefer_absorbed.argtypes = [PP]
+    L.mla_prefer_absorbed.restype = ctypes.c_int32
+    L.mla_default_num_splits.argtypes = [PP, ctypes.c_int32]
+    L.mla_default_num_splits.restype = ctypes.c_int32
+    L.mla_decode_step_workspace.argtypes = [PP]
+    L.mla_decode_step_workspace.restype = ctypes.c_int64
+    L.mla_abi_version.argtypes = []
+    L.mla_abi_version.restype = ctypes.c_int32
+    L.mla_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), P]
+    L.mla_device_errors.restype = st
+    L.mla_debug_bounds.argtypes = []
+    L.mla_debug_bounds.restype = ctypes.c_int32
+    if L.mla_abi_version() != 3:
+        raise RuntimeError(f"{path}: ABI version mismatch")
+    return L
 
 
 def _check(status: int):
@@ -246,6 +266,20 @@ def combine_up_v(p: Params, o_part, lse_part, W_UV, out, lse_out=None, stream=No
         _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
         _ptr(lse_out, "lse_out", rows, F32),
         _stream(stream)))
+
+
+DEVERR = {1: "MLA_DEVERR_SPLITS", 2: "MLA_DEVERR_SYNC", 4: "MLA_DEVERR_PAGE", 8: "MLA_DEVERR_SEQLEN"}
+
+
+def device_errors(stream=None, L=None) -> int:
+    """Synchronise the stream and return (and clear) the device error bits the
+    attention kernels raised since the last call (0 = none)."""
+    L = lib() if L is None else L
+    bits = ctypes.c_uint32(0)
+    st = L.mla_device_errors(ctypes.byref(bits), _stream(stream))
+    if st != 0:
+        raise MLAError(st, L.mla_last_error().decode())
+    return int(bits.value)
 
 
 def decode_step_workspace(p: Params) -> int:

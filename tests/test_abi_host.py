@@ -298,3 +298,15 @@ def test_decode_step_noalloc_rejects_large_steps_on_the_host():
     assert L.mla_decode_step_noalloc(ctypes.byref(big), *([d] * 10), None, None) == 2
     assert "static scratch" in L.mla_last_error().decode()
     assert L.mla_decode_step_noalloc(ctypes.byref(v3()), None, *([d] * 9), None, None) == 1
+
+
+def test_debug_build_and_error_word_entry_points():
+    """Both libraries load with the same ABI; only libmla_debug.so has the device
+    bounds checks; mla_device_errors rejects a NULL result pointer on the host."""
+    assert mla.lib().mla_debug_bounds() == 0
+    D = mla.debug_lib()
+    assert D.mla_debug_bounds() == 1
+    for n in header_functions():
+        assert hasattr(D, n), n
+    assert mla.lib().mla_device_errors(None, None) == 1
+    assert D.mla_device_errors(None, None) == 1
