@@ -63,6 +63,7 @@ WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 8, 32, 64, 16, 128, 128, "f32", "identity", 1001),
     "v3_b1": Workload("v3_b1", 1, 1, 128, 128, 512, 64, 4096, 4096, "bf16", "identity", 1002),
     "v3_b64": Workload("v3_b64", 64, 1, 128, 128, 512, 64, 1024, 8192, "bf16", "permuted", 1003),
+    "v3_b64_l4096": Workload("v3_b64_l4096", 64, 1, 128, 128, 512, 64, 4096, 4096, "bf16", "permuted", 1006),
     "v3_long": Workload("v3_long", 4, 1, 128, 128, 512, 64, 131072, 131072, "bf16", "permuted",
                         1004, min_splits=32),
     "v3_sq4_fp8": Workload("v3_sq4_fp8", 128, 4, 128, 128, 512, 64, 4096, 16384, "fp8",

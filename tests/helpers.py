@@ -95,7 +95,9 @@ def split_page_ranges(seq_lens, p: mla.Params):
 
 
 def params_for(case: I.Case, num_splits=None, split_pages=None, flags=0, out_dtype=None,
-               plan=False, num_cus=256, num_parts=0) -> mla.Params:
+               plan=False, num_cus=256, num_parts=0, part_dtype=None) -> mla.Params:
+    """Parameters for a case.  bench=True-like use: plan=True with part_dtype=mla.BF16
+    is the launch configuration the bench times for bf16 and e4m3 caches."""
     wl = case.wl
     f32 = wl.dtype == "f32"
     fl = mla.F32 if f32 else mla.BF16
@@ -111,7 +113,7 @@ def params_for(case: I.Case, num_splits=None, split_pages=None, flags=0, out_dty
                         num_splits=num_splits, split_pages=split_pages, scale=wl.scale,
                         q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl, latent_dtype=fl,
                         out_dtype=mla.F32 if out_dtype is None else out_dtype, flags=flags,
-                        num_parts=num_parts)
+                        num_parts=num_parts, part_dtype=mla.F32 if part_dtype is None else part_dtype)
     if num_parts:
         p.num_splits = max(1, int(touched_parts(case.seq_lens, num_parts).max()))
     if plan:

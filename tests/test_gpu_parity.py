@@ -377,23 +377,34 @@ def test_repeatable_bitwise():
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 
 FULL = [
-    ("v3_b64", 6, 24),       # B=64, L ~ U[1024, 8192], permuted pages
-    ("v3_long", 2, 12),      # B=4, L = 131072, >= 32 splits
-    ("v3_sq4_fp8", 4, 12),   # B=128, Sq=4, L ~ U[4096, 16384], e4m3 cache
+    ("v3_b64", 6, 24, False),       # B=64, L ~ U[1024, 8192], permuted pages
+    ("v3_long", 2, 12, False),      # B=4, L = 131072, >= 32 splits
+    ("v3_sq4_fp8", 4, 12, False),   # B=128, Sq=4, L ~ U[4096, 16384], e4m3 cache
+    ("v3_sq4_fp8", 4, 12, True),    # ... through the bf16 expansion of the cache
 ]
 
 
-@pytest.mark.parametrize("wl_name,n_seq,n_heads", FULL)
-def test_full_size_sampled(wl_name, n_seq, n_heads):
+def bench_step(case, expand=False):
+    """The step in the launch configuration the bench times: balanced plan, bf16
+    partials (bf16 and e4m3 caches), the fused tail."""
+    wl = case.wl
+    p = params_for(case, plan=True, part_dtype=mla.F32 if wl.dtype == "f32" else mla.BF16)
+    dc = DeviceCase(case)
+    st = mla.DecodeStep(p, fused=True, expand=expand)
+    st(dc.q_nope, dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table, dc.seq_lens, dc.W_UK, dc.W_UV)
+    torch.cuda.synchronize()
+    return p, st
+
+
+@pytest.mark.parametrize("wl_name,n_seq,n_heads,expand", FULL)
+def test_full_size_sampled(wl_name, n_seq, n_heads, expand):
     wl = I.workload(wl_name)
-    note(f"full {wl_name}: generating")
+    note(f"full {wl_name} expand={expand}: generating")
     case = I.make_case(wl)
     validate(case)
-    p = params_for(case, plan=True)
-    note(f"full {wl_name}: tokens={case.total_tokens} pages={case.num_pages} S={p.num_splits} "
-         f"sp={p.split_pages} kernel={mla.decode_kernel_name(p)}")
-    st = DeviceCase(case).step(p)
-    torch.cuda.synchronize()
+    p, st = bench_step(case, expand)
+    note(f"full {wl_name}: tokens={case.total_tokens} pages={case.num_pages} P={p.num_parts} S={p.num_splits} "
+         f"kernel={mla.decode_kernel_name(p)}")
     got = st.out.float().cpu().numpy().reshape(-1, wl.d_h)
     got_l = st.lse.cpu().numpy().reshape(-1)
     assert np.isfinite(got).all()
@@ -404,6 +415,25 @@ def test_full_size_sampled(wl_name, n_seq, n_heads):
     note(f"  sampled out err {e:.3e}")
     assert e <= tol_of(wl)
     assert np.abs(got_l[rows] - lse).max() <= 2e-3
+
+
+def test_full_size_every_row_b64():
+    """Every output row of the B = 64 workload (8,192 rows, L ~ U[1024, 8192]) in
+    the bench's launch configuration against the oracle."""
+    wl = I.workload("v3_b64")
+    case = I.make_case(wl)
+    validate(case)
+    p, st = bench_step(case)
+    got = st.out.float().cpu().numpy().reshape(-1, wl.d_h)
+    got_l = st.lse.cpu().numpy().reshape(-1)
+    note(f"every row v3_b64: oracle on {got.shape[0]} rows")
+    out, _, lse = O.decode(case)
+    out = out.reshape(-1, wl.d_h)
+    e = err_rms(got, out)
+    rows_e = err_rows(got, out)
+    note(f"  out err {e:.3e}, worst row {rows_e:.3e}")
+    assert e <= tol_of(wl)
+    assert np.abs(got_l - lse.reshape(-1)).max() <= 2e-3
 
 
 def test_bound_calls_match_unbound():
