@@ -571,13 +571,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
     const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
-    // workgroup -> (part, row group rg): parts spread over the 8 XCDs, the row groups
-    // of one part on the same XCD
+    // workgroup -> (part, row group rg).  Workgroups are dealt to the 8 XCDs in turn
+    // (XCD = blockIdx % 8); each XCD takes a contiguous run of parts, so that the
+    // parts of one sequence mostly share an XCD and its L2 serves their query rows
+    // after the first load, and the row groups of one part share an XCD too.
     const int n_rg = (p.Sq * p.H) / kRows;
+    const int n_parts = p.num_parts > 0 ? p.num_parts : p.B * p.num_splits;
+    const int per_xcd = (n_parts + 7) / 8;
     const int qq = blockIdx.x >> 3;
     const int rg = qq % n_rg;
-    const int part = (qq / n_rg) * 8 + (blockIdx.x & 7);
-    const int n_parts = p.num_parts > 0 ? p.num_parts : p.B * p.num_splits;
+    const int part = (blockIdx.x & 7) * per_xcd + qq / n_rg;
     if (part >= n_parts) return;                       // grid rounded up to 8 XCDs
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
