@@ -100,14 +100,14 @@ def main():
     lens = case.seq_lens.tolist()
     fl = mla.F32 if wl.dtype == "f32" else mla.BF16
     kv = mla.FP8_E4M3 if wl.dtype == "fp8" else fl
+    # bf16 partials with a bf16 latent: half the bytes the attention writes and the
+    # merge reads (each partial row rounded once, as o_latent is); the planner sizes
+    # the parts for them
     p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, case.num_pages, case.max_pages,
                         scale=wl.scale, q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl,
-                        latent_dtype=fl, out_dtype=mla.F32)
+                        latent_dtype=fl, out_dtype=mla.F32, part_dtype=mla.F32 if wl.dtype == "f32" else mla.BF16)
     p = mla.plan_splits(p, max(lens), case.total_tokens, num_cus=props.multi_processor_count,
                         min_splits=wl.min_splits)
-    # bf16 partials with a bf16 latent: half the bytes the attention writes and the
-    # merge reads (each partial row rounded once, as o_latent is)
-    p.part_dtype = mla.F32 if wl.dtype == "f32" else mla.BF16
 
     names = ("q_nope", "q_rope", "c_kv", "k_pe", "kv_scale", "block_table", "seq_lens", "W_UK", "W_UV")
     base = {k: (None if getattr(case, k) is None else getattr(case, k).to(dev)) for k in names}

@@ -406,7 +406,8 @@ mla_status_t mla_check_params(const mla_params_t *p);
  * Host-only split planner.  Given the longest sequence (tokens), the total
  * tokens of the batch and the number of compute units to fill, chooses
  * balanced splits: sets p->num_parts (P: one attention workgroup per compute
- * unit, at least 8 parts, parts of at least 4 pages on average, at least
+ * unit, at least 8 parts, parts of at least 4 pages on average (2 with bf16
+ * partials), at least
  * `min_splits` parts when the batch has that many pages) and p->num_splits, the
  * bound on the parts one sequence can touch.  It extends mla_default_num_splits
  * (uniform lengths, fixed splits) to any mix of lengths.  max_seq_len must not be

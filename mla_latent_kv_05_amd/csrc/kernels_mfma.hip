@@ -208,6 +208,9 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
+// live splits whose partial loads are issued together in the merges
+constexpr int kMergeBatch = 8;
+
 template <bool kBf16Out, bool kPartBf16>
 __global__ __launch_bounds__(256) void combine_kernel_512(
     const mla_params_t p, const void *__restrict__ o_part, const float *__restrict__ lse_part,
@@ -230,23 +233,40 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
             const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);
             sum += w;
             uint64_t live = __builtin_amdgcn_ballot_w64(w != 0.f);
+            // up to kMergeBatch live splits per round: their loads first, then the sums
+            // in split order (the same order as one split at a time)
             while (live) {
-                const int k = __builtin_ctzll(live);
-                live &= live - 1;
-                const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), k));
-                const int64_t e = op + static_cast<int64_t>(c0 + k) * kDc;
-                f32x4 v0, v1;
-                if constexpr (kPartBf16) {
-                    unpack_bf16x8(*reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(o_part) + e), v0, v1);
-                } else {
-                    const f32x4 *src = reinterpret_cast<const f32x4 *>(static_cast<const float *>(o_part) + e);
-                    v0 = src[0];
-                    v1 = src[1];
+                int kq[kMergeBatch];
+                bool vq[kMergeBatch];
+#pragma unroll
+                for (int q = 0; q < kMergeBatch; ++q) {
+                    vq[q] = live != 0;
+                    kq[q] = vq[q] ? __builtin_ctzll(live) : 0;
+                    live &= live - 1;
+                }
+                f32x4 v0[kMergeBatch], v1[kMergeBatch];
+#pragma unroll
+                for (int q = 0; q < kMergeBatch; ++q) {
+                    if (!vq[q]) continue;
+                    const int64_t e = op + static_cast<int64_t>(c0 + kq[q]) * kDc;
+                    if constexpr (kPartBf16) {
+                        unpack_bf16x8(*reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(o_part) + e), v0[q],
+                                      v1[q]);
+                    } else {
+                        const f32x4 *src = reinterpret_cast<const f32x4 *>(static_cast<const float *>(o_part) + e);
+                        v0[q] = src[0];
+                        v1[q] = src[1];
+                    }
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[j] += wk * v0[j];
-                    acc[4 + j] += wk * v1[j];
+                for (int q = 0; q < kMergeBatch; ++q) {
+                    if (!vq[q]) continue;
+                    const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), kq[q]));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[j] += wk * v0[q][j];
+                        acc[4 + j] += wk * v1[q][j];
+                    }
                 }
             }
         }
@@ -354,6 +374,43 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
             wt[i] = (lc == -INFINITY || mx[i] == -INFINITY) ? 0.f : __expf(lc - mx[i]);
             sum[i] += wt[i];
             live |= __builtin_amdgcn_ballot_w64(wt[i] != 0.f);
+        }
+        if (R - r0 <= 8) {
+            // at most one row per wave (row w of the chunk): up to kMergeBatch live
+            // splits per round, loads first, then the sums in split order
+            while (live) {
+                int kq[kMergeBatch];
+                bool vq[kMergeBatch];
+#pragma unroll
+                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                    vq[qq] = live != 0;
+                    kq[qq] = vq[qq] ? __builtin_ctzll(live) : 0;
+                    live &= live - 1;
+                }
+                f32x4 v0[kMergeBatch], v1[kMergeBatch];
+#pragma unroll
+                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                    const uint32_t off = vq[qq] ? ((c0 + kq[qq]) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
+                    if constexpr (kPartBf16) {
+                        unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[0], off, 0, 0)),
+                                      v0[qq], v1[qq]);
+                    } else {
+                        v0[qq] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[0], off, 0, 0));
+                        v1[qq] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[0], off + 16u, 0, 0));
+                    }
+                }
+#pragma unroll
+                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                    if (!vq[qq]) continue;
+                    const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[0]), kq[qq]));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[0][j] += wk * v0[qq][j];
+                        acc[0][4 + j] += wk * v1[qq][j];
+                    }
+                }
+            }
+            continue;
         }
         // two live splits per round: the loads of all rows and both splits first,
         // then the sums in split order; a row without weight on a split (or a

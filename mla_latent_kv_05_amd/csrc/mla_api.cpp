@@ -156,9 +156,11 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     // rows per token): with 2 or 4 parts every page is read by all row groups at once
     // (measured at 4 x 4,096 positions: 64 new tokens, 2 parts 1.28 ms, 8 parts 0.44 ms)
     P = std::max<int64_t>(P, 8);
-    // parts of at least 4 pages keep the fp32 partials (d_c*4 bytes per row) small next
-    // to the cache they summarise (measured at B = 1: 4 pages per part beat 8, 2 and 1)
-    P = std::min(P, std::max<int64_t>(1, pages_lo / 4));
+    // parts of at least 4 pages (2 with bf16 partials) keep the partials (d_c * 4 or 2
+    // bytes per row) small next to the cache they summarise (measured at B = 1 with
+    // fp32 partials: 4 pages per part beat 8, 2 and 1; with bf16 partials 2 beat 4 and 1)
+    const int64_t min_pages = p->part_dtype == MLA_BF16 ? 2 : 4;
+    P = std::min(P, std::max<int64_t>(1, pages_lo / min_pages));
     P = std::max(P, std::min<int64_t>(min_splits, std::max<int64_t>(1, pages_lo)));
     P = std::min<int64_t>(P, kMaxParts);
     // a sequence of n pages touches at most ceil(n / q) + 1 parts of >= q pages, and

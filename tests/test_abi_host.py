@@ -310,3 +310,12 @@ def test_debug_build_and_error_word_entry_points():
         assert hasattr(D, n), n
     assert mla.lib().mla_device_errors(None, None) == 1
     assert D.mla_device_errors(None, None) == 1
+
+
+def test_planner_part_size_follows_partial_type():
+    """Parts of at least 4 pages with fp32 partials, 2 with bf16 partials (one
+    sequence of 64 pages: 16 and 32 parts)."""
+    p = mla.make_params(1, 1, 128, 128, 512, 64, num_pages=64, max_pages=64)
+    assert mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1).num_parts == 16
+    p.part_dtype = mla.BF16
+    assert mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1).num_parts == 32
