@@ -12,7 +12,8 @@ The inputs are replicated in HBM (by default enough replicas to hold at least
 last-level cache cannot serve one step from the previous one.
 
 Timing, in this order:
-  1. the step with the fused tail: max(W, STEP_WARMUP) untimed warm-up steps,
+  1. the step with the fused tail: untimed warm-up steps (at least W, and enough
+     for WARM_S seconds of GPU work),
      then exactly K timed steps bracketed by a synchronize and events (events
      only at block boundaries);
   2. the same for the four-call step;
@@ -21,8 +22,9 @@ Timing, in this order:
      on the launch stream inside one event pair, whatever --steps is.
 The GPU reaches its sustained step rate only after some hundreds of steps of
 load (measured at 64 x 4,096 positions: 5 warm-up steps then 20 timed ones read
-~10% slower than after 300 more), so each route gets at least STEP_WARMUP
-warm-up steps whatever W is; the JSON gives W and the warm-up steps run.
+~10% slower than after 300 more, and still ~2% slower than after 1,000 more), so
+each route gets WARM_S seconds of warm-up steps whatever W is; the JSON gives W
+and the warm-up steps each route ran.
 The oracle leg (cpu_baseline) also compares the step's output for the sequences
 it computed with the GPU step's output (max and RMS error over the output RMS).
 
@@ -42,7 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 STEP_BLOCK = 50                # steps per block of the step-time spread
-STEP_WARMUP = 300              # warm-up steps of each route at least (more when W is larger)
+WARM_S = 0.3                   # seconds of warm-up steps per route (at least W steps)
 KERNEL_WARMUP = 300            # untimed attention launches before the kernel leg
 KERNEL_LAUNCHES = 600          # timed attention launches (at least; more when K is larger)
 REPLICA_BYTES = 1 << 30        # inputs replicated until the replicas hold this many bytes
@@ -135,14 +137,29 @@ def main():
     step_f = mla.DecodeStep(p, device=dev, fused=True)
     bound_f = [step_f.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                            t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
-    n_warm = max(args.warmup, STEP_WARMUP)
+
+    def warm(step_fn):
+        """W warm-up steps, then more until about WARM_S seconds of GPU work have run;
+        returns the number of warm-up steps."""
+        for i in range(args.warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(50):
+            step_fn(i)
+        torch.cuda.synchronize()
+        n = max(0, int(WARM_S / ((time.perf_counter() - t0) / 50)) - 50)
+        for i in range(n):
+            step_fn(i)
+        torch.cuda.synchronize()
+        return args.warmup + 50 + n
+
+    warm_runs = {}
 
     # 1. the fused step: warm-up steps, then exactly K timed steps bracketed by a
     # synchronize and events; an event at every block boundary (one per STEP_BLOCK
     # steps) gives the spread of the per-step time without gaps inside the steps
-    for i in range(n_warm):
-        bound_f[i % args.replicas]()
-    torch.cuda.synchronize()
+    warm_runs["fused_tail"] = warm(lambda i: bound_f[i % args.replicas]())
     assert torch.isfinite(step_f.out).all(), "non-finite output"
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-args.steps // STEP_BLOCK) + 1)]
     torch.cuda.synchronize()
@@ -159,9 +176,7 @@ def main():
               for k in range(len(marks) - 1)]
 
     # 2. the four-call step, the same way (events around the whole loop only)
-    for i in range(n_warm):
-        run(i % args.replicas)
-    torch.cuda.synchronize()
+    warm_runs["four_calls"] = warm(lambda i: run(i % args.replicas))
     assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -179,9 +194,7 @@ def main():
         step_e = mla.DecodeStep(p, device=dev, fused=True, expand=True)
         bound_e = [step_e.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                                t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
-        for i in range(n_warm):
-            bound_e[i % args.replicas]()
-        torch.cuda.synchronize()
+        warm_runs["expand_fused_tail"] = warm(lambda i: bound_e[i % args.replicas]())
         x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         x0.record(stream)
         for i in range(args.steps):
@@ -255,7 +268,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": n_warm,
+        "warmup_steps_run": warm_runs,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "higher_is_better": True,
