@@ -43,8 +43,14 @@ __global__ __launch_bounds__(64) void absorb_mfma_kernel(
     constexpr int kKs = kDh / 32;                 // 32-deep k-steps
     const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
     const int R = p.B * p.Sq;
-    const int h = blockIdx.x >> 3;
-    const int c8 = blockIdx.x & 7;                // 64-column eighth of d_c
+    // workgroups are dealt to the 8 XCDs in turn (XCD = blockIdx % 8): the eight
+    // column slices of a head go to one XCD, whose L2 then serves the head's query
+    // rows to all eight after the first load
+    const int hpx = (p.H + 7) / 8;                // heads per XCD
+    const int k8 = blockIdx.x >> 3;
+    const int h = (blockIdx.x & 7) * hpx + (k8 >> 3);
+    const int c8 = k8 & 7;                        // 64-column eighth of d_c
+    if (h >= p.H) return;
     const int col0 = c8 * 64 + r16 * 4;           // this lane's 4 columns
     const uint16_t *W = W_UK + static_cast<int64_t>(h) * kDh * kDc;
     u32x2 rows[kKs][8];
@@ -208,8 +214,10 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
-// live splits whose partial loads are issued together in the merges
-constexpr int kMergeBatch = 8;
+// live splits whose partial loads are issued together: the merge kernel (one row
+// per wave) and the fused tail's single-row path
+constexpr int kMergeBatch = 4;
+constexpr int kMergeBatchRow = 8;
 
 template <bool kBf16Out, bool kPartBf16>
 __global__ __launch_bounds__(256) void combine_kernel_512(
@@ -376,20 +384,20 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
             live |= __builtin_amdgcn_ballot_w64(wt[i] != 0.f);
         }
         if (R - r0 <= 8) {
-            // at most one row per wave (row w of the chunk): up to kMergeBatch live
+            // at most one row per wave (row w of the chunk): up to kMergeBatchRow live
             // splits per round, loads first, then the sums in split order
             while (live) {
-                int kq[kMergeBatch];
-                bool vq[kMergeBatch];
+                int kq[kMergeBatchRow];
+                bool vq[kMergeBatchRow];
 #pragma unroll
-                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                for (int qq = 0; qq < kMergeBatchRow; ++qq) {
                     vq[qq] = live != 0;
                     kq[qq] = vq[qq] ? __builtin_ctzll(live) : 0;
                     live &= live - 1;
                 }
-                f32x4 v0[kMergeBatch], v1[kMergeBatch];
+                f32x4 v0[kMergeBatchRow], v1[kMergeBatchRow];
 #pragma unroll
-                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                for (int qq = 0; qq < kMergeBatchRow; ++qq) {
                     const uint32_t off = vq[qq] ? ((c0 + kq[qq]) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
                     if constexpr (kPartBf16) {
                         unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[0], off, 0, 0)),
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
                     }
                 }
 #pragma unroll
-                for (int qq = 0; qq < kMergeBatch; ++qq) {
+                for (int qq = 0; qq < kMergeBatchRow; ++qq) {
                     if (!vq[qq]) continue;
                     const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[0]), kq[qq]));
 #pragma unroll
@@ -412,53 +420,51 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
             }
             continue;
         }
-        // two live splits per round: the loads of all rows and both splits first,
-        // then the sums in split order; a row without weight on a split (or a
-        // missing second split) loads past its buffer's end, which returns zeros
-        // without a memory access
+        // kSr live splits per round (four with bf16 partials, two with fp32): the
+        // loads of all rows and splits first, then the sums in split order; a row
+        // without weight on a split (or a missing split) loads past its buffer's
+        // end, which returns zeros without a memory access
+        constexpr int kSr = kPartBf16 ? 4 : 2;
         while (live) {
-            const int ka = __builtin_ctzll(live);
-            live &= live - 1;
-            const bool has_b = live != 0;
-            const int kb = has_b ? __builtin_ctzll(live) : ka;
-            if (has_b) live &= live - 1;
-            float wa_[kCuRowsPerWave], wb_[kCuRowsPerWave];
-            f32x4 a0[kCuRowsPerWave], a1[kCuRowsPerWave], b0[kCuRowsPerWave], b1[kCuRowsPerWave];
+            int kq[kSr];
+            bool vq[kSr];
 #pragma unroll
-            for (int i = 0; i < kCuRowsPerWave; ++i) {
-                wa_[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), ka));
-                wb_[i] = has_b ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), kb)) : 0.f;
-                const uint32_t oa = wa_[i] != 0.f ? ((c0 + ka) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
-                const uint32_t ob = wb_[i] != 0.f ? ((c0 + kb) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
-                if constexpr (kPartBf16) {
-                    unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0)),
-                                  a0[i], a1[i]);
-                    unpack_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0)),
-                                  b0[i], b1[i]);
-                } else {
-                    a0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa, 0, 0));
-                    a1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], oa + 16u, 0, 0));
-                    b0[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob, 0, 0));
-                    b1[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], ob + 16u, 0, 0));
-                }
+            for (int qq = 0; qq < kSr; ++qq) {
+                vq[qq] = live != 0;
+                kq[qq] = vq[qq] ? __builtin_ctzll(live) : 0;
+                live &= live - 1;
             }
+            float wq[kCuRowsPerWave][kSr];
+            u32x4 x0[kCuRowsPerWave][kSr], x1[kCuRowsPerWave][kSr];
 #pragma unroll
-            for (int i = 0; i < kCuRowsPerWave; ++i) {
-                if (wa_[i] != 0.f) {
+            for (int i = 0; i < kCuRowsPerWave; ++i)
+#pragma unroll
+                for (int qq = 0; qq < kSr; ++qq) {
+                    wq[i][qq] = vq[qq] ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[i]), kq[qq])) : 0.f;
+                    const uint32_t off =
+                        wq[i][qq] != 0.f ? ((c0 + kq[qq]) * kDc + lane * 8) * static_cast<uint32_t>(kEb) : 0x80000000u;
+                    x0[i][qq] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off, 0, 0));
+                    if constexpr (!kPartBf16)
+                        x1[i][qq] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prow[i], off + 16u, 0, 0));
+                }
+#pragma unroll
+            for (int i = 0; i < kCuRowsPerWave; ++i)
+#pragma unroll
+                for (int qq = 0; qq < kSr; ++qq) {
+                    if (wq[i][qq] == 0.f) continue;
+                    f32x4 v0, v1;
+                    if constexpr (kPartBf16) {
+                        unpack_bf16x8(x0[i][qq], v0, v1);
+                    } else {
+                        v0 = __builtin_bit_cast(f32x4, x0[i][qq]);
+                        v1 = __builtin_bit_cast(f32x4, x1[i][qq]);
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[i][j] += wa_[i] * a0[i][j];
-                        acc[i][4 + j] += wa_[i] * a1[i][j];
+                        acc[i][j] += wq[i][qq] * v0[j];
+                        acc[i][4 + j] += wq[i][qq] * v1[j];
                     }
                 }
-                if (wb_[i] != 0.f) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[i][j] += wb_[i] * b0[i][j];
-                        acc[i][4 + j] += wb_[i] * b1[i][j];
-                    }
-                }
-            }
         }
     }
 #pragma unroll
@@ -533,7 +539,7 @@ bool absorb_mfma_supported(const mla_params_t &p) {
 
 hipError_t launch_absorb_mfma(const mla_params_t &p, const void *q_nope, const void *W_UK,
                               void *q_abs, hipStream_t stream) {
-    const int64_t blocks = static_cast<int64_t>(p.H) * 8;
+    const int64_t blocks = (static_cast<int64_t>(p.H) + 7) / 8 * 64;
     hipLaunchKernelGGL(absorb_mfma_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, p,
                        static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(W_UK),
                        static_cast<uint16_t *>(q_abs));
