@@ -101,6 +101,32 @@ __device__ __forceinline__ void copy_1k(const u32x4 &rsrc, uint32_t l, uint32_t 
                  : "memory", "m0");
 }
 
+// One instruction copying 256 bytes: lane i's 4 bytes from base + soff + voff_i land at
+// M0 + 4 i (lanes past the buffer's end read zeros).
+__device__ __forceinline__ void copy_256(const u32x4 &rsrc, uint32_t l, uint32_t soff, uint32_t v) {
+    asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dword %[v], %[r], %[so] offen nt lds"
+                 :: [r] "s"(rsrc), [l] "s"(__builtin_amdgcn_readfirstlane(l)),
+                    [so] "s"(__builtin_amdgcn_readfirstlane(soff)), [v] "v"(v)
+                 : "memory", "m0");
+}
+
+// LDS layout by cache type.  bf16: 4 stages of 38 KiB, weight buffer 0 in the stage
+// row padding, buffer 1 after the stages.  e4m3: 3 bf16 stages (filled by the
+// conversion of the raw codes and by the RoPE copies), 2 raw stages (32 rows of 512
+// codes, then each wave's copy of the 32 token scales), buffer 0's slots 6 and 7
+// (there is no fourth stage's padding), then buffer 1.
+template <bool kFp8>
+struct Lds {
+    static constexpr int kStages = kFp8 ? 3 : 4;
+    static constexpr int kRawCodes = kTile * kDc;                   // 16384
+    static constexpr int kRawStage = kRawCodes + 4 * 256;
+    static constexpr int kRawBase = kStages * kStage;
+    static constexpr int kW0Extra = kRawBase + 2 * kRawStage;
+    static constexpr int kW1Base = kFp8 ? kW0Extra + 2048 : kSmemStages;
+    static constexpr int kEnd = kW1Base + 8192;
+    static_assert(kEnd <= kSmem, "LDS budget");
+};
+
 // s_waitcnt lgkmcnt(n) that the compiler sees (it then adds no wait of its own for
 // the LDS reads it covers); vmcnt and expcnt are left at their maxima
 template <int N>
@@ -131,9 +157,11 @@ __device__ __forceinline__ bf16x8 tr_op(const v4i16 &lo, const v4i16 &hi) {
 // ---------------------------------------------------------------------------
 // One wave's part of one segment.
 // ---------------------------------------------------------------------------
+template <bool kFp8>
 __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p, const uint16_t *__restrict__ q_abs,
                                                const uint16_t *__restrict__ q_rope, const char *__restrict__ c_kv,
-                                               const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ seg_bt,
+                                               const uint16_t *__restrict__ k_pe, const float *__restrict__ kv_scale,
+                                               const int32_t *__restrict__ seg_bt,
                                                const Segment &seg, int seq_len, int rg, void *__restrict__ o_part,
                                                float *__restrict__ lse_part) {
     // lane-dependent values are recomputed per segment (opaque to code motion, so
@@ -144,6 +172,8 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     const int n = lane & 31, g = lane >> 5;
     const int S = p.num_splits;
     const uint32_t sm = lds_addr(smem);
+    using L = Lds<kFp8>;
+    constexpr int kNst = L::kStages;
 
     seq_len = __builtin_amdgcn_readfirstlane(seq_len);
     const int t_begin = __builtin_amdgcn_readfirstlane(seg.pa * kPage);
@@ -155,6 +185,11 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     const int s_q = (rg * kRows + 32 * w) / p.H;                                              // its query position
     const int n_vis = __builtin_amdgcn_readfirstlane(seq_len - p.Sq + 1 + s_q);
 
+    // LDS address of tile t's bf16 stage, made a scalar explicitly (with three stages
+    // the compiler otherwise keeps the modulo in vector registers and spills)
+    auto stage_addr = [&](int t) -> uint32_t {
+        return sm + __builtin_amdgcn_readfirstlane((t % kNst) * kStage);
+    };
     // ---- copies: latent rows 8w .. 8w+7 and RoPE rows 8w .. 8w+7 of a tile
     // page list of the segment: lanes hold pages pl_base .. pl_base + 63
     int pl_base = 0;
@@ -182,17 +217,22 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     // copies of tile t, one instruction at a time: i < 8 latent row 8w + i, i = 8 the
     // RoPE rows 8w .. 8w+7.  A tile past the segment's end gets a zero-length buffer:
     // its instructions move nothing, so that every tile issues the same copies and
-    // the vmcnt accounting is the same for all of them.
+    // the vmcnt accounting is the same for all of them.  e4m3: the codes of rows
+    // 8w .. 8w+7 (two rows per instruction) and the 32 token scales go to the tile's
+    // raw stage, the RoPE rows to its bf16 stage.
     struct TileSrc {
-        u32x4 ckv, kpe;        // buffer descriptors of the tile's latent rows and RoPE rows
-        uint32_t st;
+        u32x4 ckv, kpe, scl;   // buffer descriptors of the tile's latent rows, RoPE rows, scales
+        uint32_t st, raw;      // its bf16 stage and (e4m3) raw stage
     };
     auto tile_src = [&](int t) -> TileSrc {
         const bool real = t < n_tiles;
         const int64_t phys = real ? tile_page(t) : 0;
         const int64_t crow0 = phys * kPage + (t & 1) * kTile;
-        return TileSrc{copy_rsrc(c_kv + crow0 * kCkvRow, real ? kTileCkv : 0u),
-                       copy_rsrc(k_pe + crow0 * kDr, real ? kTileKpe : 0u), sm + (t % kStages) * kStage};
+        constexpr int kRowBytes = kFp8 ? kDc : kCkvRow;
+        return TileSrc{copy_rsrc(c_kv + crow0 * kRowBytes, real ? kTile * kRowBytes : 0u),
+                       copy_rsrc(k_pe + crow0 * kDr, real ? kTileKpe : 0u),
+                       copy_rsrc(kFp8 ? kv_scale + crow0 : nullptr, kFp8 && real ? kTile * 4 : 0u),
+                       stage_addr(t), sm + L::kRawBase + (t & 1) * L::kRawStage};
     };
     auto copy_one = [&](const TileSrc &ts, int i) {
         if (i < 8)
@@ -204,6 +244,48 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
         const TileSrc ts = tile_src(t);
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) copy_one(ts, i);
+    };
+    // e4m3: codes copy i < 4 (rows 8w + 2i, 8w + 2i + 1), i = 4 the scales (each wave
+    // its own copy); the RoPE rows of a tile separately (rope_copy)
+    const uint32_t lane16 = static_cast<uint32_t>(lane) << 4, lane4 = static_cast<uint32_t>(lane) << 2;
+    auto raw_copy = [&](const TileSrc &ts, int i) {
+        if (i < 4)
+            copy_1k(ts.ckv, ts.raw + (8 * w + 2 * i) * kDc, (8 * w + 2 * i) * kDc, lane16);
+        else
+            copy_256(ts.scl, ts.raw + L::kRawCodes + w * 256, 0u, lane4);
+    };
+    auto rope_copy = [&](const TileSrc &ts) { copy_1k(ts.kpe, ts.st + kStageKpe + w * 1024, w * 1024, rope_voff); };
+    // e4m3 conversion of rows 8w .. 8w+7 of tile t from its raw stage into its bf16
+    // stage: bf16(float(code) * scale), one fp32 product rounded to nearest even (the
+    // value mla_expand_kv gives).  One row at a time: lane l reads codes 8l .. 8l+7 of
+    // the row (512 contiguous bytes over the wave) and writes their bf16 values as the
+    // row's logical 16-byte chunk l (a permutation of the row's chunks over the
+    // lanes), so that neither access has bank conflicts; conv_read issues the reads of
+    // row 8w + j, conv_write converts and stores it.
+    struct ConvIn {
+        u32x2 codes;
+        float scale;
+    };
+    auto conv_read = [&](int t, int j) -> ConvIn {
+        const uint32_t raw = sm + L::kRawBase + (t & 1) * L::kRawStage;
+        return ConvIn{lds_load<u32x2>(raw + (8 * w + j) * kDc + 8 * lane),
+                      lds_load<float>(raw + L::kRawCodes + w * 256 + (8 * w + j) * 4)};
+    };
+    auto conv_write = [&](int t, int j, const ConvIn &v) {
+        const int r = 8 * w + j;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], true);
+            o[2 * e] = cvt_pk_bf16(lo[0] * v.scale, lo[1] * v.scale);
+            o[2 * e + 1] = cvt_pk_bf16(hi[0] * v.scale, hi[1] * v.scale);
+        }
+        lds_store<u32x4>(stage_addr(t) + r * kLRow + ((lane ^ lat_swz(r)) << 4), o);
+    };
+    auto convert_tile = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) conv_write(t, j, conv_read(t, j));
     };
 
     // ---- query operands (B of the score product): k-step k < 32 latent dims
@@ -247,8 +329,9 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     // is spread over the padding of the stage rows (slot s: rows 16(s & 1) .. +15 of
     // stage s / 2, four cells per row); buffer 1 follows the stages.
     auto cell = [&](int buf, int slot, int idx) -> uint32_t {
-        return buf ? sm + kSmemStages + slot * 1024 + idx * 16
-                   : sm + (slot >> 1) * kStage + (16 * (slot & 1) + (idx >> 2)) * kLRow + kCkvRow + (idx & 3) * 16;
+        if (buf) return sm + L::kW1Base + slot * 1024 + idx * 16;
+        if (kFp8 && slot >= 2 * kNst) return sm + L::kW0Extra + (slot - 2 * kNst) * 1024 + idx * 16;
+        return sm + (slot >> 1) * kStage + (16 * (slot & 1) + (idx >> 2)) * kLRow + kCkvRow + (idx & 3) * 16;
     };
     auto pslot = [&](int buf, int slot) -> uint32_t { return cell(buf, slot, lane); };
 
@@ -270,8 +353,25 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
 
     // ---- score product of tile t (its stage has landed): 36 MFMAs on one
     // accumulator, each K operand read eight MFMAs ahead
-    auto score = [&](int t, const TileSrc *cp) -> f32x16 {
-        const uint32_t st = sm + (t % kStages) * kStage;
+    auto score = [&](int t, const TileSrc *cp, const TileSrc *rp = nullptr) -> f32x16 {
+        const uint32_t st = stage_addr(t);
+        // e4m3: the conversion of tile t + 1 (row 8w + j read at step 4j + 1, converted
+        // and stored at 4j + 3), the raw copies of tile t + 2 and the RoPE copy of tile t + 1
+        // (a tile past the end is converted too: its stage is not read again in the
+        // segment, and its zero-length copies move nothing)
+        ConvIn cv{};
+        auto fp8_step = [&](auto K) {
+            constexpr int k = decltype(K)::value;
+            if constexpr (k % 4 == 1 && k < 32) {
+                cv = conv_read(t + 1, k / 4);
+            } else if constexpr (k % 4 == 3 && k < 32) {
+                conv_write(t + 1, k / 4, cv);
+            } else if constexpr (k % 4 == 2 && k <= 18) {
+                raw_copy(*cp, (k - 2) / 4);
+            } else if constexpr (k == 22) {
+                rope_copy(*rp);
+            }
+        };
         const uint32_t kb0 = st + kx[0], kb1 = st + kx[1];
         uint32_t kpb[4];
 #pragma unroll
@@ -282,13 +382,15 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
 #define D128_KREAD(k) a[k] = ld128(D128_KADDR(k));
         // groups of four MFMAs; the reads of group g+2 are issued during group g, and
         // one wait per group covers its four operands
-        D128_KREAD(0) D128_KREAD(1) D128_KREAD(2) D128_KREAD(3) D128_KREAD(4) D128_KREAD(5) D128_KREAD(6) D128_KREAD(7)
+        D128_KREAD(0) D128_KREAD(1) D128_KREAD(2) D128_KREAD(3)
+        D128_KREAD(4) D128_KREAD(5) D128_KREAD(6) D128_KREAD(7)
         pin();
 #define D128_KSTEP(k)                                                 \
         if constexpr ((k) == 0) score_mfma_first(acc, a[k], qreg[k]); \
         else score_mfma(acc, a[k], qreg[k]);                          \
         if constexpr ((k) + 8 < kSteps) D128_KREAD((k) + 8)           \
-        if constexpr ((k) % 4 == 2) if (cp) copy_one(*cp, (k) / 4);   \
+        if constexpr (kFp8) fp8_step(std::integral_constant<int, (k)>{}); \
+        else if constexpr ((k) % 4 == 2) if (cp) copy_one(*cp, (k) / 4); \
         pin();
 #define D128_KGROUP(g)                                                \
         if constexpr (4 * (g) + 4 < kSteps) wait_lgkm<4>();           \
@@ -383,7 +485,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     // the MFMAs (step k after MFMA k + 2)
     auto latent = [&](int t, int buf, auto WithSm, Softmax &x, u32x4 &pn0, u32x4 &pn1) {
         constexpr bool kWithSm = decltype(WithSm)::value;
-        const uint32_t st = sm + (t % kStages) * kStage;
+        const uint32_t st = stage_addr(t);
         const uint32_t vb0 = st + vx[0], vb1 = st + vx[1];
         u32x4 pw[2][2];                                  // [head block][k-step]
 #pragma unroll
@@ -444,15 +546,37 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
         // ---- the tile loop.  Iteration t: scores of tile t (copies of tile t+2
         // between its MFMAs), then the latent sum of tile t-1 with the softmax of
         // tile t between its MFMAs.  The weights of tile t go to buffer t & 1.
-        issue_tile(0);
-        issue_tile(1);
-        wait_vmcnt<kCopies>();                           // query loads and tile 0 landed
-        barrier_lds();
-        issue_tile(2);
+        if constexpr (kFp8) {
+            // tile 0's RoPE rows, codes and scales and tile 1's codes and scales in
+            // flight; tile 0 converted before its scores
+            {
+                const TileSrc t0 = tile_src(0), t1 = tile_src(1);
+                rope_copy(t0);
+#pragma unroll
+                for (int i = 0; i < 5; ++i) raw_copy(t0, i);
+#pragma unroll
+                for (int i = 0; i < 5; ++i) raw_copy(t1, i);
+            }
+            wait_vmcnt<0>();                             // query loads, tiles 0 and 1 landed
+            barrier_lds();
+            convert_tile(0);
+            barrier_lds();
+        } else {
+            issue_tile(0);
+            issue_tile(1);
+            wait_vmcnt<kCopies>();                       // query loads and tile 0 landed
+            barrier_lds();
+            issue_tile(2);
+        }
         {
             Softmax x;
             x.buf = 0;
-            x.sc = score(0, nullptr);
+            if constexpr (kFp8) {
+                const TileSrc r1 = tile_src(1), c2 = tile_src(2);   // ascending: tile_page moves forward
+                x.sc = score(0, &c2, &r1);               // converts tile 1, copies tiles 1 (RoPE) and 2
+            } else {
+                x.sc = score(0, nullptr);
+            }
             score_done(x.sc);
             mask(0, x.sc);
             u32x4 pn0, pn1;
@@ -462,12 +586,19 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
 #undef D128_SM
         }
         for (int t = 1; t < n_tiles; ++t) {
-            wait_vmcnt<kCopies>();                       // tile t landed (tile t+1 may be in flight)
-            barrier_lds();                               // ... for every wave, and the weights of tile t-1
-            const TileSrc next = tile_src(t + 2);
             Softmax x;
             x.buf = t & 1;
-            x.sc = score(t, &next);                      // copies tile t+2 between its MFMAs
+            if constexpr (kFp8) {
+                wait_vmcnt<0>();                         // tile t's RoPE rows and tile t+1's codes landed
+                barrier_lds();                           // ... and tile t converted, for every wave
+                const TileSrc r = tile_src(t + 1), c = tile_src(t + 2);   // ascending (page list window)
+                x.sc = score(t, &c, &r);
+            } else {
+                wait_vmcnt<kCopies>();                   // tile t landed (tile t+1 may be in flight)
+                barrier_lds();                           // ... for every wave, and the weights of tile t-1
+                const TileSrc next = tile_src(t + 2);
+                x.sc = score(t, &next);                  // copies tile t+2 between its MFMAs
+            }
             mask(t, x.sc);                               // (softmax reads the scores two MFMAs later)
             u32x4 pn0, pn1;
             latent(t - 1, (t - 1) & 1, std::true_type{}, x, pn0, pn1);
@@ -477,7 +608,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
             // weights never meet non-finite values in the latent product.  Each wave
             // clears its own rows once its copies of the tile have landed; other waves
             // may still read them for scores, which are masked there whatever they hold.
-            const uint32_t st = sm + ((n_tiles - 1) % kStages) * kStage;
+            const uint32_t st = stage_addr(n_tiles - 1);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 if (8 * w + i >= last_valid) lds_store<u32x4>(st + (8 * w + i) * kLRow + 16 * lane, u32x4{0u, 0u, 0u, 0u});
@@ -497,7 +628,12 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
             const float lw_tot = pair_sum(lw_run);
             if (lane < 32) lds_store<float>(cell(xb, w, n), l_tot == 0.f ? 0.f : 1.f / lw_tot);
         }
-        if (lane == 0) lds_store<int>(cell(xb, 4, w), __builtin_amdgcn_ballot_w64(over) != 0);
+        {
+            // the ballot runs with every lane active (inside `lane == 0` it would see
+            // lane 0's flag only)
+            const int any_over = __builtin_amdgcn_ballot_w64(over) != 0;
+            if (lane == 0) lds_store<int>(cell(xb, 4, w), any_over);
+        }
         barrier_lds();
         const int ov = lds_load<int>(cell(xb, 4, 0)) | lds_load<int>(cell(xb, 4, 1)) | lds_load<int>(cell(xb, 4, 2)) |
                        lds_load<int>(cell(xb, 4, 3));
@@ -566,9 +702,11 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     }
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
-    const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const int32_t *__restrict__ block_table,
+    const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const float *__restrict__ kv_scale,
+    const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, void *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     // workgroup -> (part, row group rg).  Workgroups are dealt to the 8 XCDs in turn
@@ -598,8 +736,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
             if (!first) barrier_lds();                 // the previous segment's LDS reads are done
             first = false;
             wait_vmcnt<0>();                           // its stores too (the copy waits count from here)
-            attend_segment(smem, p, q_abs, q_rope, c_kv, k_pe,
-                           block_table + static_cast<int64_t>(seg.b) * p.max_pages + seg.pa, seg,
+            attend_segment<kFp8>(smem, p, q_abs, q_rope, c_kv, k_pe, kv_scale,
+                                 block_table + static_cast<int64_t>(seg.b) * p.max_pages + seg.pa, seg,
                            seq_lens[seg.b], rg, o_part, lse_part);
         } else if (threadIdx.x == 0) {
             raise_error(MLA_DEVERR_SPLITS);            // num_splits below the plan's bound
@@ -614,19 +752,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
 int decode_rows_per_workgroup(const mla_params_t &p) { return decode128_supported(p) ? kRows : kDecodeRowsPerBlock; }
 
 bool decode128_supported(const mla_params_t &p) {
-    return decode_mfma_supported(p) && p.kv_dtype == MLA_BF16 && (p.Sq * p.H) % kRows == 0;
+    return decode_mfma_supported(p) && (p.kv_dtype == MLA_BF16 || p.kv_dtype == MLA_FP8_E4M3) &&
+           (p.Sq * p.H) % kRows == 0;
 }
 
 hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
-                            float *lse_part, hipStream_t stream) {
+                            const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                            const int32_t *seq_lens, void *o_part, float *lse_part, hipStream_t stream) {
     const int64_t parts = p.num_parts > 0 ? p.num_parts : static_cast<int64_t>(p.B) * p.num_splits;
     const int64_t n_rg = (static_cast<int64_t>(p.Sq) * p.H) / kRows;
-    const int64_t blocks = ((parts + 7) / 8) * 8 * n_rg;
-    hipLaunchKernelGGL(decode128_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
-                       static_cast<const uint16_t *>(q_abs), static_cast<const uint16_t *>(q_rope),
-                       static_cast<const char *>(c_kv), static_cast<const uint16_t *>(k_pe), block_table, seq_lens,
-                       o_part, lse_part);
+    const dim3 grid(static_cast<unsigned>(((parts + 7) / 8) * 8 * n_rg));
+    const auto qa = static_cast<const uint16_t *>(q_abs);
+    const auto qr = static_cast<const uint16_t *>(q_rope);
+    const auto kv = static_cast<const char *>(c_kv);
+    const auto kp = static_cast<const uint16_t *>(k_pe);
+    if (p.kv_dtype == MLA_FP8_E4M3)
+        hipLaunchKernelGGL(decode128_kernel<true>, grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp, kv_scale,
+                           block_table, seq_lens, o_part, lse_part);
+    else
+        hipLaunchKernelGGL(decode128_kernel<false>, grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp, kv_scale,
+                           block_table, seq_lens, o_part, lse_part);
     return hipGetLastError();
 }
 

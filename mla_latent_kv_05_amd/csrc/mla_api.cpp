@@ -226,7 +226,7 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
                              : rows * p->num_splits;
     if (grid > 0x7fffffffll) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: grid of %lld workgroups too large", (long long)grid);
     if (mla::decode128_supported(*p))
-        return hip_status(mla::launch_decode128(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
+        return hip_status(mla::launch_decode128(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, o_part,
                                                 lse_part, st),
                           "mla_decode_splitkv launch");
     if (mla::decode8_supported(*p))

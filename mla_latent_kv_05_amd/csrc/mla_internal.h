@@ -70,12 +70,12 @@ hipError_t launch_prefill_attention(const mla_params_t &p, const void *q_nope, c
 // Heads x query rows handled by one attention workgroup of the e4m3 kernel
 // (kernels_decode.hip) and of the eight-wave bf16 kernel (kernels_decode8.hip).
 constexpr int kDecodeRowsPerBlock = 64;
-// ... of the four-wave bf16 kernel (kernels_decode128.hip).
+// ... of the four-wave kernel (kernels_decode128.hip; bf16 and e4m3 caches).
 constexpr int kDecodeRowsPerGroup = 128;
 bool decode128_supported(const mla_params_t &p);
 hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
-                            const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
-                            float *lse_part, hipStream_t stream);
+                            const void *k_pe, const float *kv_scale, const int32_t *block_table,
+                            const int32_t *seq_lens, void *o_part, float *lse_part, hipStream_t stream);
 // Balanced parts are cut in units of work: a sequence with n > 0 pages costs
 // kSeqStartCost + n units, its start cost first, then one unit per page; an empty
 // sequence costs nothing.  The batch's units, taken in sequence order, are cut into

@@ -169,6 +169,47 @@ def test_decode_bf16_partials(wl_name, over, lens, num_parts, flags):
     assert np.array_equal(o16[full], want)
 
 
+@pytest.mark.parametrize("lens,split_pages,num_parts,part", [
+    ([1, 66, 700, 9000], 1000, 0, mla.F32),     # whole sequences: a 141-page segment
+    ([4, 129, 700, 0], 2, 0, mla.F32),
+    ([5000, 3, 2, 4100], None, 16, mla.BF16),   # balanced parts, bf16 partials
+    ([33, 64, 95, 10], 1, 0, mla.BF16),         # ragged last tiles, one page per split
+])
+def test_e4m3_partials_equal_those_of_the_expanded_cache(lens, split_pages, num_parts, part):
+    """The kernel that reads the e4m3 cache converts each code as mla_expand_kv does
+    (bf16 of the code times its token's scale): its partials equal, bit for bit,
+    those of the bf16 kernel on the expanded cache, and match the oracle."""
+    wl = I.workload("v3_sq4_fp8", B=len(lens))
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, split_pages=split_pages, num_parts=num_parts, part_dtype=part)
+    note(f"e4m3 vs expanded lens={lens} sp={split_pages} P={num_parts} S={p.num_splits} "
+         f"kernel={mla.decode_kernel_name(p)}")
+    dc = DeviceCase(case)
+    q_abs = I.random_q_abs(wl, seed=123).cuda()
+    rows = (wl.B, wl.Sq, wl.H)
+    pdt = torch.bfloat16 if part == mla.BF16 else torch.float32
+    res = []
+    kv16 = torch.empty((case.num_pages, 64, wl.d_c), dtype=torch.bfloat16, device="cuda")
+    mla.expand_kv(p, dc.c_kv, dc.kv_scale, kv16)
+    pb = p.copy()
+    pb.kv_dtype = mla.BF16
+    for pp, ckv, scl in ((p, dc.c_kv, dc.kv_scale), (pb, kv16, None)):
+        o_part = torch.zeros(rows + (p.num_splits, wl.d_c), dtype=pdt, device="cuda")
+        lse_part = torch.full(rows + (p.num_splits,), float("nan"), device="cuda")
+        mla.decode_splitkv(pp, q_abs, dc.q_rope, ckv, dc.k_pe, scl, dc.block_table, dc.seq_lens, o_part, lse_part)
+        res.append((o_part.float().cpu(), lse_part.cpu()))
+    torch.cuda.synchronize()
+    (o8, l8), (o16, l16) = res
+    assert torch.equal(l8, l16)
+    assert torch.equal(o8, o16)
+    if part == mla.F32 and max(lens) <= 1000:
+        beg, end = split_page_ranges(case.seq_lens.numpy(), p)
+        ref_o, ref_l = O.decode_page_ranges(O.dims_of(case), q_abs.cpu(), case.q_rope, case.c_kv, case.kv_scale,
+                                            case.k_pe, case.block_table, case.seq_lens, beg, end)
+        check_partials(wl, o8.numpy(), l8.numpy(), ref_o, ref_l)
+
+
 @pytest.mark.parametrize("wl_name,S,part", [("v3_b64", 7, mla.F32), ("tiny", 3, mla.F32), ("v3_sq4_fp8", 40, mla.F32),
                                              ("v3_b64", 7, mla.BF16), ("tiny", 3, mla.BF16), ("v3_b64", 70, mla.BF16)])
 def test_combine_lse(wl_name, S, part):
@@ -252,8 +293,16 @@ def test_step_matches_oracle(wl_name, over, lens):
     vis = lse > -np.inf
     # lse: a row that sees one position returns that one score, whose error from the
     # bf16 absorbed query is about scale * 2^-9 * |q_abs| / sqrt(3) ~ 4e-4 (one sigma)
-    # at these distributions; with many new tokens such rows exist, so 4e-3 (10 sigma)
-    lse_tol = 1e-5 if wl.dtype == "f32" else (4e-3 if wl.Sq >= 16 else 2e-3)
+    # at these distributions; with many new tokens such rows exist, so 4e-3 (10 sigma).
+    # e4m3: the cache enters the product as bf16(code x scale), a second rounding of
+    # the same size (one score: about 6e-4 from either rounding, 9e-4 from both), so
+    # 6e-3 (7 sigma).
+    if wl.dtype == "f32":
+        lse_tol = 1e-5
+    elif wl.dtype == "fp8":
+        lse_tol = 6e-3
+    else:
+        lse_tol = 4e-3 if wl.Sq >= 16 else 2e-3
     assert np.abs(st.lse.cpu().numpy()[vis] - lse[vis]).max() <= lse_tol
     assert np.all(st.lse.cpu().numpy()[~vis] == -np.inf)
 
@@ -351,6 +400,59 @@ def test_degenerate_lengths():
     assert np.array_equal(got_l == -np.inf, lse == -np.inf)
     assert np.all(st.out.cpu().numpy()[lse == -np.inf] == 0)
     assert err_rms(st.out.cpu().numpy(), out) <= TOL["fp8"]
+
+
+def rising_case(name, factor=64.0):
+    """Two sequences whose tokens past the first page have their latent and RoPE
+    rows scaled by `factor` (e4m3: the token scales), so that the scores of a split
+    starting at page 0 rise far above the maximum of its first tile, and those of
+    later splits rise by varying amounts.  e4m3: the token scales are rounded to
+    powers of two first, so that code x scale is exact in bf16 (scores of a few
+    hundred would otherwise turn the cache's bf16 rounding into large weight errors)."""
+    wl = I.workload(name, B=2)
+    case = I.make_case(wl, seq_lens=[700, 300])
+    if case.kv_scale is not None:
+        case.kv_scale = torch.exp2(torch.round(torch.log2(case.kv_scale)))
+    pages = set()
+    for b, n in enumerate(case.seq_lens.tolist()):
+        pages.update(int(x) for x in case.block_table[b, 1:-(-n // 64)].tolist())
+    idx = torch.tensor(sorted(pages), dtype=torch.int64)
+    if case.kv_scale is not None:
+        case.kv_scale[idx] *= factor
+    else:
+        case.c_kv[idx] = (case.c_kv[idx].float() * factor).to(case.c_kv.dtype)
+    case.k_pe[idx] = (case.k_pe[idx].float() * factor).to(case.k_pe.dtype)
+    return case
+
+
+def first_tile_excess(case, q_abs, b, n_split_tokens):
+    """Per query row of sequence b: the largest score (log2 units) among its first
+    n_split_tokens tokens minus the largest among the first 32."""
+    qa = O.decode_values(q_abs)[b]
+    qr = O.decode_values(case.q_rope)[b]
+    n = int(case.seq_lens[b])
+    pages = case.block_table[b, :-(-n // 64)].tolist()
+    c = np.concatenate([O.cache_values(case)[pg] for pg in pages])[:n_split_tokens]
+    k = np.concatenate([O.decode_values(case.k_pe)[pg] for pg in pages])[:n_split_tokens]
+    z = (np.einsum("shc,tc->sht", qa, c) + np.einsum("shr,tr->sht", qr, k)) * case.wl.scale / math.log(2)
+    return z.max(-1) - z[..., :32].max(-1)
+
+
+@pytest.mark.parametrize("name", ["v3_b64", "v3_sq4_fp8"])
+def test_second_pass_when_scores_rise_along_a_split(name):
+    """Scores that rise along a split by more than 2^64 over the maximum of its first
+    tile make the bf16 and e4m3 kernels compute the split again with the split's own
+    maximum as the reference: the partials stay finite and match the oracle (run on
+    the same bf16 q_abs, so that scores of a few hundred do not magnify its rounding)."""
+    case = rising_case(name)
+    q_abs = I.random_q_abs(case.wl, seed=123)              # the q_abs run_decode passes
+    assert first_tile_excess(case, q_abs, 0, 256).min() > 64   # every row of split 0 of sequence 0
+    for split_pages in (4, 16):
+        p = params_for(case, split_pages=split_pages)
+        note(f"{name} rising scores split_pages={split_pages} kernel={mla.decode_kernel_name(p)}")
+        o, l, ref_o, ref_l = run_decode(case, p)
+        assert np.isfinite(o[ref_l != -np.inf]).all() and not np.isnan(l).any()
+        check_partials(case.wl, o, l, ref_o, ref_l)
 
 
 def test_wide_block_table_and_unreferenced_pages():
