@@ -66,6 +66,15 @@ typedef enum {
 
 /* Flags (mla_params_t.flags). */
 #define MLA_FLAG_GENERIC 1u  /* use the fp32 VALU kernels even where MFMA kernels apply */
+/* Attention kernel for a bf16 cache where both MFMA kernels apply (Sq*H a multiple
+ * of 128).  By default the four-wave kernel (128 query rows per workgroup) runs,
+ * unless its grid would hold at most 128 workgroups (a small batch): the eight-wave
+ * kernel (64 rows per workgroup, twice the workgroups) then runs instead.  These
+ * bits force one of them (not both; a forced kernel that cannot take *p makes
+ * mla_decode_splitkv return MLA_ERR_UNSUPPORTED).  Both compute the same softmax
+ * and partials up to rounding. */
+#define MLA_FLAG_ROWS64 2u   /* the eight-wave kernel (bf16 cache, Sq*H a multiple of 64) */
+#define MLA_FLAG_ROWS128 4u  /* the four-wave kernel (bf16 or e4m3 cache, Sq*H a multiple of 128) */
 
 /*
  * Problem description shared by the four calls.
@@ -445,8 +454,10 @@ mla_status_t mla_device_errors(uint32_t *bits, void *stream);
 /* 1 when this library was built with the MLA_DEBUG_BOUNDS device checks, else 0. */
 int32_t mla_debug_bounds(void);
 
-/* Name of the kernel family mla_decode_splitkv would use for *p:
- * "mfma_bf16", "mfma_fp8" or "generic_f32" (host-only). */
+/* Name of the attention kernel mla_decode_splitkv would launch for *p (host-only):
+ * "mfma_bf16_128" / "mfma_fp8_128" (four waves, 128 query rows per workgroup),
+ * "mfma_bf16_64" (eight waves, 64 rows), "mfma_fp8_64" (e4m3 cache, four waves, 64
+ * rows), "generic_f32" (fp32 VALU), or "invalid" (bad parameters or flags). */
 const char *mla_decode_kernel_name(const mla_params_t *p);
 
 /* Static string for a status code. */

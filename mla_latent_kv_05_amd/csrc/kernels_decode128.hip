@@ -749,7 +749,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
 
 }  // namespace
 
-int decode_rows_per_workgroup(const mla_params_t &p) { return decode128_supported(p) ? kRows : kDecodeRowsPerBlock; }
+// Workgroups at or below which a bf16 launch goes to the eight-wave kernel: with at
+// most one 128-row workgroup per two compute units, twice as many 64-row workgroups
+// (each loading half the query rows and storing half the partials) still fit at
+// once and finish sooner (B = 1, 4,096 positions, 32 parts: 18 us against 26 us).
+constexpr int64_t kSmallGrid128 = 128;
+
+DecodeKernel decode_kernel_for(const mla_params_t &p) {
+    const bool k128 = decode128_supported(p), k8 = decode8_supported(p);
+    if (k128 && (p.flags & MLA_FLAG_ROWS128)) return DecodeKernel::k128;
+    if (k8 && (p.flags & MLA_FLAG_ROWS64)) return DecodeKernel::k8;
+    if (k128 && k8) {
+        const int64_t parts = p.num_parts > 0 ? p.num_parts : static_cast<int64_t>(p.B) * p.num_splits;
+        return parts * ((static_cast<int64_t>(p.Sq) * p.H) / kRows) <= kSmallGrid128 ? DecodeKernel::k8
+                                                                                        : DecodeKernel::k128;
+    }
+    return k128 ? DecodeKernel::k128 : k8 ? DecodeKernel::k8 : DecodeKernel::kMfma64;
+}
+
+int decode_rows_per_workgroup(const mla_params_t &p) {
+    return decode_kernel_for(p) == DecodeKernel::k128 ? kRows : kDecodeRowsPerBlock;
+}
 
 bool decode128_supported(const mla_params_t &p) {
     return decode_mfma_supported(p) && (p.kv_dtype == MLA_BF16 || p.kv_dtype == MLA_FP8_E4M3) &&

@@ -304,13 +304,18 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
 // weight rows, which were loaded before the merge.
 // ---------------------------------------------------------------------------
 constexpr int kCuRowsPerWave = kUpRows / 8;
+constexpr int kFewRows = 8;                      // rows per head up to which the whole workgroup merges one row
 
-template <bool kOutBf16, bool kPartBf16>
+template <bool kOutBf16, bool kPartBf16, bool kFew>
 __global__ __launch_bounds__(512) void combine_up_v_kernel(
     const mla_params_t p, const void *__restrict__ o_part, const float *__restrict__ lse_part,
     const uint16_t *__restrict__ W_UV, void *__restrict__ out, float *__restrict__ lse_out) {
     constexpr int kDh = 128;
-    __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2];
+    constexpr int kEb = kPartBf16 ? 2 : 4;
+    // kFew (at most kFewRows rows per head): partial rows staged in LDS, kSlots at a time
+    constexpr int kSlots = kPartBf16 ? 64 : 32;
+    constexpr int kStageBytes = kFew ? kSlots * kDc * kEb : 0;
+    __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2 + kStageBytes];
     const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = p.B * p.Sq;
@@ -322,8 +327,90 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     const int r0 = rc * kUpRows;
     const int d0 = w * 16;
     const uint32_t sm = lds_addr(smem);
-    // merge rows rr = w + 8i: lane owns latent columns 8 lane .. 8 lane + 7
     const int S = p.num_splits;
+    // this wave's weights (16 rows d0 ..), in flight during the merge
+    const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
+    bf16x8 wa[kDc / 32];
+    auto load_weights = [&] {
+#pragma unroll
+        for (int ks = 0; ks < kDc / 32; ++ks)
+            wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
+    };
+    if constexpr (kFew) {
+        // At most kFewRows rows (r0 = 0), one at a time, with the whole workgroup: every
+        // wave finds the row's live splits from its lse values, the waves load the live
+        // partial rows into LDS together (one round trip for up to kSlots splits), and
+        // lane l of wave w then sums latent column 64w + l over them in split order --
+        // per column the arithmetic and order of combine_kernel_512.
+        const uint32_t stg = sm + kUpRows * kDc * 2;
+        const int col = w * 64 + lane;
+        auto lse_at = [&](int64_t rowi, int c0) {
+            const float v = lse_part[rowi * S + min(c0 + lane, S - 1)];
+            return c0 + lane < S ? v : -INFINITY;
+        };
+        const float l_row0 = lse_at(h, 0);             // issued before the weights (loads complete in order)
+        load_weights();
+        for (int rr = 0; rr < R; ++rr) {
+            const int64_t rowi = static_cast<int64_t>(rr) * p.H + h;
+            const float l_c0 = rr == 0 ? l_row0 : lse_at(rowi, 0);
+            float mx = l_c0;
+            for (int c0 = 64; c0 < S; c0 += 64) mx = fmaxf(mx, lse_at(rowi, c0));
+            mx = wave_max_f(mx);
+            float sum = 0.f, acc = 0.f;
+            for (int c0 = 0; c0 < S; c0 += 64) {
+                const float lc = c0 == 0 ? l_c0 : lse_at(rowi, c0);
+                const float wt = (lc == -INFINITY || mx == -INFINITY) ? 0.f : __expf(lc - mx);
+                sum += wt;
+                const uint64_t live = __builtin_amdgcn_ballot_w64(wt != 0.f);
+#pragma unroll
+                for (int cb = 0; cb < 64; cb += kSlots) {
+                    const uint64_t lv = (live >> cb) & (kSlots == 64 ? ~0ull : (1ull << kSlots) - 1);
+                    if (!lv) continue;
+                    __syncthreads();                   // the previous round's LDS reads are done
+                    // wave w stages splits c0 + cb + 8q + w of this round
+                    u32x4 x[kSlots / 8][kEb / 2];
+#pragma unroll
+                    for (int q = 0; q < kSlots / 8; ++q) {
+                        const int k = 8 * q + w;
+                        if ((lv >> k) & 1) {
+                            const char *src = static_cast<const char *>(o_part) +
+                                              ((rowi * S + c0 + cb + k) * kDc + lane * 8) * kEb;
+#pragma unroll
+                            for (int e = 0; e < kEb / 2; ++e) x[q][e] = reinterpret_cast<const u32x4 *>(src)[e];
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < kSlots / 8; ++q) {
+                        const int k = 8 * q + w;
+                        if ((lv >> k) & 1)
+#pragma unroll
+                            for (int e = 0; e < kEb / 2; ++e)
+                                lds_store<u32x4>(stg + (k * kDc + lane * 8) * kEb + 16 * e, x[q][e]);
+                    }
+                    __syncthreads();
+                    uint64_t m2 = lv;
+                    while (m2) {
+                        const int k = __builtin_ctzll(m2);
+                        m2 &= m2 - 1;
+                        const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt), cb + k));
+                        float v;
+                        if constexpr (kPartBf16)
+                            v = __uint_as_float(static_cast<uint32_t>(lds_load<uint16_t>(stg + (k * kDc + col) * 2)) << 16);
+                        else
+                            v = lds_load<float>(stg + (k * kDc + col) * 4);
+                        acc += wk * v;
+                    }
+                }
+            }
+            const float tot = wave_sum_f(sum);
+            const float inv = tot > 0.f ? 1.f / tot : 0.f;
+            lds_store<uint16_t>(sm + rr * 1024 + (((col >> 3) ^ (rr & 15)) << 4) + (col & 7) * 2,
+                                static_cast<uint16_t>(pack_bf16x2(acc * inv, 0.f) & 0xffffu));
+            if (lse_out && w == 0 && lane == 0) lse_out[rowi] = mx == -INFINITY ? -INFINITY : mx + __logf(tot);
+        }
+        for (int rr = R + w; rr < kUpRows; rr += 8) lds_store<u32x4>(sm + rr * 1024 + 16 * lane, u32x4{0u, 0u, 0u, 0u});
+    } else {
+    // merge rows rr = w + 8i: lane owns latent columns 8 lane .. 8 lane + 7
     int64_t row[kCuRowsPerWave];
     bool ok[kCuRowsPerWave];
     float mx[kCuRowsPerWave], sum[kCuRowsPerWave], acc[kCuRowsPerWave][8];
@@ -345,7 +432,6 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         return ok[i] && c0 + lane < S ? v : -INFINITY;
     };
     // each row's partials as a raw buffer of S * d_c elements
-    constexpr int kEb = kPartBf16 ? 2 : 4;
     __amdgpu_buffer_rsrc_t prow[kCuRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kCuRowsPerWave; ++i)
@@ -360,14 +446,9 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         l0[i] = ok[i] && lane < S ? l0[i] : -INFINITY;
         mx[i] = l0[i];
     }
-    // this wave's weights (16 rows d0 ..), issued after the split lse values (loads
-    // complete in order: waiting for the lse values does not wait for the weights),
-    // in flight during the merge
-    const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
-    bf16x8 wa[kDc / 32];
-#pragma unroll
-    for (int ks = 0; ks < kDc / 32; ++ks)
-        wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
+    // the weights, issued after the split lse values (loads complete in order:
+    // waiting for the lse values does not wait for the weights)
+    load_weights();
     for (int c0 = 64; c0 < S; c0 += 64)
 #pragma unroll
         for (int i = 0; i < kCuRowsPerWave; ++i) mx[i] = fmaxf(mx[i], lse_of(i, c0));
@@ -478,6 +559,7 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
         lds_store<u32x4>(sm + rr * 1024 + ((lane ^ (rr & 15)) << 4), o);     // zero rows past R
         if (lse_out && ok[i] && lane == 0) lse_out[row[i]] = mx[i] == -INFINITY ? -INFINITY : mx[i] + __logf(tot);
     }
+    }
     __syncthreads();
 
     constexpr int kRt = kUpRows / 16;             // 16-row tiles
@@ -520,14 +602,24 @@ hipError_t launch_combine_up_v(const mla_params_t &p, const void *o_part, const 
     const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(p.H) + 7) / 8 * 8 * ((R + kUpRows - 1) / kUpRows)));
     const auto w = static_cast<const uint16_t *>(W_UV);
     const bool ob = p.out_dtype == MLA_BF16, pb = p.part_dtype == MLA_BF16;
-    if (ob && pb)
-        hipLaunchKernelGGL((combine_up_v_kernel<true, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
-    else if (ob)
-        hipLaunchKernelGGL((combine_up_v_kernel<true, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
-    else if (pb)
-        hipLaunchKernelGGL((combine_up_v_kernel<false, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
-    else
-        hipLaunchKernelGGL((combine_up_v_kernel<false, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, w, out, lse_out);
+    const bool few = R <= kFewRows;
+#define MLA_CUV(OB, PB)                                                                                          \
+    if (few)                                                                                                     \
+        hipLaunchKernelGGL((combine_up_v_kernel<OB, PB, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, \
+                           w, out, lse_out);                                                                     \
+    else                                                                                                         \
+        hipLaunchKernelGGL((combine_up_v_kernel<OB, PB, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, \
+                           w, out, lse_out);
+    if (ob && pb) {
+        MLA_CUV(true, true)
+    } else if (ob) {
+        MLA_CUV(true, false)
+    } else if (pb) {
+        MLA_CUV(false, true)
+    } else {
+        MLA_CUV(false, false)
+    }
+#undef MLA_CUV
     return hipGetLastError();
 }
 

@@ -75,7 +75,10 @@ mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
     if (!is_float_dtype(p->latent_dtype)) return fail(MLA_ERR_DTYPE, "latent_dtype must be F32 or BF16");
     if (!is_float_dtype(p->out_dtype)) return fail(MLA_ERR_DTYPE, "out_dtype must be F32 or BF16");
     if (!is_float_dtype(p->part_dtype)) return fail(MLA_ERR_DTYPE, "part_dtype must be F32 or BF16");
-    if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC)) return fail(MLA_ERR_SHAPE, "unknown flag bits 0x%x", p->flags);
+    if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC | MLA_FLAG_ROWS64 | MLA_FLAG_ROWS128))
+        return fail(MLA_ERR_SHAPE, "unknown flag bits 0x%x", p->flags);
+    if ((p->flags & MLA_FLAG_ROWS64) && (p->flags & MLA_FLAG_ROWS128))
+        return fail(MLA_ERR_SHAPE, "MLA_FLAG_ROWS64 and MLA_FLAG_ROWS128 together");
     return MLA_OK;
 }
 
@@ -132,8 +135,13 @@ mla_status_t mla_check_params(const mla_params_t *p) { return check(p); }
 
 const char *mla_decode_kernel_name(const mla_params_t *p) {
     if (!p || check(p) != MLA_OK) return "invalid";
-    if (mla::decode_mfma_supported(*p)) return p->kv_dtype == MLA_FP8_E4M3 ? "mfma_fp8" : "mfma_bf16";
-    return "generic_f32";
+    if (!mla::decode_mfma_supported(*p)) return "generic_f32";
+    switch (mla::decode_kernel_for(*p)) {
+    case mla::DecodeKernel::k128: return p->kv_dtype == MLA_FP8_E4M3 ? "mfma_fp8_128" : "mfma_bf16_128";
+    case mla::DecodeKernel::k8: return "mfma_bf16_64";
+    case mla::DecodeKernel::kMfma64: return "mfma_fp8_64";
+    }
+    return "invalid";
 }
 
 mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total_tokens,
@@ -147,9 +155,14 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     const int64_t pages_lo = (total_tokens + page - 1) / page;   // <= the batch's true page count
     // one workgroup per compute unit: each part is processed by Sq*H/64 workgroups
     // on the MFMA path (one per (row, split) on the generic path)
+    // (the 128-row kernel's workgroups when it applies: a plan that leaves it few
+    // workgroups sends a bf16 launch to the 64-row kernel, with twice as many)
     const bool mfma = mla::decode_mfma_supported(*p);
     const int64_t rows = (int64_t)p->Sq * p->H;
-    const int64_t wg_per_part = mfma ? std::max<int64_t>(1, rows / mla::decode_rows_per_workgroup(*p)) : rows;
+    const int64_t wg_per_part =
+        mfma ? std::max<int64_t>(1, rows / (mla::decode128_supported(*p) ? mla::kDecodeRowsPerGroup
+                                                                         : mla::kDecodeRowsPerBlock))
+             : rows;
     int64_t P = std::max<int64_t>(1, num_cus / wg_per_part);
     if (!mfma) P = std::max<int64_t>(1, 2ll * num_cus / wg_per_part);
     // at least 8 parts even when that takes several rounds of workgroups (many query
@@ -225,18 +238,25 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
                              ? (parts + 7) / 8 * 8 * (rows / p->B / mla::decode_rows_per_workgroup(*p))
                              : rows * p->num_splits;
     if (grid > 0x7fffffffll) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: grid of %lld workgroups too large", (long long)grid);
-    if (mla::decode128_supported(*p))
-        return hip_status(mla::launch_decode128(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, o_part,
-                                                lse_part, st),
-                          "mla_decode_splitkv launch");
-    if (mla::decode8_supported(*p))
-        return hip_status(mla::launch_decode8(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
-                                              lse_part, st),
-                          "mla_decode_splitkv launch");
-    if (mla::decode_mfma_supported(*p))
+    if (mla::decode_mfma_supported(*p)) {
+        const mla::DecodeKernel k = mla::decode_kernel_for(*p);
+        if (((p->flags & MLA_FLAG_ROWS128) && k != mla::DecodeKernel::k128) ||
+            ((p->flags & MLA_FLAG_ROWS64) && k != mla::DecodeKernel::k8))
+            return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: the forced attention kernel does not take these parameters");
+        if (k == mla::DecodeKernel::k128)
+            return hip_status(mla::launch_decode128(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens,
+                                                    o_part, lse_part, st),
+                              "mla_decode_splitkv launch");
+        if (k == mla::DecodeKernel::k8)
+            return hip_status(mla::launch_decode8(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
+                                                  lse_part, st),
+                              "mla_decode_splitkv launch");
         return hip_status(mla::launch_decode_mfma(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table,
                                                   seq_lens, o_part, lse_part, st),
                           "mla_decode_splitkv launch");
+    }
+    if (p->flags & (MLA_FLAG_ROWS64 | MLA_FLAG_ROWS128))
+        return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a forced MFMA attention kernel does not take these parameters");
     return hip_status(mla::launch_decode_generic(*p, q_abs, q_rope, c_kv, k_pe, kv_scale, block_table,
                                                  seq_lens, o_part, lse_part, st),
                       "mla_decode_splitkv launch");

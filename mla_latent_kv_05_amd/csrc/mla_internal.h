@@ -87,7 +87,12 @@ hipError_t take_errors_generic(uint32_t *bits);
 hipError_t take_errors_decode_mfma(uint32_t *bits);
 hipError_t take_errors_decode8(uint32_t *bits);
 hipError_t take_errors_decode128(uint32_t *bits);
-// query rows per attention workgroup for the kernel mla_decode_splitkv picks
+// the attention kernel mla_decode_splitkv launches for p (MFMA path): the
+// four-wave 128-row kernel, else the eight-wave 64-row kernel (bf16), else the
+// four-wave 64-row kernel (e4m3)
+enum class DecodeKernel { k128, k8, kMfma64 };
+DecodeKernel decode_kernel_for(const mla_params_t &p);
+// query rows per attention workgroup of that kernel
 int decode_rows_per_workgroup(const mla_params_t &p);
 
 }  // namespace mla

@@ -20,6 +20,8 @@ DEBUG_LIB_PATH = os.path.join(PKG, "libmla_debug.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 FLAG_GENERIC = 1
+FLAG_ROWS64 = 2       # force the eight-wave 64-row attention kernel (bf16 cache)
+FLAG_ROWS128 = 4      # force the four-wave 128-row attention kernel
 PAGE = 64
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",

@@ -60,7 +60,7 @@ def test_valid_params_pass():
     ("d_r", -1, 2), ("page_size", 32, 2), ("num_pages", 0, 2), ("max_pages", 0, 2),
     ("num_splits", 0, 4), ("num_splits", 5000, 4), ("split_pages", 0, 4), ("scale", 0.0, 2),
     ("scale", float("inf"), 2), ("q_dtype", 2, 3), ("w_dtype", 7, 3), ("kv_dtype", 3, 3),
-    ("pe_dtype", 2, 3), ("latent_dtype", 2, 3), ("out_dtype", -1, 3), ("flags", 4, 2),
+    ("pe_dtype", 2, 3), ("latent_dtype", 2, 3), ("out_dtype", -1, 3), ("flags", 8, 2), ("flags", 6, 2),
     ("num_parts", -1, 4), ("num_parts", 1 << 21, 4),
 ])
 def test_invalid_params_rejected(field, value, status):
@@ -170,8 +170,16 @@ def test_status_strings():
 
 
 def test_kernel_dispatch_names():
-    assert mla.decode_kernel_name(v3()) == "mfma_bf16"
-    assert mla.decode_kernel_name(v3(kv_dtype=mla.FP8_E4M3, Sq=4)) == "mfma_fp8"
+    # B=2 x 2 splits: 4 workgroups of the 128-row kernel, a small grid -> 64 rows
+    assert mla.decode_kernel_name(v3()) == "mfma_bf16_64"
+    assert mla.decode_kernel_name(v3(B=64, num_splits=2)) == "mfma_bf16_64"          # 128 workgroups
+    assert mla.decode_kernel_name(v3(B=65, num_splits=2)) == "mfma_bf16_128"         # 130 workgroups
+    assert mla.decode_kernel_name(v3(flags=mla.FLAG_ROWS128)) == "mfma_bf16_128"
+    assert mla.decode_kernel_name(v3(B=65, num_splits=2, flags=mla.FLAG_ROWS64)) == "mfma_bf16_64"
+    assert mla.decode_kernel_name(v3(kv_dtype=mla.FP8_E4M3, Sq=4)) == "mfma_fp8_128"   # no 64-row bf16 kernel
+    assert mla.decode_kernel_name(v3(kv_dtype=mla.FP8_E4M3, H=64)) == "mfma_fp8_64"    # 64 rows: not 128
+    assert mla.decode_kernel_name(v3(H=64)) == "mfma_bf16_64"
+    assert mla.decode_kernel_name(v3(flags=mla.FLAG_ROWS64 | mla.FLAG_ROWS128)) == "invalid"
     assert mla.decode_kernel_name(v3(flags=mla.FLAG_GENERIC)) == "generic_f32"
     tiny = mla.make_params(1, 1, 8, 32, 64, 16, 2, 2, q_dtype=mla.F32, w_dtype=mla.F32,
                            kv_dtype=mla.F32, pe_dtype=mla.F32, latent_dtype=mla.F32)

@@ -37,7 +37,8 @@ def decode(L, p, dc, q_abs, block_table=None, seq_lens=None):
     return o, lse, mla.device_errors(L=L)
 
 
-CASES = [("v3_b64", {}, 0), ("v3_b64", {"H": 64}, 0), ("v3_sq4_fp8", {}, 0), ("v3_b64", {}, mla.FLAG_GENERIC)]
+CASES = [("v3_b64", {}, mla.FLAG_ROWS128), ("v3_b64", {}, mla.FLAG_ROWS64), ("v3_b64", {"H": 64}, 0),
+         ("v3_sq4_fp8", {}, 0), ("v3_b64", {}, mla.FLAG_GENERIC)]
 
 
 @pytest.mark.parametrize("wl_name,over,flags", CASES)

@@ -28,6 +28,11 @@ def note(msg):
     (1, 1, 1, mla.F32, True, mla.F32),        # one row, one split
     (64, 1, 3, mla.F32, True, mla.BF16),      # bf16 partials
     (37, 4, 70, mla.F32, True, mla.BF16),
+    # at most 8 rows per head: the whole workgroup merges one row at a time
+    (1, 1, 32, mla.F32, True, mla.BF16),      # one row, 32 splits (B = 1 decode)
+    (8, 1, 64, mla.BF16, True, mla.BF16),     # 8 rows, 64 splits
+    (2, 4, 130, mla.F32, True, mla.BF16),     # 8 rows, three groups of 64 splits
+    (3, 1, 40, mla.F32, True, mla.F32),       # fp32 partials: 32 staged per round
 ])
 def test_combine_up_v_equals_two_calls(B, Sq, S, out_dtype, with_lse, part):
     wl = I.workload("v3_b64", B=B, Sq=Sq)

@@ -68,7 +68,9 @@ def test_absorb_q(wl_name, R, flags):
         assert_bf16_rounding(qa.float().cpu().numpy(), ref)
 
 
-def run_decode(case, p):
+def run_decode(case, p, ref=None):
+    """The kernel's partials for p and the oracle's (ref: those of an earlier call
+    with the same plan, reused)."""
     dc = DeviceCase(case)
     q_abs = I.random_q_abs(case.wl, seed=123)
     S = p.num_splits
@@ -79,10 +81,19 @@ def run_decode(case, p):
     mla.decode_splitkv(p, q_abs.cuda(), dc.q_rope, dc.c_kv, dc.k_pe, dc.kv_scale, dc.block_table,
                        dc.seq_lens, o_part, lse_part)
     torch.cuda.synchronize()
-    beg, end = split_page_ranges(case.seq_lens.numpy(), p)
-    ref_o, ref_l = O.decode_page_ranges(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
-                                        case.k_pe, case.block_table, case.seq_lens, beg, end)
-    return o_part.float().cpu().numpy(), lse_part.cpu().numpy(), ref_o, ref_l
+    if ref is None:
+        beg, end = split_page_ranges(case.seq_lens.numpy(), p)
+        ref = O.decode_page_ranges(O.dims_of(case), q_abs, case.q_rope, case.c_kv, case.kv_scale,
+                                   case.k_pe, case.block_table, case.seq_lens, beg, end)
+    return o_part.float().cpu().numpy(), lse_part.cpu().numpy(), ref[0], ref[1]
+
+
+def kernel_variants(wl, flags):
+    """Flag sets to run: where both bf16 attention kernels take the workload, each of
+    them forced (small test grids would otherwise always get the 64-row kernel)."""
+    if flags == 0 and wl.dtype == "bf16" and (wl.Sq * wl.H) % 128 == 0:
+        return [mla.FLAG_ROWS128, mla.FLAG_ROWS64]
+    return [flags]
 
 
 def check_partials(wl, o, l, ref_o, ref_l):
@@ -112,11 +123,13 @@ def test_decode_splitkv(wl_name, lens, split_pages, flags):
     wl = I.workload(wl_name, B=len(lens))
     case = I.make_case(wl, seq_lens=lens)
     validate(case)
-    p = params_for(case, split_pages=split_pages, flags=flags)
-    note(f"decode_splitkv {wl_name} lens={lens} sp={split_pages} S={p.num_splits} "
-         f"kernel={mla.decode_kernel_name(p)}")
-    o, l, ref_o, ref_l = run_decode(case, p)
-    check_partials(wl, o, l, ref_o, ref_l)
+    ref = None
+    for fl in kernel_variants(wl, flags):
+        p = params_for(case, split_pages=split_pages, flags=fl)
+        note(f"decode_splitkv {wl_name} lens={lens} sp={split_pages} S={p.num_splits} "
+             f"kernel={mla.decode_kernel_name(p)}")
+        o, l, *ref = run_decode(case, p, ref)
+        check_partials(wl, o, l, *ref)
 
 
 @pytest.mark.parametrize("wl_name,lens,num_parts,extra_slots,flags", [
@@ -135,16 +148,19 @@ def test_decode_balanced_splits(wl_name, lens, num_parts, extra_slots, flags):
     wl = I.workload(wl_name, B=len(lens))
     case = I.make_case(wl, seq_lens=lens)
     validate(case)
-    p = params_for(case, num_parts=num_parts, flags=flags)
-    p.num_splits += extra_slots
-    note(f"balanced {wl_name} lens={lens} P={num_parts} S={p.num_splits} kernel={mla.decode_kernel_name(p)}")
-    o, l, ref_o, ref_l = run_decode(case, p)
-    check_partials(wl, o, l, ref_o, ref_l)
+    ref = None
+    for fl in kernel_variants(wl, flags):
+        p = params_for(case, num_parts=num_parts, flags=fl)
+        p.num_splits += extra_slots
+        note(f"balanced {wl_name} lens={lens} P={num_parts} S={p.num_splits} kernel={mla.decode_kernel_name(p)}")
+        o, l, *ref = run_decode(case, p, ref)
+        check_partials(wl, o, l, *ref)
 
 
 @pytest.mark.parametrize("wl_name,over,lens,num_parts,flags", [
-    ("v3_b64", {}, [1, 63, 64, 65, 200, 700], 5, 0),                  # four-wave kernel, 128 rows
-    ("v3_b64", {"H": 64}, [1, 63, 64, 65, 200, 700], 5, 0),           # eight-wave kernel, 64 rows
+    ("v3_b64", {}, [1, 63, 64, 65, 200, 700], 5, mla.FLAG_ROWS128),   # four-wave kernel, 128 rows
+    ("v3_b64", {}, [1, 63, 64, 65, 200, 700], 5, mla.FLAG_ROWS64),    # eight-wave kernel, 64 rows
+    ("v3_b64", {"H": 64}, [1, 63, 64, 65, 200, 700], 5, 0),           # eight-wave kernel, 64 heads
     ("v3_sq4_fp8", {}, [4, 129, 700, 0], 3, 0),                        # e4m3 cache
     ("v3_b64", {}, [130, 5, 1000], 2, mla.FLAG_GENERIC),              # fp32 VALU kernel
 ])
@@ -194,6 +210,7 @@ def test_e4m3_partials_equal_those_of_the_expanded_cache(lens, split_pages, num_
     mla.expand_kv(p, dc.c_kv, dc.kv_scale, kv16)
     pb = p.copy()
     pb.kv_dtype = mla.BF16
+    pb.flags = mla.FLAG_ROWS128                   # the same kernel (small grids default to 64 rows)
     for pp, ckv, scl in ((p, dc.c_kv, dc.kv_scale), (pb, kv16, None)):
         o_part = torch.zeros(rows + (p.num_splits, wl.d_c), dtype=pdt, device="cuda")
         lse_part = torch.full(rows + (p.num_splits,), float("nan"), device="cuda")
@@ -448,11 +465,13 @@ def test_second_pass_when_scores_rise_along_a_split(name):
     q_abs = I.random_q_abs(case.wl, seed=123)              # the q_abs run_decode passes
     assert first_tile_excess(case, q_abs, 0, 256).min() > 64   # every row of split 0 of sequence 0
     for split_pages in (4, 16):
-        p = params_for(case, split_pages=split_pages)
-        note(f"{name} rising scores split_pages={split_pages} kernel={mla.decode_kernel_name(p)}")
-        o, l, ref_o, ref_l = run_decode(case, p)
-        assert np.isfinite(o[ref_l != -np.inf]).all() and not np.isnan(l).any()
-        check_partials(case.wl, o, l, ref_o, ref_l)
+        ref = None
+        for fl in kernel_variants(case.wl, 0):
+            p = params_for(case, split_pages=split_pages, flags=fl)
+            note(f"{name} rising scores split_pages={split_pages} kernel={mla.decode_kernel_name(p)}")
+            o, l, *ref = run_decode(case, p, ref)
+            assert np.isfinite(o[ref[1] != -np.inf]).all() and not np.isnan(l).any()
+            check_partials(case.wl, o, l, *ref)
 
 
 def test_wide_block_table_and_unreferenced_pages():
