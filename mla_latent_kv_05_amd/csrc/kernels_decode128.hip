@@ -749,12 +749,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
 
 }  // namespace
 
-// Workgroups at or below which a bf16 launch goes to the eight-wave kernel: with at
-// most one 128-row workgroup per two compute units, twice as many 64-row workgroups
-// (each loading half the query rows and storing half the partials) still fit at
-// once and finish sooner (B = 1, 4,096 positions, 32 parts: 18 us against 26 us).
-constexpr int64_t kSmallGrid128 = 128;
-
 DecodeKernel decode_kernel_for(const mla_params_t &p) {
     const bool k128 = decode128_supported(p), k8 = decode8_supported(p);
     if (k128 && (p.flags & MLA_FLAG_ROWS128)) return DecodeKernel::k128;

@@ -272,8 +272,8 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
                     const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), kq[q]));
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[j] += wk * v0[q][j];
-                        acc[4 + j] += wk * v1[q][j];
+                        acc[j] = __builtin_fmaf(wk, v0[q][j], acc[j]);
+                        acc[4 + j] = __builtin_fmaf(wk, v1[q][j], acc[4 + j]);
                     }
                 }
             }
@@ -305,6 +305,7 @@ __global__ __launch_bounds__(256) void combine_kernel_512(
 // ---------------------------------------------------------------------------
 constexpr int kCuRowsPerWave = kUpRows / 8;
 constexpr int kFewRows = 8;                      // rows per head up to which the whole workgroup merges one row
+constexpr int kFewSplit = 2;                     // ... and workgroups per head then (one per CU at 225 VGPRs)
 
 template <bool kOutBf16, bool kPartBf16, bool kFew>
 __global__ __launch_bounds__(512) void combine_up_v_kernel(
@@ -315,44 +316,90 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     // kFew (at most kFewRows rows per head): partial rows staged in LDS, kSlots at a time
     constexpr int kSlots = kPartBf16 ? 64 : 32;
     constexpr int kStageBytes = kFew ? kSlots * kDc * kEb : 0;
-    __shared__ __attribute__((aligned(16))) char smem[kUpRows * kDc * 2 + kStageBytes];
+    constexpr int kLatRows = kFew ? 16 : kUpRows;  // merged rows held for the up-projection
+    __shared__ __attribute__((aligned(16))) char smem[kLatRows * kDc * 2 + kStageBytes];
     const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R = p.B * p.Sq;
     const int n_rc = (R + kUpRows - 1) / kUpRows;
     const int q = blockIdx.x >> 3;
-    const int rc = q % n_rc;
-    const int h = (q / n_rc) * 8 + (blockIdx.x & 7);
+    // kFew: kFewSplit workgroups per head on one XCD (low bits of q), each forming
+    // kDh / kFewSplit of the output dims with its first waves (all of them merge the
+    // rows: the later ones' partial reads mostly hit the shared L2), so that no
+    // compute unit has to pull all of a head's weights through alone
+    constexpr int kProjWaves = kFew ? 8 / kFewSplit : 8;
+    const int half = kFew ? (q % kFewSplit) : 0;
+    const int qh = kFew ? (q / kFewSplit) : q;
+    const int rc = kFew ? 0 : qh % n_rc;
+    const int h = (kFew ? qh : qh / n_rc) * 8 + (blockIdx.x & 7);
     if (h >= p.H) return;                         // grid rounded up to 8 heads
     const int r0 = rc * kUpRows;
-    const int d0 = w * 16;
+    const bool proj = w < kProjWaves;             // waves that form output dims
+    const int d0 = kFew ? half * (kDh / kFewSplit) + w * 16 : w * 16;
     const uint32_t sm = lds_addr(smem);
     const int S = p.num_splits;
     // this wave's weights (16 rows d0 ..), in flight during the merge
     const uint16_t *W = W_UV + static_cast<int64_t>(h) * kDh * kDc;
     bf16x8 wa[kDc / 32];
     auto load_weights = [&] {
+        if (!proj) return;
 #pragma unroll
         for (int ks = 0; ks < kDc / 32; ++ks)
             wa[ks] = *reinterpret_cast<const bf16x8 *>(W + static_cast<int64_t>(d0 + r16) * kDc + ks * 32 + g * 8);
     };
     if constexpr (kFew) {
         // At most kFewRows rows (r0 = 0), one at a time, with the whole workgroup: every
-        // wave finds the row's live splits from its lse values, the waves load the live
-        // partial rows into LDS together (one round trip for up to kSlots splits), and
-        // lane l of wave w then sums latent column 64w + l over them in split order --
-        // per column the arithmetic and order of combine_kernel_512.
-        const uint32_t stg = sm + kUpRows * kDc * 2;
+        // wave finds the row's live splits from its lse values, the waves load the
+        // partial rows into LDS together (with at most kSlots splits, all of them, issued
+        // with the lse values: one round trip per row), and lane l of wave w then sums
+        // latent column 64w + l over the live ones in split order -- per column the
+        // arithmetic and order of combine_kernel_512.
+        const uint32_t stg = sm + kLatRows * kDc * 2;
         const int col = w * 64 + lane;
+        const bool one_round = S <= kSlots;
         auto lse_at = [&](int64_t rowi, int c0) {
             const float v = lse_part[rowi * S + min(c0 + lane, S - 1)];
             return c0 + lane < S ? v : -INFINITY;
         };
-        const float l_row0 = lse_at(h, 0);             // issued before the weights (loads complete in order)
-        load_weights();
+        // wave w's staged splits: c0 + cb + 8q + w
+        u32x4 x[kSlots / 8][kEb / 2];
+        auto load_part = [&](int64_t rowi, int c, int q) {
+            const char *src = static_cast<const char *>(o_part) + ((rowi * S + c) * kDc + lane * 8) * kEb;
+#pragma unroll
+            for (int e = 0; e < kEb / 2; ++e) x[q][e] = reinterpret_cast<const u32x4 *>(src)[e];
+        };
+        auto stage_part = [&](int k, int q) {
+#pragma unroll
+            for (int e = 0; e < kEb / 2; ++e) lds_store<u32x4>(stg + (k * kDc + lane * 8) * kEb + 16 * e, x[q][e]);
+        };
+        // the weighted sum of the staged live splits lv (bit k: slot k, lse lane cb + k),
+        // over every slot in order with the dead ones' weight and value replaced by
+        // zero (a zero term leaves the sum unchanged, bit for bit), so that the LDS
+        // reads need not wait for each other
+        auto sum_staged = [&](uint64_t lv, int cb, float wt, float &acc) {
+#pragma unroll
+            for (int k = 0; k < kSlots; ++k) {
+                const bool on = (lv >> k) & 1;
+                float v;
+                if constexpr (kPartBf16)
+                    v = __uint_as_float(static_cast<uint32_t>(lds_load<uint16_t>(stg + (k * kDc + col) * 2)) << 16);
+                else
+                    v = lds_load<float>(stg + (k * kDc + col) * 4);
+                const float wk = on ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt), (cb + k) & 63)) : 0.f;
+                acc = __builtin_fmaf(wk, on ? v : 0.f, acc);
+            }
+        };
         for (int rr = 0; rr < R; ++rr) {
             const int64_t rowi = static_cast<int64_t>(rr) * p.H + h;
-            const float l_c0 = rr == 0 ? l_row0 : lse_at(rowi, 0);
+            // loads complete in order: the lse values first, then the partials, then
+            // (first row) the weights
+            const float l_c0 = lse_at(rowi, 0);
+            if (one_round) {
+#pragma unroll
+                for (int q = 0; q < kSlots / 8; ++q)
+                    if (8 * q + w < S) load_part(rowi, 8 * q + w, q);
+            }
+            if (rr == 0) load_weights();
             float mx = l_c0;
             for (int c0 = 64; c0 < S; c0 += 64) mx = fmaxf(mx, lse_at(rowi, c0));
             mx = wave_max_f(mx);
@@ -362,53 +409,38 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
                 const float wt = (lc == -INFINITY || mx == -INFINITY) ? 0.f : __expf(lc - mx);
                 sum += wt;
                 const uint64_t live = __builtin_amdgcn_ballot_w64(wt != 0.f);
+                if (one_round) {
+                    __syncthreads();                   // the previous row's LDS reads are done
+#pragma unroll
+                    for (int q = 0; q < kSlots / 8; ++q)
+                        if (8 * q + w < S) stage_part(8 * q + w, q);
+                    __syncthreads();
+                    sum_staged(live, 0, wt, acc);
+                    continue;
+                }
 #pragma unroll
                 for (int cb = 0; cb < 64; cb += kSlots) {
                     const uint64_t lv = (live >> cb) & (kSlots == 64 ? ~0ull : (1ull << kSlots) - 1);
                     if (!lv) continue;
                     __syncthreads();                   // the previous round's LDS reads are done
-                    // wave w stages splits c0 + cb + 8q + w of this round
-                    u32x4 x[kSlots / 8][kEb / 2];
 #pragma unroll
-                    for (int q = 0; q < kSlots / 8; ++q) {
-                        const int k = 8 * q + w;
-                        if ((lv >> k) & 1) {
-                            const char *src = static_cast<const char *>(o_part) +
-                                              ((rowi * S + c0 + cb + k) * kDc + lane * 8) * kEb;
+                    for (int q = 0; q < kSlots / 8; ++q)
+                        if ((lv >> (8 * q + w)) & 1) load_part(rowi, c0 + cb + 8 * q + w, q);
 #pragma unroll
-                            for (int e = 0; e < kEb / 2; ++e) x[q][e] = reinterpret_cast<const u32x4 *>(src)[e];
-                        }
-                    }
-#pragma unroll
-                    for (int q = 0; q < kSlots / 8; ++q) {
-                        const int k = 8 * q + w;
-                        if ((lv >> k) & 1)
-#pragma unroll
-                            for (int e = 0; e < kEb / 2; ++e)
-                                lds_store<u32x4>(stg + (k * kDc + lane * 8) * kEb + 16 * e, x[q][e]);
-                    }
+                    for (int q = 0; q < kSlots / 8; ++q)
+                        if ((lv >> (8 * q + w)) & 1) stage_part(8 * q + w, q);
                     __syncthreads();
-                    uint64_t m2 = lv;
-                    while (m2) {
-                        const int k = __builtin_ctzll(m2);
-                        m2 &= m2 - 1;
-                        const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt), cb + k));
-                        float v;
-                        if constexpr (kPartBf16)
-                            v = __uint_as_float(static_cast<uint32_t>(lds_load<uint16_t>(stg + (k * kDc + col) * 2)) << 16);
-                        else
-                            v = lds_load<float>(stg + (k * kDc + col) * 4);
-                        acc += wk * v;
-                    }
+                    sum_staged(lv, cb, wt, acc);
                 }
             }
             const float tot = wave_sum_f(sum);
             const float inv = tot > 0.f ? 1.f / tot : 0.f;
             lds_store<uint16_t>(sm + rr * 1024 + (((col >> 3) ^ (rr & 15)) << 4) + (col & 7) * 2,
                                 static_cast<uint16_t>(pack_bf16x2(acc * inv, 0.f) & 0xffffu));
-            if (lse_out && w == 0 && lane == 0) lse_out[rowi] = mx == -INFINITY ? -INFINITY : mx + __logf(tot);
+            if (lse_out && half == 0 && w == 0 && lane == 0)
+                lse_out[rowi] = mx == -INFINITY ? -INFINITY : mx + __logf(tot);
         }
-        for (int rr = R + w; rr < kUpRows; rr += 8) lds_store<u32x4>(sm + rr * 1024 + 16 * lane, u32x4{0u, 0u, 0u, 0u});
+        for (int rr = R + w; rr < kLatRows; rr += 8) lds_store<u32x4>(sm + rr * 1024 + 16 * lane, u32x4{0u, 0u, 0u, 0u});
     } else {
     // merge rows rr = w + 8i: lane owns latent columns 8 lane .. 8 lane + 7
     int64_t row[kCuRowsPerWave];
@@ -494,8 +526,8 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
                     const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt[0]), kq[qq]));
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[0][j] += wk * v0[qq][j];
-                        acc[0][4 + j] += wk * v1[qq][j];
+                        acc[0][j] = __builtin_fmaf(wk, v0[qq][j], acc[0][j]);
+                        acc[0][4 + j] = __builtin_fmaf(wk, v1[qq][j], acc[0][4 + j]);
                     }
                 }
             }
@@ -542,8 +574,8 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
                     }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        acc[i][j] += wq[i][qq] * v0[j];
-                        acc[i][4 + j] += wq[i][qq] * v1[j];
+                        acc[i][j] = __builtin_fmaf(wq[i][qq], v0[j], acc[i][j]);
+                        acc[i][4 + j] = __builtin_fmaf(wq[i][qq], v1[j], acc[i][4 + j]);
                     }
                 }
         }
@@ -562,7 +594,10 @@ __global__ __launch_bounds__(512) void combine_up_v_kernel(
     }
     __syncthreads();
 
-    constexpr int kRt = kUpRows / 16;             // 16-row tiles
+    if (!proj) return;
+    // 16-row tiles (kFew: at most kFewRows rows, one tile)
+    constexpr int kRt = kFew ? 1 : kUpRows / 16;
+    static_assert(!kFew || kFewRows <= 16, "one tile holds the few rows");
     f32x4 acc2[kRt];
 #pragma unroll
     for (int rt = 0; rt < kRt; ++rt) acc2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -603,10 +638,11 @@ hipError_t launch_combine_up_v(const mla_params_t &p, const void *o_part, const 
     const auto w = static_cast<const uint16_t *>(W_UV);
     const bool ob = p.out_dtype == MLA_BF16, pb = p.part_dtype == MLA_BF16;
     const bool few = R <= kFewRows;
+    const dim3 grid_few(static_cast<unsigned>((static_cast<int64_t>(p.H) + 7) / 8 * 8 * kFewSplit));
 #define MLA_CUV(OB, PB)                                                                                          \
     if (few)                                                                                                     \
-        hipLaunchKernelGGL((combine_up_v_kernel<OB, PB, true>), grid, dim3(512), 0, stream, p, o_part, lse_part, \
-                           w, out, lse_out);                                                                     \
+        hipLaunchKernelGGL((combine_up_v_kernel<OB, PB, true>), grid_few, dim3(512), 0, stream, p, o_part,       \
+                           lse_part, w, out, lse_out);                                                           \
     else                                                                                                         \
         hipLaunchKernelGGL((combine_up_v_kernel<OB, PB, false>), grid, dim3(512), 0, stream, p, o_part, lse_part, \
                            w, out, lse_out);

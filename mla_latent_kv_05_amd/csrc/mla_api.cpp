@@ -174,6 +174,15 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     // fp32 partials: 4 pages per part beat 8, 2 and 1; with bf16 partials 2 beat 4 and 1)
     const int64_t min_pages = p->part_dtype == MLA_BF16 ? 2 : 4;
     P = std::min(P, std::max<int64_t>(1, pages_lo / min_pages));
+    // a small batch whose plan leaves the 128-row kernel few workgroups runs on the
+    // 64-row kernel (twice the workgroups): there, with bf16 partials, parts of one
+    // unit each (at most one page) up to one 64-row workgroup per compute unit
+    // (measured at B = 1, 4,096 positions: 128 parts 34 us per step, 32 parts 37 us)
+    if (mfma && p->part_dtype == MLA_BF16 && mla::decode128_supported(*p) && mla::decode8_supported(*p) &&
+        !(p->flags & MLA_FLAG_ROWS128) && P * wg_per_part <= mla::kSmallGrid128) {
+        const int64_t units_lo = pages_lo + (int64_t)p->B * mla::kSeqStartCost;
+        P = std::max(P, std::min(units_lo, std::max<int64_t>(1, num_cus / (2 * wg_per_part))));
+    }
     P = std::max(P, std::min<int64_t>(min_splits, std::max<int64_t>(1, pages_lo)));
     P = std::min<int64_t>(P, kMaxParts);
     // a sequence of n pages touches at most ceil(n / q) + 1 parts of >= q pages, and

@@ -91,6 +91,12 @@ hipError_t take_errors_decode128(uint32_t *bits);
 // four-wave 128-row kernel, else the eight-wave 64-row kernel (bf16), else the
 // four-wave 64-row kernel (e4m3)
 enum class DecodeKernel { k128, k8, kMfma64 };
+// Workgroups of the 128-row kernel at or below which a bf16 launch goes to the
+// eight-wave kernel: with at most one 128-row workgroup per two compute units, twice
+// as many 64-row workgroups (each loading half the query rows and storing half the
+// partials) still fit at once and finish sooner (B = 1, 4,096 positions, 32 parts:
+// 18 us against 26 us).
+constexpr int64_t kSmallGrid128 = 128;
 DecodeKernel decode_kernel_for(const mla_params_t &p);
 // query rows per attention workgroup of that kernel
 int decode_rows_per_workgroup(const mla_params_t &p);

@@ -322,8 +322,20 @@ def test_debug_build_and_error_word_entry_points():
 
 def test_planner_part_size_follows_partial_type():
     """Parts of at least 4 pages with fp32 partials, 2 with bf16 partials (one
-    sequence of 64 pages: 16 and 32 parts)."""
+    sequence of 64 pages: 16 and 32 parts), except that a small bf16 batch on the
+    64-row kernel gets parts of one work unit (64 pages + the sequence's start cost
+    of 6 units: 70 parts, one page each), up to 128 parts."""
     p = mla.make_params(1, 1, 128, 128, 512, 64, num_pages=64, max_pages=64)
     assert mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1).num_parts == 16
     p.part_dtype = mla.BF16
+    q = mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1)
+    assert (q.num_parts, q.num_splits, mla.decode_kernel_name(q)) == (70, 64, "mfma_bf16_64")
+    p.flags = mla.FLAG_ROWS128                              # the 128-row kernel: parts of 2 pages
     assert mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1).num_parts == 32
+    p.flags = 0
+    p.B, p.num_pages = 4, 256                                 # 4 x 64 pages: 128 parts, 64-row kernel
+    q = mla.plan_splits(p, 4096, 4 * 4096, num_cus=256, min_splits=1)
+    assert (q.num_parts, mla.decode_kernel_name(q)) == (128, "mfma_bf16_64")
+    p.B, p.num_pages = 64, 4096                               # 64 x 64 pages: 256 parts, 128-row kernel
+    q = mla.plan_splits(p, 4096, 64 * 4096, num_cus=256, min_splits=1)
+    assert (q.num_parts, mla.decode_kernel_name(q)) == (256, "mfma_bf16_128")
