@@ -93,18 +93,28 @@ __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ u32x4 copy_rsrc(const void *base, uint32_t bytes) {
     return u32x4{lo32(base), hi32(base) & 0xffffu, static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), 0x20000u};
 }
+// kNt: non-temporal (the bf16 stream, read once; the e4m3 stream is read again by
+// the other row groups of a part at Sq > 1, and its loads without the hint measured
+// 3 % faster there, 6 % slower for bf16 at Sq = 1)
+template <bool kNt = true>
 __device__ __forceinline__ void copy_1k(const u32x4 &rsrc, uint32_t l, uint32_t soff, uint32_t v) {
     // (one wait state between the M0 write and the copy that reads it)
-    asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v], %[r], %[so] offen nt lds"
-                 :: [r] "s"(rsrc), [l] "s"(__builtin_amdgcn_readfirstlane(l)),
-                    [so] "s"(__builtin_amdgcn_readfirstlane(soff)), [v] "v"(v)
-                 : "memory", "m0");
+    if constexpr (kNt)
+        asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v], %[r], %[so] offen nt lds"
+                     :: [r] "s"(rsrc), [l] "s"(__builtin_amdgcn_readfirstlane(l)),
+                        [so] "s"(__builtin_amdgcn_readfirstlane(soff)), [v] "v"(v)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v], %[r], %[so] offen lds"
+                     :: [r] "s"(rsrc), [l] "s"(__builtin_amdgcn_readfirstlane(l)),
+                        [so] "s"(__builtin_amdgcn_readfirstlane(soff)), [v] "v"(v)
+                     : "memory", "m0");
 }
 
 // One instruction copying 256 bytes: lane i's 4 bytes from base + soff + voff_i land at
 // M0 + 4 i (lanes past the buffer's end read zeros).
 __device__ __forceinline__ void copy_256(const u32x4 &rsrc, uint32_t l, uint32_t soff, uint32_t v) {
-    asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dword %[v], %[r], %[so] offen nt lds"
+    asm volatile("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tbuffer_load_dword %[v], %[r], %[so] offen lds"
                  :: [r] "s"(rsrc), [l] "s"(__builtin_amdgcn_readfirstlane(l)),
                     [so] "s"(__builtin_amdgcn_readfirstlane(soff)), [v] "v"(v)
                  : "memory", "m0");
@@ -250,11 +260,11 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     const uint32_t lane16 = static_cast<uint32_t>(lane) << 4, lane4 = static_cast<uint32_t>(lane) << 2;
     auto raw_copy = [&](const TileSrc &ts, int i) {
         if (i < 4)
-            copy_1k(ts.ckv, ts.raw + (8 * w + 2 * i) * kDc, (8 * w + 2 * i) * kDc, lane16);
+            copy_1k<false>(ts.ckv, ts.raw + (8 * w + 2 * i) * kDc, (8 * w + 2 * i) * kDc, lane16);
         else
             copy_256(ts.scl, ts.raw + L::kRawCodes + w * 256, 0u, lane4);
     };
-    auto rope_copy = [&](const TileSrc &ts) { copy_1k(ts.kpe, ts.st + kStageKpe + w * 1024, w * 1024, rope_voff); };
+    auto rope_copy = [&](const TileSrc &ts) { copy_1k<false>(ts.kpe, ts.st + kStageKpe + w * 1024, w * 1024, rope_voff); };
     // e4m3 conversion of rows 8w .. 8w+7 of tile t from its raw stage into its bf16
     // stage: bf16(float(code) * scale), one fp32 product rounded to nearest even (the
     // value mla_expand_kv gives).  One row at a time: lane l reads codes 8l .. 8l+7 of
