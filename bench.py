@@ -12,8 +12,8 @@ The inputs are replicated in HBM (by default enough replicas to hold at least
 last-level cache cannot serve one step from the previous one.
 
 Timing, in this order:
-  1. the step with the fused tail: untimed warm-up steps (at least W, and enough
-     for WARM_S seconds of GPU work),
+  1. the step with the fused tail: untimed warm-up steps (at least W, then blocks
+     of WARM_BLOCK steps, each followed by a synchronize, for WARM_S seconds),
      then exactly K timed steps bracketed by a synchronize and events (events
      only at block boundaries);
   2. the same for the four-call step;
@@ -24,7 +24,10 @@ The GPU reaches its sustained step rate only after some hundreds of steps of
 load (measured at 64 x 4,096 positions: 5 warm-up steps then 20 timed ones read
 ~10% slower than after 300 more, and still ~2% slower than after 1,000 more), so
 each route gets WARM_S seconds of warm-up steps whatever W is; the JSON gives W
-and the warm-up steps each route ran.
+and the warm-up steps each route ran.  The warm-up synchronizes every WARM_BLOCK
+steps, as a decode loop does to read each step's result: thousands of steps
+enqueued at once (a second of work) left the next timed steps 5-20 % slower for a
+while, the GPU's power management having lowered its clocks.
 The oracle leg (cpu_baseline) also compares the step's output for the sequences
 it computed with the GPU step's output (max and RMS error over the output RMS).
 
@@ -44,7 +47,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 STEP_BLOCK = 50                # steps per block of the step-time spread
-WARM_S = 0.3                   # seconds of warm-up steps per route (at least W steps)
+WARM_S = 0.5                   # seconds of warm-up steps per route (at least W steps)
+WARM_BLOCK = 50                # warm-up steps between synchronizes
 KERNEL_WARMUP = 300            # untimed attention launches before the kernel leg
 KERNEL_LAUNCHES = 600          # timed attention launches (at least; more when K is larger)
 REPLICA_BYTES = 1 << 30        # inputs replicated until the replicas hold this many bytes
@@ -138,30 +142,31 @@ def main():
     bound_f = [step_f.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                            t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
 
-    def warm(step_fn):
-        """W warm-up steps, then more until about WARM_S seconds of GPU work have run;
-        returns the number of warm-up steps."""
+    def warm(step_fn, seconds=WARM_S):
+        """W warm-up steps, then blocks of WARM_BLOCK steps, each followed by a
+        synchronize (as a decode loop synchronizes to read each step's result),
+        until `seconds` have passed; returns the number of warm-up steps."""
         for i in range(args.warmup):
             step_fn(i)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(50):
-            step_fn(i)
-        torch.cuda.synchronize()
-        n = max(0, int(WARM_S / ((time.perf_counter() - t0) / 50)) - 50)
-        for i in range(n):
-            step_fn(i)
-        torch.cuda.synchronize()
-        return args.warmup + 50 + n
+        n, t0 = args.warmup, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for i in range(WARM_BLOCK):
+                step_fn(i)
+            torch.cuda.synchronize()
+            n += WARM_BLOCK
+        return n
 
     warm_runs = {}
 
     # 1. the fused step: warm-up steps, then exactly K timed steps bracketed by a
     # synchronize and events; an event at every block boundary (one per STEP_BLOCK
     # steps) gives the spread of the per-step time without gaps inside the steps
-    warm_runs["fused_tail"] = warm(lambda i: bound_f[i % args.replicas]())
-    assert torch.isfinite(step_f.out).all(), "non-finite output"
+    # (the output checks run after the timed steps: the first allocation of a device
+    # block by torch between the warm-up and the timed steps slowed the next steps
+    # by 10-20 % for about a millisecond)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-args.steps // STEP_BLOCK) + 1)]
+    warm_runs["fused_tail"] = warm(lambda i: bound_f[i % args.replicas]())
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     marks[0].record(stream)
@@ -175,17 +180,19 @@ def main():
     blk_us = [marks[k].elapsed_time(marks[k + 1]) * 1e3 / min(STEP_BLOCK, args.steps - k * STEP_BLOCK)
               for k in range(len(marks) - 1)]
 
+    assert torch.isfinite(step_f.out).all(), "non-finite output"
+
     # 2. the four-call step, the same way (events around the whole loop only)
-    warm_runs["four_calls"] = warm(lambda i: run(i % args.replicas))
-    assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    warm_runs["four_calls"] = warm(lambda i: run(i % args.replicas))
     t_start.record(stream)
     for i in range(args.steps):
         run(i % args.replicas)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    assert torch.equal(step_f.out, step.out), "fused tail differs from the four-call step"
 
     # e4m3 cache: also the route that expands the cache to bf16 first (for a step
     # bound by the matrix cores); same result within the e4m3 bound
@@ -194,8 +201,8 @@ def main():
         step_e = mla.DecodeStep(p, device=dev, fused=True, expand=True)
         bound_e = [step_e.bind(t["q_nope"], t["q_rope"], t["c_kv"], t["k_pe"], t["kv_scale"], t["block_table"],
                                t["seq_lens"], t["W_UK"], t["W_UV"], stream) for t in reps]
-        warm_runs["expand_fused_tail"] = warm(lambda i: bound_e[i % args.replicas]())
         x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm_runs["expand_fused_tail"] = warm(lambda i: bound_e[i % args.replicas]())
         x0.record(stream)
         for i in range(args.steps):
             bound_e[i % args.replicas]()
@@ -219,9 +226,9 @@ def main():
     # one event pair on the launch stream (no per-launch events, whose stream gaps
     # would be timed too); events at block boundaries give the spread
     n_dec = max(KERNEL_LAUNCHES, args.steps)
+    kmarks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-n_dec // STEP_BLOCK) + 1)]
     for i in range(KERNEL_WARMUP):
         dec_calls[i % args.replicas]()
-    kmarks = [torch.cuda.Event(enable_timing=True) for _ in range(-(-n_dec // STEP_BLOCK) + 1)]
     torch.cuda.synchronize()
     kmarks[0].record(stream)
     for i in range(n_dec):
