@@ -109,9 +109,13 @@ def main():
     # bf16 partials with a bf16 latent: half the bytes the attention writes and the
     # merge reads (each partial row rounded once, as o_latent is); the planner sizes
     # the parts for them
+    # an e4m3 cache holds power-of-two token scales (the append's format, which the
+    # generator follows): MLA_FLAG_POW2_SCALE lets the kernel widen with one
+    # instruction per two codes
     p = mla.make_params(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, case.num_pages, case.max_pages,
                         scale=wl.scale, q_dtype=fl, w_dtype=fl, kv_dtype=kv, pe_dtype=fl,
-                        latent_dtype=fl, out_dtype=mla.F32, part_dtype=mla.F32 if wl.dtype == "f32" else mla.BF16)
+                        latent_dtype=fl, out_dtype=mla.F32, part_dtype=mla.F32 if wl.dtype == "f32" else mla.BF16,
+                        flags=mla.FLAG_POW2_SCALE if wl.dtype == "fp8" else 0)
     p = mla.plan_splits(p, max(lens), case.total_tokens, num_cus=props.multi_processor_count,
                         min_splits=wl.min_splits)
 

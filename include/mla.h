@@ -63,6 +63,7 @@ typedef enum {
 #define MLA_DEVERR_SYNC 2u    /* a bounded wait between the waves of a workgroup gave up */
 #define MLA_DEVERR_PAGE 4u    /* (MLA_DEBUG_BOUNDS build) block_table entry outside [0, num_pages) */
 #define MLA_DEVERR_SEQLEN 8u  /* (MLA_DEBUG_BOUNDS build) seq_lens entry outside [0, max_pages * 64] */
+#define MLA_DEVERR_SCALE 16u  /* (MLA_DEBUG_BOUNDS build) MLA_FLAG_POW2_SCALE with a scale that is no power of two */
 
 /* Flags (mla_params_t.flags). */
 #define MLA_FLAG_GENERIC 1u  /* use the fp32 VALU kernels even where MFMA kernels apply */
@@ -75,6 +76,13 @@ typedef enum {
  * and partials up to rounding. */
 #define MLA_FLAG_ROWS64 2u   /* the eight-wave kernel (bf16 cache, Sq*H a multiple of 64) */
 #define MLA_FLAG_ROWS128 4u  /* the four-wave kernel (bf16 or e4m3 cache, Sq*H a multiple of 128) */
+/* e4m3 cache: every kv_scale entry of a position a sequence holds is a power of two
+ * (mla_append_kv writes only such scales).  The four-wave kernel then widens the
+ * codes with gfx950's MX-style conversion, one instruction per two codes, instead
+ * of widening, multiplying and rounding: the same values, bit for bit.  A scale
+ * that is no power of two gives wrong values for its row (the conversion uses only
+ * the scale's exponent); the MLA_DEBUG_BOUNDS build raises MLA_DEVERR_SCALE. */
+#define MLA_FLAG_POW2_SCALE 8u
 
 /*
  * Problem description shared by the four calls.
@@ -307,10 +315,12 @@ mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, 
  *   y[i + half] = x[i + half] cos theta_i + x[i] sin theta_i
  * computed in fp64, rounded once to fp32, then to the destination format.
  * Latent rows are stored in kv_dtype (round to nearest even from fp32).  For an
- * FP8_E4M3 cache, per token: scale = max(amax, 2^-20) / 448 and r_j = x_j / scale
- * (correctly rounded fp32 divisions), code_j = the E4M3 value nearest to r_j
- * (ties to even, |r_j| > 448 saturating to 448, sign kept), and the token's
- * kv_scale entry = scale.
+ * FP8_E4M3 cache, per token: s0 = max(amax, 2^-20) / 448 (a correctly rounded
+ * fp32 division), scale = the smallest power of two >= s0, r_j = x_j / scale
+ * (exact), code_j = the E4M3 value nearest to r_j (ties to even, |r_j| > 448
+ * saturating to 448, sign kept), and the token's kv_scale entry = scale.  Every
+ * scale written is a power of two, so a cache filled only by this call may be
+ * read with MLA_FLAG_POW2_SCALE.
  *
  *   c_new      [B,Sq,d_c]    q_dtype  (in: latent rows of the new tokens)
  *   kpe_new    [B,Sq,d_r]    q_dtype  (in: RoPE keys before rotation; may be NULL iff d_r == 0)

@@ -24,8 +24,10 @@
 // reads and writes both members of a rotated pair, so the query may be rotated
 // in place.  y is formed in fp64, rounded once to fp32 and then to the
 // destination format (bf16: round to nearest even).  For an e4m3 cache the wave
-// reduces its row's amax; scale = max(amax, 2^-20) / 448 and r = x / scale are
-// correctly rounded fp32 divisions, and each r goes to the nearest e4m3 value
+// reduces its row's amax; s0 = max(amax, 2^-20) / 448 is a correctly rounded fp32
+// division, the scale is the smallest power of two >= s0 (per-token power-of-two
+// scales, which the decode kernel widens with one MX-style conversion per two
+// codes), r = x / scale, and each r goes to the nearest e4m3 value
 // (ties to even, magnitudes above 448 saturating) by an exact power-of-two
 // scaling and rint; the row's kv_scale entry gets the scale.
 // Bound: HBM (a few KB per token, no reuse).
@@ -56,6 +58,14 @@ __device__ __forceinline__ uint8_t f32_to_e4m3_sat(float r) {
         if (code > 0x7eu) code = 0x7eu;
     }
     return static_cast<uint8_t>(code | sign);
+}
+
+// the token scale: the smallest power of two >= max(amax, 2^-20) / 448 (s0 is a
+// positive normal float: a power of two has no mantissa bits; otherwise the next
+// binade's power)
+__device__ __forceinline__ float pow2_scale(float amax) {
+    const uint32_t b = __float_as_uint(__fdiv_rn(fmaxf(amax, 0x1p-20f), 448.f));
+    return __uint_as_float((b & 0x7fffffu) ? (b & 0xff800000u) + 0x800000u : b);
 }
 
 // (x_lo, x_hi) rotated by the angle with cosine c and sine s, stored as `dt`
@@ -148,7 +158,7 @@ __device__ __forceinline__ void latent_row(const mla_params_t &p, bool vec, cons
             for (int m = lane; m < p.d_c; m += 64) amax = fmaxf(amax, fabsf(load_elem(c_new, p.q_dtype, src + m)));
         }
         for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-        const float scale = __fdiv_rn(fmaxf(amax, 0x1p-20f), 448.f);
+        const float scale = pow2_scale(amax);
         if (vec) {
             for (int m = 8 * lane; m < p.d_c; m += 512) {
                 float v[8];
@@ -231,7 +241,7 @@ __device__ __forceinline__ void rows_v3(const mla_params_t &p, const void *c_new
 #pragma unroll
             for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[t][k]));
             for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-            const float scale = __fdiv_rn(fmaxf(amax, 0x1p-20f), 448.f);
+            const float scale = pow2_scale(amax);
             *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(c_kv) + dst) = e4m3x8(v[t], scale);
             if (lane == 0) kv_scale[tr[t].crow] = scale;
         } else {

@@ -167,7 +167,7 @@ __device__ __forceinline__ bf16x8 tr_op(const v4i16 &lo, const v4i16 &hi) {
 // ---------------------------------------------------------------------------
 // One wave's part of one segment.
 // ---------------------------------------------------------------------------
-template <bool kFp8>
+template <bool kFp8, bool kPow2>
 __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p, const uint16_t *__restrict__ q_abs,
                                                const uint16_t *__restrict__ q_rope, const char *__restrict__ c_kv,
                                                const uint16_t *__restrict__ k_pe, const float *__restrict__ kv_scale,
@@ -281,15 +281,33 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
         return ConvIn{lds_load<u32x2>(raw + (8 * w + j) * kDc + 8 * lane),
                       lds_load<float>(raw + L::kRawCodes + w * 256 + (8 * w + j) * 4)};
     };
+    // kPow2 (MLA_FLAG_POW2_SCALE: the caller states that every valid row's scale is a
+    // power of two, as mla_append_kv writes them): code * scale is then exact in bf16,
+    // and gfx950's MX-style conversion applies such a scale itself, one instruction
+    // per two codes.  It uses only the scale's exponent, so any other scale needs
+    // the widening, the two products and the rounding.  The MLA_DEBUG_BOUNDS build
+    // checks the statement for the rows it converts (MLA_DEVERR_SCALE).
     auto conv_write = [&](int t, int j, const ConvIn &v) {
         const int r = 8 * w + j;
         u32x4 o;
+        if constexpr (kPow2) {
+#ifdef MLA_DEBUG_BOUNDS
+            const bool valid = t < n_tiles - 1 || (t == n_tiles - 1 && r < last_valid);
+            if (valid && lane == 0 && (__float_as_uint(v.scale) & 0x7fffffu) != 0u) raise_error(MLA_DEVERR_SCALE);
+#endif
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], true);
-            o[2 * e] = cvt_pk_bf16(lo[0] * v.scale, lo[1] * v.scale);
-            o[2 * e + 1] = cvt_pk_bf16(hi[0] * v.scale, hi[1] * v.scale);
+            for (int e = 0; e < 2; ++e) {
+                o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.codes[e], v.scale, false));
+                o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.codes[e], v.scale, true));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v.codes[e], true);
+                o[2 * e] = cvt_pk_bf16(lo[0] * v.scale, lo[1] * v.scale);
+                o[2 * e + 1] = cvt_pk_bf16(hi[0] * v.scale, hi[1] * v.scale);
+            }
         }
         lds_store<u32x4>(stage_addr(t) + r * kLRow + ((lane ^ lat_swz(r)) << 4), o);
     };
@@ -712,7 +730,7 @@ __device__ __forceinline__ void attend_segment(char *smem, const mla_params_t &p
     }
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kPow2>
 __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
     const mla_params_t p, const uint16_t *__restrict__ q_abs, const uint16_t *__restrict__ q_rope,
     const char *__restrict__ c_kv, const uint16_t *__restrict__ k_pe, const float *__restrict__ kv_scale,
@@ -746,7 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode128_kernel(
             if (!first) barrier_lds();                 // the previous segment's LDS reads are done
             first = false;
             wait_vmcnt<0>();                           // its stores too (the copy waits count from here)
-            attend_segment<kFp8>(smem, p, q_abs, q_rope, c_kv, k_pe, kv_scale,
+            attend_segment<kFp8, kPow2>(smem, p, q_abs, q_rope, c_kv, k_pe, kv_scale,
                                  block_table + static_cast<int64_t>(seg.b) * p.max_pages + seg.pa, seg,
                            seq_lens[seg.b], rg, o_part, lse_part);
         } else if (threadIdx.x == 0) {
@@ -790,12 +808,15 @@ hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void
     const auto qr = static_cast<const uint16_t *>(q_rope);
     const auto kv = static_cast<const char *>(c_kv);
     const auto kp = static_cast<const uint16_t *>(k_pe);
-    if (p.kv_dtype == MLA_FP8_E4M3)
-        hipLaunchKernelGGL(decode128_kernel<true>, grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp, kv_scale,
-                           block_table, seq_lens, o_part, lse_part);
+    if (p.kv_dtype == MLA_FP8_E4M3 && (p.flags & MLA_FLAG_POW2_SCALE))
+        hipLaunchKernelGGL((decode128_kernel<true, true>), grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp,
+                           kv_scale, block_table, seq_lens, o_part, lse_part);
+    else if (p.kv_dtype == MLA_FP8_E4M3)
+        hipLaunchKernelGGL((decode128_kernel<true, false>), grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp,
+                           kv_scale, block_table, seq_lens, o_part, lse_part);
     else
-        hipLaunchKernelGGL(decode128_kernel<false>, grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp, kv_scale,
-                           block_table, seq_lens, o_part, lse_part);
+        hipLaunchKernelGGL((decode128_kernel<false, false>), grid, dim3(kThreads), 0, stream, p, qa, qr, kv, kp,
+                           kv_scale, block_table, seq_lens, o_part, lse_part);
     return hipGetLastError();
 }
 

@@ -75,7 +75,7 @@ mla_status_t check(const mla_params_t *p, int max_sq = kMaxAbsorbedSq) {
     if (!is_float_dtype(p->latent_dtype)) return fail(MLA_ERR_DTYPE, "latent_dtype must be F32 or BF16");
     if (!is_float_dtype(p->out_dtype)) return fail(MLA_ERR_DTYPE, "out_dtype must be F32 or BF16");
     if (!is_float_dtype(p->part_dtype)) return fail(MLA_ERR_DTYPE, "part_dtype must be F32 or BF16");
-    if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC | MLA_FLAG_ROWS64 | MLA_FLAG_ROWS128))
+    if (p->flags & ~static_cast<uint32_t>(MLA_FLAG_GENERIC | MLA_FLAG_ROWS64 | MLA_FLAG_ROWS128 | MLA_FLAG_POW2_SCALE))
         return fail(MLA_ERR_SHAPE, "unknown flag bits 0x%x", p->flags);
     if ((p->flags & MLA_FLAG_ROWS64) && (p->flags & MLA_FLAG_ROWS128))
         return fail(MLA_ERR_SHAPE, "MLA_FLAG_ROWS64 and MLA_FLAG_ROWS128 together");

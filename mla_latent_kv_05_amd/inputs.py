@@ -115,11 +115,14 @@ def _to_store(x: np.ndarray, fmt: str) -> torch.Tensor:
 def quantize_e4m3_per_token(x: torch.Tensor):
     """Per-token (last-dim row) OCP e4m3 quantisation of a float32 tensor.
 
-    scale = max(amax, 2^-20) / 448, code = RNE(x / scale) saturated to +-448.
+    scale = the smallest power of two >= max(amax, 2^-20) / 448 (the cache format
+    the append writes), code = RNE(x / scale) saturated to +-448.
     Returns (uint8 codes, float32 scales with the row shape).
     """
     amax = x.abs().amax(dim=-1)
-    scale = torch.clamp(amax, min=E4M3_MIN_SCALE) / E4M3_MAX
+    s0 = torch.clamp(amax, min=E4M3_MIN_SCALE) / E4M3_MAX
+    m, e = torch.frexp(s0)
+    scale = torch.where(m == 0.5, s0, torch.ldexp(torch.ones_like(s0), e))
     y = (x / scale.unsqueeze(-1)).clamp_(-E4M3_MAX, E4M3_MAX)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
     return codes.contiguous(), scale.to(torch.float32).contiguous()

@@ -22,6 +22,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 FLAG_GENERIC = 1
 FLAG_ROWS64 = 2       # force the eight-wave 64-row attention kernel (bf16 cache)
 FLAG_ROWS128 = 4      # force the four-wave 128-row attention kernel
+FLAG_POW2_SCALE = 8   # e4m3 cache: every kv_scale is a power of two (as mla_append_kv writes)
 PAGE = 64
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE",
@@ -270,7 +271,7 @@ def combine_up_v(p: Params, o_part, lse_part, W_UV, out, lse_out=None, stream=No
         _stream(stream)))
 
 
-DEVERR = {1: "MLA_DEVERR_SPLITS", 2: "MLA_DEVERR_SYNC", 4: "MLA_DEVERR_PAGE", 8: "MLA_DEVERR_SEQLEN"}
+DEVERR = {1: "MLA_DEVERR_SPLITS", 2: "MLA_DEVERR_SYNC", 4: "MLA_DEVERR_PAGE", 8: "MLA_DEVERR_SEQLEN", 16: "MLA_DEVERR_SCALE"}
 
 
 def device_errors(stream=None, L=None) -> int:

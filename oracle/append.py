@@ -21,9 +21,11 @@ What it computes, with the passages it follows:
                 sec. 3, why RoPE: a position-dependent rotation R_pos for which
                 <R_m q, R_n k> depends on n - m only).
   e4m3 cache    the pages fix no quantiser.  Per token: amax = max |x| over the
-                latent row, scale = max(amax, 2^-20) / 448 and r_j = x_j / scale,
-                both divisions in fp32 (the precision the kernel decides in);
-                the code is the E4M3 value nearest to r_j, ties to the even code,
+                latent row, s0 = max(amax, 2^-20) / 448 (an fp32 division, the
+                precision the kernel decides in), the scale is the smallest power
+                of two >= s0 (a per-token power-of-two scale, as in the MX formats
+                the hardware converts natively), and r_j = x_j / scale (fp32); the
+                code is the E4M3 value nearest to r_j, ties to the even code,
                 magnitudes above 448 saturating to 448, sign kept.
   expansion     the values such a cache holds, code * scale, as bf16: the code's
                 E4M3 value times the token's scale in one fp32 product, rounded
@@ -100,9 +102,11 @@ def quantize_e4m3_rows(x: np.ndarray):
     scales [n] float32)."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=-1)
-    scale = np.maximum(amax, np.float32(MIN_AMAX)).astype(np.float32) / np.float32(E4M3_MAX)
+    s0 = np.maximum(amax, np.float32(MIN_AMAX)).astype(np.float32) / np.float32(E4M3_MAX)
+    m, e = np.frexp(s0.astype(np.float64))                    # s0 = m 2^e, m in [0.5, 1)
+    scale = np.where(m == 0.5, s0, np.ldexp(1.0, e)).astype(np.float32)
     r = x / scale[..., None]                                 # float32 division
-    return e4m3_nearest(r), scale.astype(np.float32)
+    return e4m3_nearest(r), scale
 
 
 def expand_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

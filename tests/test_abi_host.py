@@ -60,7 +60,7 @@ def test_valid_params_pass():
     ("d_r", -1, 2), ("page_size", 32, 2), ("num_pages", 0, 2), ("max_pages", 0, 2),
     ("num_splits", 0, 4), ("num_splits", 5000, 4), ("split_pages", 0, 4), ("scale", 0.0, 2),
     ("scale", float("inf"), 2), ("q_dtype", 2, 3), ("w_dtype", 7, 3), ("kv_dtype", 3, 3),
-    ("pe_dtype", 2, 3), ("latent_dtype", 2, 3), ("out_dtype", -1, 3), ("flags", 8, 2), ("flags", 6, 2),
+    ("pe_dtype", 2, 3), ("latent_dtype", 2, 3), ("out_dtype", -1, 3), ("flags", 16, 2), ("flags", 6, 2),
     ("num_parts", -1, 4), ("num_parts", 1 << 21, 4),
 ])
 def test_invalid_params_rejected(field, value, status):

@@ -15,7 +15,7 @@ from tests.helpers import DeviceCase, params_for
 
 pytestmark = pytest.mark.gpu
 
-SPLITS, SYNC, PAGE, SEQLEN = 1, 2, 4, 8
+SPLITS, SYNC, PAGE, SEQLEN, SCALE = 1, 2, 4, 8, 16
 
 
 def note(msg):
@@ -38,7 +38,7 @@ def decode(L, p, dc, q_abs, block_table=None, seq_lens=None):
 
 
 CASES = [("v3_b64", {}, mla.FLAG_ROWS128), ("v3_b64", {}, mla.FLAG_ROWS64), ("v3_b64", {"H": 64}, 0),
-         ("v3_sq4_fp8", {}, 0), ("v3_b64", {}, mla.FLAG_GENERIC)]
+         ("v3_sq4_fp8", {}, 0), ("v3_b64", {}, mla.FLAG_GENERIC), ("v3_sq4_fp8", {}, mla.FLAG_POW2_SCALE)]
 
 
 @pytest.mark.parametrize("wl_name,over,flags", CASES)
@@ -59,7 +59,7 @@ def test_stale_plan_is_flagged(wl_name, over, flags):
     assert decode(L, p, dc, q_abs)[2] == SPLITS
 
 
-@pytest.mark.parametrize("wl_name,over,flags", [CASES[0], CASES[2], CASES[3]])
+@pytest.mark.parametrize("wl_name,over,flags", [CASES[0], CASES[2], CASES[3], CASES[5]])
 def test_debug_build_flags_bad_pages_and_lengths(wl_name, over, flags):
     D = mla.debug_lib()
     assert D.mla_debug_bounds() == 1 and mla.lib().mla_debug_bounds() == 0
@@ -86,3 +86,43 @@ def test_debug_build_flags_bad_pages_and_lengths(wl_name, over, flags):
     sl = dc.seq_lens.clone()
     sl[1] = p.max_pages * 64 + 100
     assert decode(D, p, dc, q_abs, seq_lens=sl)[2] & SEQLEN
+
+
+def test_debug_build_flags_a_scale_that_is_no_power_of_two():
+    """MLA_FLAG_POW2_SCALE states that the e4m3 scales are powers of two; the debug
+    build checks it for every row it converts (a scale past a sequence's end is not
+    counted) and raises MLA_DEVERR_SCALE, and without the flag the same cache is
+    read exactly (the bf16 kernel on its expansion gives the same partials)."""
+    D = mla.debug_lib()
+    lens = [700, 130, 64]
+    wl = I.workload("v3_sq4_fp8", B=len(lens))
+    case = I.make_case(wl, seq_lens=lens)
+    for b, n in enumerate(lens):                   # the generator's scales, on valid rows
+        t = torch.arange(n)
+        rows = case.kv_scale[case.block_table[b, t // 64].long(), t % 64]
+        assert bool(((rows.view(torch.int32) & 0x7fffff) == 0).all())
+    dc = DeviceCase(case)
+    q_abs = I.random_q_abs(wl, seed=7).cuda()
+    p = params_for(case, num_parts=5, flags=mla.FLAG_POW2_SCALE)
+    mla.device_errors(L=D)
+    assert decode(D, p, dc, q_abs)[2] == 0
+    # one valid row with a scale of 1.5 x a power of two: flagged with the flag
+    pg = int(case.block_table[1, 0])
+    dc.kv_scale[pg, 5] *= 1.5
+    assert decode(D, p, dc, q_abs)[2] == SCALE
+    # without the flag the row is read exactly, as on the expanded cache
+    q = p.copy()
+    q.flags = 0
+    o8, l8, err = decode(mla.lib(), q, dc, q_abs)
+    assert err == 0
+    kv16 = torch.empty((case.num_pages, 64, wl.d_c), dtype=torch.bfloat16, device="cuda")
+    mla.expand_kv(q, dc.c_kv, dc.kv_scale, kv16)
+    qb = q.copy()
+    qb.kv_dtype = mla.BF16
+    qb.flags = mla.FLAG_ROWS128
+    dc16 = DeviceCase(case)
+    dc16.c_kv = kv16
+    dc16.kv_scale = None
+    o16, l16, err = decode(mla.lib(), qb, dc16, q_abs)
+    assert err == 0
+    assert torch.equal(o8, o16) and torch.equal(l8, l16)

@@ -8,7 +8,9 @@ and the mathematics fix, not against itself:
     that fix the frequency schedule;
   * the E4M3 quantiser: torch's float8_e4m3fn conversion (a library routine) on
     random values and on every exact midpoint between codes, the OCP maximum,
-    and the per-token scale on rows whose amax is a power of two times 448;
+    and the per-token scale: the smallest power of two at or above
+    max(amax, 2^-20) / 448, checked by its defining inequalities and on rows
+    whose amax is a power of two times 448;
   * placement: positions and slots of a hand-built block table.
 """
 import math
@@ -95,15 +97,20 @@ def test_e4m3_quantise_rows():
     x = rng.standard_normal((6, 512)).astype(np.float32)
     x[1] *= 1e-9                               # amax below 2^-20: scale floored
     x[2, 7] = 448.0 * 4                        # amax 1792: scale exactly 4, the max maps to 0x7E
+    x[3, 0] = 448.0 * 4 * 1.0000001           # just above: the next power of two
     codes, scales = A.quantize_e4m3_rows(x)
     assert scales.dtype == np.float32
     assert scales[2] == np.float32(4.0) and codes[2, 7] == 0x7E
-    assert scales[1] == np.float32(2.0 ** -20) / np.float32(448.0)
+    assert scales[3] == np.float32(8.0)
+    # 2^-20 / 448 = 2^-28 / 1.75: the scale of a floored row is 2^-28
+    assert scales[1] == np.float32(2.0 ** -28)
     for i in range(6):
         amax = np.float32(max(np.abs(x[i]).max(), np.float32(2.0 ** -20)))
-        s = amax / np.float32(448.0)
-        assert scales[i] == s
-        assert np.array_equal(codes[i], _torch_e4m3(x[i] / s))
+        s0 = amax / np.float32(448.0)
+        s = float(scales[i])
+        assert math.frexp(s)[0] == 0.5                   # a power of two
+        assert s >= float(s0) and s / 2 < float(s0)      # the smallest one >= s0
+        assert np.array_equal(codes[i], _torch_e4m3(x[i] / np.float32(s)))
 
 
 def test_positions_and_slots():
