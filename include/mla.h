@@ -299,6 +299,53 @@ mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, 
                                      float *lse_out, void *stream);
 
 /*
+ * mla_decode_step_persistent -- the step of mla_decode_step for a small batch
+ * of single new tokens, in one launch: absorb, attention and the merge with the
+ * up-projection run as one kernel ("DeepSeek-MLA-Principle", matrix absorption
+ * 3): the query is absorbed once, attention runs in latent space, the output is
+ * up-projected once; "DeepSeek MLA 架构详解" sec. 3, the decode module).
+ * Workgroups take one of three roles by index (absorb, attention per page and
+ * 32 heads, merge and up-projection per head and 64 rows); a workgroup waits
+ * only for workgroups of lower index through counters in the workspace, so the
+ * launch drains however many of them are resident at once.
+ *
+ * Computes what mla_decode_step computes, within rounding (not bit for bit: q_abs
+ * and the partials are summed in another order).  Each page of 64 positions is
+ * one split; its partial is normalised and rounded once to bf16, as with
+ * part_dtype = BF16.  num_splits, split_pages, num_parts, part_dtype and the flags
+ * are ignored.  On an MI355X this one launch is slower than mla_decode_step's
+ * three (the waits between its roles cross the compute dies' L2 caches); it is
+ * for callers that want a single launch.
+ *
+ * Supported (else MLA_ERR_UNSUPPORTED): Sq = 1, 1 <= B <= 8, H a multiple of 32
+ * up to 128, d_h = 128, d_c = 512, d_r = 64, q_dtype = w_dtype = kv_dtype =
+ * pe_dtype = latent_dtype = BF16, out_dtype BF16 or F32, max_pages <= 4096.
+ *
+ *   q_nope, q_rope, c_kv, k_pe, block_table, seq_lens, W_UK, W_UV
+ *                as for mla_decode_step (in; q_rope and k_pe not NULL)
+ *   out        [B,1,H,d_h] out_dtype (out)
+ *   lse_out    [B,1,H] fp32 (out; may be NULL; -inf for an empty sequence, whose
+ *              out rows are zero)
+ *   workspace  device memory of at least mla_decode_step_persistent_workspace(p)
+ *              bytes, 256-byte aligned.  Its first 256 bytes are the kernel's
+ *              counters: they must be zero before the workspace's first use with
+ *              this call (allocate it zeroed), and every call leaves them zero.  The
+ *              rest is scratch.  Calls that share a workspace must not overlap.
+ * The waits between workgroups are bounded: one that gives up sets
+ * MLA_DEVERR_SYNC (mla_device_errors) and the kernel still ends.
+ * Returns MLA_ERR_NULL / MLA_ERR_SHAPE / MLA_ERR_UNSUPPORTED without launching
+ * anything, MLA_ERR_HIP if the launch fails.
+ */
+mla_status_t mla_decode_step_persistent(const mla_params_t *p, const void *q_nope, const void *q_rope,
+                                        const void *c_kv, const void *k_pe, const int32_t *block_table,
+                                        const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out,
+                                        float *lse_out, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes mla_decode_step_persistent needs for *p (host-only; -1 for an
+ * invalid or unsupported p). */
+int64_t mla_decode_step_persistent_workspace(const mla_params_t *p);
+
+/*
  * mla_append_kv -- write the Sq new tokens of every sequence into the paged
  * cache, rotating the shared RoPE key at each token's position; optionally
  * rotate the query's RoPE part at the same positions.  The decode module of

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libmla.so")
 DEBUG_LIB = os.path.join(PKG, "libmla_debug.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["mla_api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
-           "kernels_decode8.hip", "kernels_decode128.hip", "kernels_append.hip", "kernels_prefill.hip", "kernels_expand.hip"]
+           "kernels_decode8.hip", "kernels_decode128.hip", "kernels_append.hip", "kernels_prefill.hip",
+           "kernels_expand.hip", "kernels_step_persistent.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -391,6 +391,7 @@ mla_status_t mla_device_errors(uint32_t *bits, void *stream) {
     if (e == hipSuccess) e = mla::take_errors_decode_mfma(bits);
     if (e == hipSuccess) e = mla::take_errors_decode8(bits);
     if (e == hipSuccess) e = mla::take_errors_decode128(bits);
+    if (e == hipSuccess) e = mla::take_errors_step_persistent(bits);
     return hip_status(e, "mla_device_errors");
 }
 
@@ -510,6 +511,40 @@ mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, 
     if (s != MLA_OK) return s;
     return run_step(p, q_nope, q_rope, c_kv, k_pe, kv_scale, block_table, seq_lens, W_UK, W_UV, out, lse_out, ws,
                     stream);
+}
+
+int64_t mla_decode_step_persistent_workspace(const mla_params_t *p) {
+    if (check(p) != MLA_OK || !mla::step_persistent_supported(*p)) return -1;
+    return mla::step_persistent_layout(*p).bytes;
+}
+
+mla_status_t mla_decode_step_persistent(const mla_params_t *p, const void *q_nope, const void *q_rope,
+                                        const void *c_kv, const void *k_pe, const int32_t *block_table,
+                                        const int32_t *seq_lens, const void *W_UK, const void *W_UV, void *out,
+                                        float *lse_out, void *workspace, int64_t workspace_bytes, void *stream) {
+    mla_status_t s = check_step(p, q_nope, c_kv, block_table, seq_lens, W_UK, W_UV, out,
+                                "mla_decode_step_persistent");
+    if (s != MLA_OK) return s;
+    if (!q_rope || !k_pe) return fail(MLA_ERR_NULL, "mla_decode_step_persistent: NULL q_rope or k_pe");
+    if (!mla::step_persistent_supported(*p))
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "mla_decode_step_persistent: needs Sq = 1, B <= 8, H a multiple of 32 up to 128, d_h = 128, "
+                    "d_c = 512, d_r = 64, bf16 q, weights, cache, RoPE keys and q_abs, bf16 or f32 out, "
+                    "max_pages <= %d",
+                    mla::kStepPersistentMaxPages);
+    if (!workspace) return fail(MLA_ERR_NULL, "mla_decode_step_persistent: NULL workspace");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(MLA_ERR_SHAPE, "mla_decode_step_persistent: workspace must be 256-byte aligned");
+    const int64_t need = mla::step_persistent_layout(*p).bytes;
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_SHAPE,
+                    "mla_decode_step_persistent: workspace of %lld bytes, need %lld "
+                    "(mla_decode_step_persistent_workspace)",
+                    (long long)workspace_bytes, (long long)need);
+    return hip_status(mla::launch_step_persistent(*p, q_nope, q_rope, c_kv, k_pe, block_table, seq_lens, W_UK, W_UV,
+                                                  out, lse_out, static_cast<char *>(workspace),
+                                                  static_cast<hipStream_t>(stream)),
+                      "mla_decode_step_persistent launch");
 }
 
 }  // extern "C"

@@ -82,6 +82,18 @@ hipError_t launch_decode128(const mla_params_t &p, const void *q_abs, const void
 // num_parts equal parts, so a part that also starts a sequence (one more segment:
 // its query loads, its first copies and its partial output) streams fewer pages.
 constexpr int kSeqStartCost = 6;
+// the whole step of a small batch in one cooperative launch (kernels_step_persistent.hip)
+constexpr int kStepPersistentMaxPages = 4096;          // merge weights of one sequence in LDS
+struct StepPersistentLayout {
+    int64_t q_abs, lse_part, o_part, bytes;             // byte offsets in the workspace; counters at 0
+};
+bool step_persistent_supported(const mla_params_t &p);
+StepPersistentLayout step_persistent_layout(const mla_params_t &p);
+hipError_t launch_step_persistent(const mla_params_t &p, const void *q_nope, const void *q_rope, const void *c_kv,
+                                  const void *k_pe, const int32_t *block_table, const int32_t *seq_lens,
+                                  const void *W_UK, const void *W_UV, void *out, float *lse_out, char *ws,
+                                  hipStream_t stream);
+hipError_t take_errors_step_persistent(uint32_t *bits);
 // each attention unit's device error word: OR it into *bits, then clear it
 hipError_t take_errors_generic(uint32_t *bits);
 hipError_t take_errors_decode_mfma(uint32_t *bits);

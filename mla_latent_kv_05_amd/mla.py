@@ -32,6 +32,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE"
 EXPORTS = ("mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_up_v", "mla_combine_up_v",
            "mla_append_kv", "mla_decompress_kv", "mla_prefill_attention", "mla_prefer_absorbed", "mla_prefill_lmax", "mla_expand_kv",
            "mla_decode_step", "mla_decode_step_workspace", "mla_decode_step_noalloc",
+           "mla_decode_step_persistent", "mla_decode_step_persistent_workspace",
            "mla_device_errors", "mla_debug_bounds",
            "mla_check_params", "mla_plan_splits", "mla_default_num_splits", "mla_decode_kernel_name",
            "mla_status_string", "mla_last_error", "mla_abi_version")
@@ -105,6 +106,7 @@ def _load(path):
         ("mla_prefill_attention", [PP, P, P, P, P, P, P, P, P, P]),
         ("mla_decode_step", [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]),
         ("mla_decode_step_noalloc", [PP, P, P, P, P, P, P, P, P, P, P, P, P]),
+        ("mla_decode_step_persistent", [PP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int64, P]),
         ("mla_check_params", [PP]),
         ("mla_plan_splits", [PP, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
     ):
@@ -125,6 +127,8 @@ def _load(path):
     L.mla_default_num_splits.restype = ctypes.c_int32
     L.mla_decode_step_workspace.argtypes = [PP]
     L.mla_decode_step_workspace.restype = ctypes.c_int64
+    L.mla_decode_step_persistent_workspace.argtypes = [PP]
+    L.mla_decode_step_persistent_workspace.restype = ctypes.c_int64
     L.mla_abi_version.argtypes = []
     L.mla_abi_version.restype = ctypes.c_int32
     L.mla_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), P]
@@ -565,3 +569,40 @@ class DecodeStep:
             combine_lse(p, self.o_part, self.lse_part, self.o_latent, self.lse, stream)
             up_v(p, self.o_latent, W_UV, self.out, stream)
         return self.out
+
+
+def decode_step_persistent_workspace(p: Params) -> int:
+    """Bytes of device workspace decode_step_persistent needs for p (raises for an
+    unsupported p)."""
+    r = lib().mla_decode_step_persistent_workspace(ctypes.byref(p))
+    if r < 0:
+        raise MLAError(6, "mla_decode_step_persistent does not support these parameters")
+    return int(r)
+
+
+def decode_step_persistent(p: Params, q_nope, q_rope, c_kv, k_pe, block_table, seq_lens, W_UK, W_UV, out,
+                           lse_out=None, workspace=None, stream=None) -> None:
+    """The decode step of a small batch in one launch.  `workspace`: a
+    uint8 GPU tensor of at least decode_step_persistent_workspace(p) bytes whose
+    first 256 bytes are zero before its first use (torch.zeros); each call leaves
+    them zero."""
+    rows = (p.B, p.Sq, p.H)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise ValueError("workspace: a uint8 GPU tensor is required")
+    _check(lib().mla_decode_step_persistent(
+        ctypes.byref(p),
+        _ptr(q_nope, "q_nope", rows + (p.d_h,), p.q_dtype),
+        _ptr(q_rope, "q_rope", rows + (p.d_r,), p.q_dtype),
+        _ptr(c_kv, "c_kv", (p.num_pages, PAGE, p.d_c), p.kv_dtype),
+        _ptr(k_pe, "k_pe", (p.num_pages, PAGE, p.d_r), p.pe_dtype),
+        _ptr(block_table, "block_table", (p.B, p.max_pages)),
+        _ptr(seq_lens, "seq_lens", (p.B,)),
+        _ptr(W_UK, "W_UK", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(W_UV, "W_UV", (p.H, p.d_h, p.d_c), p.w_dtype),
+        _ptr(out, "out", rows + (p.d_h,), p.out_dtype),
+        _ptr(lse_out, "lse_out", rows, F32),
+        _ptr(workspace, "workspace"),
+        ctypes.c_int64(workspace.numel()),
+        _stream(stream)))

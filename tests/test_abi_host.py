@@ -308,6 +308,43 @@ def test_decode_step_noalloc_rejects_large_steps_on_the_host():
     assert L.mla_decode_step_noalloc(ctypes.byref(v3()), None, *([d] * 9), None, None) == 1
 
 
+def test_persistent_step_workspace_and_support():
+    """Workspace of the one-launch step: 256 bytes of counters, then q_abs, the
+    page partials' lse values and the page partials (bf16), each 256-byte aligned;
+    -1 for parameters it does not support."""
+    def a(n):
+        return (n + 255) // 256 * 256
+    p = v3(B=3, Sq=1, max_pages=70, part_dtype=mla.BF16)
+    rows = 3 * 128
+    assert mla.decode_step_persistent_workspace(p) == 256 + a(rows * 512 * 2) + a(rows * 70 * 4) + a(rows * 70 * 512 * 2)
+    L = mla.lib()
+    for kw in ({"Sq": 2}, {"B": 9}, {"H": 48}, {"H": 256}, {"kv_dtype": mla.FP8_E4M3}, {"d_h": 64},
+               {"latent_dtype": mla.F32}, {"max_pages": 4097}):
+        q = v3(**{"B": 1, "Sq": 1, **kw})
+        assert L.mla_decode_step_persistent_workspace(ctypes.byref(q)) == -1, kw
+    for kw in ({"H": 32}, {"H": 96}, {"B": 8}, {"out_dtype": mla.F32}, {"max_pages": 4096}):
+        q = v3(**{"B": 1, "Sq": 1, **kw})
+        assert L.mla_decode_step_persistent_workspace(ctypes.byref(q)) > 0, kw
+
+
+def test_persistent_step_validates_on_the_host():
+    """Every argument error is returned before any HIP call (so this runs without
+    a GPU)."""
+    L = mla.lib()
+    d = ctypes.c_void_p(0x1000)
+    p = v3(B=1, Sq=1)
+    n = mla.decode_step_persistent_workspace(p)
+    args = [d] * 9                      # q_nope .. out (kv_scale is not an argument)
+    call = lambda q, *rest: L.mla_decode_step_persistent(ctypes.byref(q), *rest)
+    assert call(p, None, *args[1:], None, d, n, None) == 1            # NULL q_nope
+    assert call(p, d, None, *args[2:], None, d, n, None) == 1         # NULL q_rope
+    assert call(p, *args, None, None, n, None) == 1                   # NULL workspace
+    assert call(p, *args, None, ctypes.c_void_p(0x1008), n, None) == 2   # misaligned
+    assert call(p, *args, None, d, n - 1, None) == 2                  # too small
+    assert call(v3(B=1, Sq=2), *args, None, d, n, None) == 6          # unsupported
+    assert "Sq = 1" in L.mla_last_error().decode()
+
+
 def test_debug_build_and_error_word_entry_points():
     """Both libraries load with the same ABI; only libmla_debug.so has the device
     bounds checks; mla_device_errors rejects a NULL result pointer on the host."""
