@@ -214,8 +214,13 @@ __device__ __forceinline__ void absorb_item(const Args &a, int item) {
 // latent rows past the sequence's end are zeroed instead, so that the latent sum
 // meets only finite values (their weights are zero; a cache slot past the end may
 // hold anything)
-__device__ __forceinline__ void issue_page(const Args &a, uint32_t sm, int b, int j, int n_valid) {
-    const mla_params_t &p = a.p;
+struct PageSrc {
+    const uint16_t *c_kv, *k_pe;
+    const int32_t *block_table;
+};
+
+__device__ __forceinline__ void issue_page(const mla_params_t &p, const PageSrc &a, uint32_t sm, int b, int j,
+                                           int n_valid) {
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     n_valid = __builtin_amdgcn_readfirstlane(n_valid);
     const int64_t page = __builtin_amdgcn_readfirstlane(
@@ -242,7 +247,18 @@ __device__ __forceinline__ void issue_page(const Args &a, uint32_t sm, int b, in
     }
 }
 
-// q_abs is published; the page copy may still be in flight.
+// Where an attention item reads its query and writes its partial: split j of
+// head h of sequence b is row (b H + h) * split_stride + j of o_part (512 bf16)
+// and of lse_part.  kDev: device-scope stores (read by other workgroups of the
+// same launch), else plain stores.
+struct AttnIo {
+    const uint16_t *q_abs, *q_rope;
+    uint16_t *o_part;
+    float *lse_part;
+    int split_stride;
+};
+
+// q_abs is readable; the page copy may still be in flight.
 //   scores   wave w: head block hb = w % 2 (16 heads) and token half th = w / 2
 //            (32 tokens): S^T[token, head] = K Q^T, 18 steps of 32 dims (16
 //            latent, 2 RoPE), two 16-token blocks
@@ -250,8 +266,9 @@ __device__ __forceinline__ void issue_page(const Args &a, uint32_t sm, int b, in
 //            sums; the bf16 weights go to LDS as P[head][token]
 //   latent   wave w: latent columns 128 w .. 128 w + 127 of all 32 heads:
 //            O^T += V^T P^T, V^T by transposing reads, tokens in natural order
-__device__ __forceinline__ void attend_quarter(const Args &a, uint32_t sm, int b, int j, int n_valid, int hq) {
-    const mla_params_t &p = a.p;
+template <bool kDev>
+__device__ __forceinline__ void attend_quarter(const mla_params_t &p, const AttnIo &a, uint32_t sm, int b, int j,
+                                               int n_valid, int hq) {
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hb = w & 1, th = w >> 1;
     const int l16 = lane & 15, q4 = lane >> 4;            // 16x16 operand lane: row / column l16, k-group q4
@@ -368,7 +385,7 @@ __device__ __forceinline__ void attend_quarter(const Args &a, uint32_t sm, int b
     const int hbn = n >> 4, ln = n & 15;
     const float lw_tot = lds_load<float>(st + 512 + 4 * (16 * hbn + ln)) + lds_load<float>(st + 512 + 4 * (16 * (hbn + 2) + ln));
     const float inv = 1.f / lw_tot;
-    const int64_t prow = (static_cast<int64_t>(b) * p.H + h0 + n) * p.max_pages + j;
+    const int64_t prow = (static_cast<int64_t>(b) * p.H + h0 + n) * a.split_stride + j;
     uint16_t *dst = a.o_part + prow * dec::kDc + 128 * w;
     // lane (n, g) holds latent columns 32 cb + 8 k + 4 g .. + 3 (k = 0..3); lanes n and
     // n ^ 32 exchange halves so that each stores 16 contiguous bytes
@@ -389,12 +406,15 @@ __device__ __forceinline__ void attend_quarter(const Args &a, uint32_t sm, int b
                 v[t] = r[0];
                 v[2 + t] = r[1];
             }
-            store_dev_x4(dst + 32 * cb + 16 * pr + 8 * g, v);
+            if constexpr (kDev) store_dev_x4(dst + 32 * cb + 16 * pr + 8 * g, v);
+            else *reinterpret_cast<u32x4 *>(dst + 32 * cb + 16 * pr + 8 * g) = v;
         }
     if (w < 2 && q4 == 0) {                                    // head 16 w + l16: maximum and sum
         const float l_tot = ls + lds_load<float>(st + 256 + 4 * (16 * (w + 2) + l16));
-        const int64_t prow_h = (static_cast<int64_t>(b) * p.H + h0 + 16 * w + l16) * p.max_pages + j;
-        store_dev_f32(a.lse_part + prow_h, (m + __log2f(l_tot)) * dec::kLn2);
+        const int64_t prow_h = (static_cast<int64_t>(b) * p.H + h0 + 16 * w + l16) * a.split_stride + j;
+        const float lse = (m + __log2f(l_tot)) * dec::kLn2;
+        if constexpr (kDev) store_dev_f32(a.lse_part + prow_h, lse);
+        else a.lse_part[prow_h] = lse;
     }
 }
 
@@ -547,9 +567,9 @@ __global__ __launch_bounds__(kThreads, 2) void step_persistent_kernel(const Args
                 base += pages[bb];
             }
             const int nv = min(dec::kPage, a.seq_lens[b] - dec::kPage * j);
-            issue_page(a, sm, b, j, nv);
+            issue_page(p, PageSrc{a.c_kv, a.k_pe, a.block_table}, sm, b, j, nv);
             wait_count(&a.count[0], static_cast<uint32_t>(n_absorb));
-            attend_quarter(a, sm, b, j, nv, hq);
+            attend_quarter<true>(p, AttnIo{a.q_abs, a.q_rope, a.o_part, a.lse_part, p.max_pages}, sm, b, j, nv, hq);
             signal(&a.count[1]);
         }
     } else {
@@ -573,7 +593,61 @@ __global__ __launch_bounds__(kThreads, 2) void step_persistent_kernel(const Args
     }
 }
 
+// ---------------------------------------------------------------------------
+// mla_decode_splitkv with fixed splits of one page each (the plan of a small batch
+// of single new tokens): one workgroup per (sequence, page, quarter of 32 heads),
+// the attention item above with plain stores.  A split past the sequence's pages
+// gets lse = -inf.  The quarters of a page are consecutive-by-8 workgroups (one
+// compute die) and share the page through its L2.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void decode_page_kernel(const mla_params_t p, const uint16_t *__restrict__ q_abs,
+                                                                   const uint16_t *__restrict__ q_rope,
+                                                                   const uint16_t *__restrict__ c_kv,
+                                                                   const uint16_t *__restrict__ k_pe,
+                                                                   const int32_t *__restrict__ block_table,
+                                                                   const int32_t *__restrict__ seq_lens,
+                                                                   uint16_t *__restrict__ o_part,
+                                                                   float *__restrict__ lse_part) {
+    __shared__ __attribute__((aligned(1024))) char smem[kAttnSmem];
+    const int n_q = p.H / 32;
+    const int S = p.num_splits;
+    const int per_seq = (S + 7) / 8 * 8 * n_q;        // workgroups of one sequence
+    const int b = blockIdx.x / per_seq, i = blockIdx.x % per_seq;
+    const int r = i >> 3, hq = r % n_q;
+    const int j = (i & 7) + 8 * (r / n_q);            // the split (= page) of this workgroup
+    if (j >= S) return;
+    const int len = seq_lens[b];
+    const int pages = seq_pages(p, len);
+    if (j == 0 && hq == 0 && threadIdx.x == 0 && pages > S) raise_error(MLA_DEVERR_SPLITS);
+    if (j >= pages) {                                  // no page: an empty split
+        if (threadIdx.x < 32)
+            lse_part[(static_cast<int64_t>(b) * p.H + 32 * hq + threadIdx.x) * S + j] = -INFINITY;
+        return;
+    }
+    const uint32_t sm = lds_addr(smem);
+    const int nv = min(dec::kPage, len - dec::kPage * j);
+    issue_page(p, PageSrc{c_kv, k_pe, block_table}, sm, b, j, nv);
+    attend_quarter<false>(p, AttnIo{q_abs, q_rope, o_part, lse_part, S}, sm, b, j, nv, hq);
+}
+
 }  // namespace
+
+bool decode_page_supported(const mla_params_t &p) {
+    return p.Sq == 1 && p.H >= 32 && p.H % 32 == 0 && p.d_c == dec::kDc && p.d_r == dec::kDr &&
+           p.page_size == dec::kPage && p.q_dtype == MLA_BF16 && p.kv_dtype == MLA_BF16 && p.pe_dtype == MLA_BF16 &&
+           p.latent_dtype == MLA_BF16 && p.part_dtype == MLA_BF16;
+}
+
+hipError_t launch_decode_page(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
+                              const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
+                              float *lse_part, hipStream_t stream) {
+    const int64_t per_seq = (static_cast<int64_t>(p.num_splits) + 7) / 8 * 8 * (p.H / 32);
+    hipLaunchKernelGGL(decode_page_kernel, dim3(static_cast<unsigned>(p.B * per_seq)), dim3(kThreads), 0, stream, p,
+                       static_cast<const uint16_t *>(q_abs), static_cast<const uint16_t *>(q_rope),
+                       static_cast<const uint16_t *>(c_kv), static_cast<const uint16_t *>(k_pe), block_table, seq_lens,
+                       static_cast<uint16_t *>(o_part), lse_part);
+    return hipGetLastError();
+}
 
 bool step_persistent_supported(const mla_params_t &p) {
     return p.Sq == 1 && p.B >= 1 && p.B <= kMaxB && p.H >= 32 && p.H <= 128 && p.H % 32 == 0 && p.d_h == kDh &&

@@ -32,6 +32,13 @@ mla_status_t fail(mla_status_t s, const char *fmt, ...) {
 
 bool is_float_dtype(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
+// fixed splits of one page each, one new token, bf16 partials, no forced kernel:
+// the page kernel
+bool use_page_kernel(const mla_params_t &p) {
+    return !(p.flags & (MLA_FLAG_ROWS64 | MLA_FLAG_ROWS128 | MLA_FLAG_GENERIC)) && p.num_parts == 0 &&
+           p.split_pages == 1 && mla::decode_page_supported(p);
+}
+
 // new tokens per sequence: at most kMaxAbsorbedSq on the absorbed path, kMaxPrefill on
 // the non-absorbed one
 constexpr int kMaxAbsorbedSq = 256;
@@ -135,6 +142,7 @@ mla_status_t mla_check_params(const mla_params_t *p) { return check(p); }
 
 const char *mla_decode_kernel_name(const mla_params_t *p) {
     if (!p || check(p) != MLA_OK) return "invalid";
+    if (use_page_kernel(*p)) return "page_bf16";
     if (!mla::decode_mfma_supported(*p)) return "generic_f32";
     switch (mla::decode_kernel_for(*p)) {
     case mla::DecodeKernel::k128: return p->kv_dtype == MLA_FP8_E4M3 ? "mfma_fp8_128" : "mfma_bf16_128";
@@ -158,6 +166,22 @@ mla_status_t mla_plan_splits(mla_params_t *p, int32_t max_seq_len, int64_t total
     // (the 128-row kernel's workgroups when it applies: a plan that leaves it few
     // workgroups sends a bf16 launch to the 64-row kernel, with twice as many)
     const bool mfma = mla::decode_mfma_supported(*p);
+    // a small batch of single new tokens with bf16 partials: fixed splits of one page
+    // each, on the page kernel (one workgroup per page and 32 heads, all launched at
+    // once), when its workgroups stay within kPagePlanPerCu per compute unit
+    {
+        mla_params_t q = *p;
+        q.num_parts = 0;
+        q.split_pages = 1;
+        q.num_splits = (int32_t)std::min<int64_t>(max_pages_seq, kMaxSplits);
+        if (use_page_kernel(q) && max_pages_seq <= kMaxSplits &&
+            (int64_t)p->B * ((max_pages_seq + 7) / 8 * 8) * (p->H / 32) <= mla::kPagePlanPerCu * num_cus) {
+            p->num_parts = 0;
+            p->split_pages = 1;
+            p->num_splits = q.num_splits;
+            return MLA_OK;
+        }
+    }
     const int64_t rows = (int64_t)p->Sq * p->H;
     const int64_t wg_per_part =
         mfma ? std::max<int64_t>(1, rows / (mla::decode128_supported(*p) ? mla::kDecodeRowsPerGroup
@@ -241,6 +265,13 @@ mla_status_t mla_decode_splitkv(const mla_params_t *p, const void *q_abs, const 
     if (p->kv_dtype == MLA_FP8_E4M3 && !kv_scale)
         return fail(MLA_ERR_NULL, "mla_decode_splitkv: kv_scale is required for an FP8_E4M3 cache");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use_page_kernel(*p)) {
+        if ((int64_t)p->B * ((p->num_splits + 7) / 8 * 8) * (p->H / 32) > 0x7fffffffll)
+            return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: grid too large");
+        return hip_status(mla::launch_decode_page(*p, q_abs, q_rope, c_kv, k_pe, block_table, seq_lens, o_part,
+                                                  lse_part, st),
+                          "mla_decode_splitkv launch");
+    }
     const int64_t rows = (int64_t)p->B * p->Sq * p->H;
     const int64_t parts = p->num_parts > 0 ? p->num_parts : (int64_t)p->B * p->num_splits;
     const int64_t grid = mla::decode_mfma_supported(*p)

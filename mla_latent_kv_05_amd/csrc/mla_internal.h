@@ -99,10 +99,19 @@ hipError_t take_errors_generic(uint32_t *bits);
 hipError_t take_errors_decode_mfma(uint32_t *bits);
 hipError_t take_errors_decode8(uint32_t *bits);
 hipError_t take_errors_decode128(uint32_t *bits);
-// the attention kernel mla_decode_splitkv launches for p (MFMA path): the
+// the attention kernel mla_decode_splitkv launches for p on the MFMA path: the
 // four-wave 128-row kernel, else the eight-wave 64-row kernel (bf16), else the
-// four-wave 64-row kernel (e4m3)
+// four-wave 64-row kernel (e4m3).  Before that path: with fixed splits of one
+// page each, a single new token and bf16 partials, the page kernel (one
+// workgroup per page and 32 heads, kernels_step_persistent.hip).
 enum class DecodeKernel { k128, k8, kMfma64 };
+bool decode_page_supported(const mla_params_t &p);
+hipError_t launch_decode_page(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
+                              const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
+                              float *lse_part, hipStream_t stream);
+// Batches of single new tokens whose one-page plan has at most this many page
+// workgroups (pages x H / 32) per compute unit are planned with one-page splits.
+constexpr int64_t kPagePlanPerCu = 2;
 // Workgroups of the 128-row kernel at or below which a bf16 launch goes to the
 // eight-wave kernel: with at most one 128-row workgroup per two compute units, twice
 // as many 64-row workgroups (each loading half the query rows and storing half the

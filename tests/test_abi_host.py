@@ -185,6 +185,15 @@ def test_kernel_dispatch_names():
                            kv_dtype=mla.F32, pe_dtype=mla.F32, latent_dtype=mla.F32)
     assert mla.decode_kernel_name(tiny) == "generic_f32"
     assert mla.decode_kernel_name(v3(H=8)) == "generic_f32"       # 8 heads: not a multiple of 16
+    # fixed splits of one page, one new token, bf16 partials: the page kernel
+    page = dict(num_splits=4, split_pages=1, part_dtype=mla.BF16)
+    assert mla.decode_kernel_name(v3(**page)) == "page_bf16"
+    assert mla.decode_kernel_name(v3(H=32, **page)) == "page_bf16"
+    assert mla.decode_kernel_name(v3(flags=mla.FLAG_ROWS64, **page)) == "mfma_bf16_64"
+    assert mla.decode_kernel_name(v3(Sq=2, **page)) != "page_bf16"
+    assert mla.decode_kernel_name(v3(num_splits=4, split_pages=1)) != "page_bf16"    # fp32 partials
+    assert mla.decode_kernel_name(v3(num_splits=2, part_dtype=mla.BF16)) != "page_bf16"  # 2 pages per split
+    assert mla.decode_kernel_name(v3(kv_dtype=mla.FP8_E4M3, **page)) != "page_bf16"
 
 
 @pytest.mark.parametrize("B,lo,hi,Sq,min_splits,seed", [
@@ -359,12 +368,22 @@ def test_debug_build_and_error_word_entry_points():
 
 def test_planner_part_size_follows_partial_type():
     """Parts of at least 4 pages with fp32 partials, 2 with bf16 partials (one
-    sequence of 64 pages: 16 and 32 parts), except that a small bf16 batch on the
-    64-row kernel gets parts of one work unit (64 pages + the sequence's start cost
-    of 6 units: 70 parts, one page each), up to 128 parts."""
+    sequence of 64 pages: 16 and 32 parts).  A batch of single new tokens with bf16
+    partials whose one-page plan has at most 2 page workgroups (pages x H / 32) per
+    compute unit gets fixed splits of one page on the page kernel (B = 1 and 2 at
+    64 pages); else a small bf16 batch on the 64-row kernel gets parts of one work
+    unit (64 pages + the sequence's start cost of 6 units: 70 parts, one page each),
+    up to 128 parts."""
     p = mla.make_params(1, 1, 128, 128, 512, 64, num_pages=64, max_pages=64)
     assert mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1).num_parts == 16
     p.part_dtype = mla.BF16
+    q = mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1)
+    assert (q.num_parts, q.split_pages, q.num_splits, mla.decode_kernel_name(q)) == (0, 1, 64, "page_bf16")
+    p.B, p.num_pages = 2, 128
+    q = mla.plan_splits(p, 4096, 2 * 4096, num_cus=256, min_splits=1)
+    assert (q.num_parts, q.num_splits, mla.decode_kernel_name(q)) == (0, 64, "page_bf16")
+    p.B, p.num_pages = 1, 64
+    p.flags = mla.FLAG_ROWS64                               # forced: the balanced plan of the 64-row kernel
     q = mla.plan_splits(p, 4096, 4096, num_cus=256, min_splits=1)
     assert (q.num_parts, q.num_splits, mla.decode_kernel_name(q)) == (70, 64, "mfma_bf16_64")
     p.flags = mla.FLAG_ROWS128                              # the 128-row kernel: parts of 2 pages

@@ -126,3 +126,40 @@ def test_debug_build_flags_a_scale_that_is_no_power_of_two():
     o16, l16, err = decode(mla.lib(), qb, dc16, q_abs)
     assert err == 0
     assert torch.equal(o8, o16) and torch.equal(l8, l16)
+
+
+def test_page_kernel_errors():
+    """The page kernel (fixed one-page splits, bf16 partials): too few splits for the
+    block table are refused on the host (MLA_ERR_SPLITS, nothing launched), and the
+    debug build flags an out-of-range page and length and matches the release build
+    on valid input."""
+    lens = [700, 3]
+    wl = I.workload("v3_b64", B=len(lens))
+    case = I.make_case(wl, seq_lens=lens)
+    dc = DeviceCase(case)
+    q_abs = I.random_q_abs(wl, seed=8).cuda()
+    p = params_for(case, split_pages=1, part_dtype=mla.BF16)
+    note(f"page kernel errors kernel={mla.decode_kernel_name(p)} S={p.num_splits}")
+    assert mla.decode_kernel_name(p) == "page_bf16"
+    L, D = mla.lib(), mla.debug_lib()
+    mla.device_errors(L=L)
+    mla.device_errors(L=D)
+    o_r, l_r, err = decode(L, p, dc, q_abs)
+    assert err == 0
+    o_d, l_d, err = decode(D, p, dc, q_abs)
+    assert err == 0
+    assert torch.equal(o_d, o_r) and torch.equal(l_d, l_r)
+    q = p.copy()
+    q.num_splits = 2                                         # 700 positions need 11 one-page splits
+    o = torch.zeros((wl.B, 1, wl.H, 2, wl.d_c), device="cuda")
+    lse = torch.zeros((wl.B, 1, wl.H, 2), device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.mla_decode_splitkv(ctypes.byref(q), ptr(q_abs), ptr(dc.q_rope), ptr(dc.c_kv), ptr(dc.k_pe), None,
+                                ptr(dc.block_table), ptr(dc.seq_lens), ptr(o), ptr(lse), st) == 4   # MLA_ERR_SPLITS
+    bt = dc.block_table.clone()
+    bt[0, 3] = case.num_pages + 1000
+    assert decode(D, p, dc, q_abs, block_table=bt)[2] == PAGE
+    sl = dc.seq_lens.clone()
+    sl[1] = p.max_pages * 64 + 100
+    assert decode(D, p, dc, q_abs, seq_lens=sl)[2] & SEQLEN

@@ -96,10 +96,12 @@ def kernel_variants(wl, flags):
     return [flags]
 
 
-def check_partials(wl, o, l, ref_o, ref_l, key_gain=1.0):
+def check_partials(wl, o, l, ref_o, ref_l, key_gain=1.0, part_bf16=False):
     """lse bounds as for a whole step (see test_step_matches_oracle): 2e-3 for a bf16
     cache, 6e-3 for e4m3 (a second rounding of the key); key_gain is how much larger
-    than the generator's the keys may be, which scales both roundings' errors."""
+    than the generator's the keys may be, which scales both roundings' errors.  With
+    bf16 partials each element's own rounding (at most 2^-9 of its value; 2^-8
+    allowed) is taken off before the bound on o_part, as for a bf16 output."""
     empty = ref_l == -np.inf
     assert not np.isnan(l).any(), "an lse_part slot was left unwritten"
     assert np.array_equal(l == -np.inf, empty), "empty splits differ"
@@ -107,7 +109,11 @@ def check_partials(wl, o, l, ref_o, ref_l, key_gain=1.0):
     if full.any():
         lse_tol = {"f32": 1e-5, "fp8": 6e-3}.get(wl.dtype, 2e-3) * key_gain
         assert np.abs(l[full] - ref_l[full]).max() <= lse_tol
-        e = err_rms(o[full], ref_o[full])
+        if part_bf16:
+            d = np.maximum(np.abs(o[full].astype(np.float64) - ref_o[full]) - 2.0 ** -8 * np.abs(ref_o[full]), 0.0)
+            e = float(d.max()) / float(np.sqrt(np.mean(ref_o[full] ** 2)))
+        else:
+            e = err_rms(o[full], ref_o[full])
         note(f"  o_part err {e:.3e}")
         assert e <= tol_of(wl)
 
@@ -134,6 +140,28 @@ def test_decode_splitkv(wl_name, lens, split_pages, flags):
              f"kernel={mla.decode_kernel_name(p)}")
         o, l, *ref = run_decode(case, p, ref)
         check_partials(wl, o, l, *ref)
+
+
+@pytest.mark.parametrize("over,lens,extra", [
+    ({}, [1, 63, 64, 65, 200, 700], 0),
+    ({}, [0, 130, 1], 2),              # an empty sequence and spare split slots: lse -inf
+    ({"H": 32}, [77, 300], 0),
+    ({"H": 96}, [64, 129], 0),
+    ({}, [4096], 0),                   # the DeepSeek-V3 B = 1 length
+])
+def test_page_kernel(over, lens, extra):
+    """Fixed splits of one page with bf16 partials: the page kernel (one workgroup per
+    page and 32 heads) against the oracle's page partials; a split past a sequence's
+    pages reads lse = -inf."""
+    wl = I.workload("v3_b64", B=len(lens), **over)
+    case = I.make_case(wl, seq_lens=lens)
+    validate(case)
+    p = params_for(case, split_pages=1, part_dtype=mla.BF16)
+    p.num_splits += extra
+    note(f"page kernel {over} lens={lens} S={p.num_splits} kernel={mla.decode_kernel_name(p)}")
+    assert mla.decode_kernel_name(p) == "page_bf16"
+    o, l, ref_o, ref_l = run_decode(case, p)
+    check_partials(wl, o, l, ref_o, ref_l, part_bf16=True)
 
 
 @pytest.mark.parametrize("wl_name,lens,num_parts,extra_slots,flags", [
