@@ -36,6 +36,7 @@ Prints one JSON line.  value = latent-cache TB/s = (tokens x 1152 B) / step time
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -216,6 +217,39 @@ def main():
         diff = float((step_e.out - step.out).abs().max() / step.out.pow(2).mean().sqrt())
         assert diff <= 6e-2, f"expanded-cache route differs from the e4m3 route by {diff}"
 
+    # a small batch of single new tokens: also the single-launch step, for reference
+    # (not a headline route: slower on this GPU; equal within rounding, not bit for bit)
+    ms_single = None
+    L = mla.lib()
+    if L.mla_decode_step_persistent_workspace(ctypes.byref(p)) > 0:
+        nws = mla.decode_step_persistent_workspace(p)
+        ws1 = [torch.zeros(nws, dtype=torch.uint8, device=dev) for _ in reps]
+        out1 = torch.empty_like(step.out)
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        args1 = [(ctypes.byref(p), ptr(t["q_nope"]), ptr(t["q_rope"]), ptr(t["c_kv"]), ptr(t["k_pe"]),
+                  ptr(t["block_table"]), ptr(t["seq_lens"]), ptr(t["W_UK"]), ptr(t["W_UV"]), ptr(out1), None,
+                  ptr(ws1[r]), ctypes.c_int64(nws), ctypes.c_void_p(stream.cuda_stream)) for r, t in enumerate(reps)]
+        fn1 = L.mla_decode_step_persistent
+
+        def single(i):
+            st = fn1(*args1[i % args.replicas])
+            if st != 0:
+                raise mla.MLAError(st, L.mla_last_error().decode())
+
+        warm_runs["single_launch"] = warm(single)
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for i in range(args.steps):
+            single(i)
+        u1.record(stream)
+        torch.cuda.synchronize()
+        ms_single = u0.elapsed_time(u1) / args.steps
+        single(0)                                  # the replicas hold the same inputs
+        torch.cuda.synchronize()
+        diff = float((out1.float() - step_f.out.float()).abs().max() / step_f.out.float().pow(2).mean().sqrt())
+        assert diff <= 2e-2, f"single-launch step differs from the fused step by {diff}"
+        assert mla.device_errors() == 0, "single-launch step: device error word set"
+
     cost = A.step_cost(wl.B, wl.Sq, wl.H, wl.d_h, wl.d_c, wl.d_r, lens, fmt=wl.dtype, out_fmt="f32")
     ms_four = ms_step
     ms_step = min(ms_step, ms_fused)               # the headline step: the fastest route (same result)
@@ -327,6 +361,10 @@ def main():
                                       "us_per_step": round(ms_expand * 1e3, 2),
                                       "value": round(cost.cache_bytes / (ms_expand * 1e-3) / 1e12, 4)}}
                if ms_expand is not None else {}),
+            **({"single_launch": {"calls": "decode_step_persistent (one launch; reference, not a headline route)",
+                                  "us_per_step": round(ms_single * 1e3, 2),
+                                  "value": round(cost.cache_bytes / (ms_single * 1e-3) / 1e12, 4)}}
+               if ms_single is not None else {}),
         },
         "append": append,
         "prefill": prefill,
