@@ -153,18 +153,20 @@ __device__ __forceinline__ void wait_count(uint32_t *c, uint32_t target) {
 }
 
 // ---------------------------------------------------------------------------
-// absorb item (h, ch): q_abs[b, h, m] = sum_d q_nope[b, h, d] W_UK[h, d, m] for
-// m in [256 ch, 256 ch + 256), every b.  Wave w takes columns 256 ch + 64 w ..
-// + 63; lane l sums rows 16 (l / 8) .. + 15 of the 8 columns 8 (l % 8) .. + 7,
-// then the eight row groups are added across lanes (l ^ 32, l ^ 16, l ^ 8).
+// absorb item (h, ch): q_abs[r, h, m] = sum_d q_nope[r, h, d] W_UK[h, d, m] for
+// m in [256 ch, 256 ch + 256), every query row r < R (R <= 8).  Wave w takes
+// columns 256 ch + 64 w .. + 63; lane l sums rows 16 (l / 8) .. + 15 of the 8
+// columns 8 (l % 8) .. + 7 in fp32, then the eight row groups are added across
+// lanes (l ^ 32, l ^ 16, l ^ 8).  store(index, value) writes one q_abs element.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void absorb_item(const Args &a, int item) {
-    const mla_params_t &p = a.p;
+template <typename Store>
+__device__ __forceinline__ void absorb_rows(const mla_params_t &p, const uint16_t *__restrict__ q_nope,
+                                            const uint16_t *__restrict__ W_UK, int R, int item, Store &&store) {
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = item >> 1, ch = item & 1;
     const int rg = lane >> 3;
     const int col = 256 * ch + 64 * w + 8 * (lane & 7);
-    const uint16_t *wk = a.W_UK + (static_cast<int64_t>(h) * kDh + 16 * rg) * dec::kDc + col;
+    const uint16_t *wk = W_UK + (static_cast<int64_t>(h) * kDh + 16 * rg) * dec::kDc + col;
     u32x4 wv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) wv[r] = *reinterpret_cast<const u32x4 *>(wk + r * dec::kDc);
@@ -172,8 +174,8 @@ __device__ __forceinline__ void absorb_item(const Args &a, int item) {
     const int e_out = 4 * b5 + 2 * b4 + b3;           // the column this lane ends with
 #pragma unroll
     for (int b = 0; b < kMaxB; ++b) {
-        if (b >= p.B) break;
-        const uint16_t *qn = a.q_nope + (static_cast<int64_t>(b) * p.H + h) * kDh + 16 * rg;
+        if (b >= R) break;
+        const uint16_t *qn = q_nope + (static_cast<int64_t>(b) * p.H + h) * kDh + 16 * rg;
         const u32x4 q0 = *reinterpret_cast<const u32x4 *>(qn), q1 = *reinterpret_cast<const u32x4 *>(qn + 8);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -201,7 +203,7 @@ __device__ __forceinline__ void absorb_item(const Args &a, int item) {
         }
         const float send = b3 ? v2[0] : v2[1];
         const float v1 = (b3 ? v2[1] : v2[0]) + __shfl_xor(send, 8);
-        store_dev_u16(a.q_abs + (static_cast<int64_t>(b) * p.H + h) * dec::kDc + col + e_out, bf16_bits(v1));
+        store((static_cast<int64_t>(b) * p.H + h) * dec::kDc + col + e_out, v1);
     }
 }
 
@@ -546,7 +548,8 @@ __global__ __launch_bounds__(kThreads, 2) void step_persistent_kernel(const Args
     const int n_items = n_att * n_q;
 
     if (wg < n_absorb) {
-        absorb_item(a, wg);
+        absorb_rows(p, a.q_nope, a.W_UK, p.B, wg,
+                    [&](int64_t i, float v) { store_dev_u16(a.q_abs + i, bf16_bits(v)); });
         signal(&a.count[0]);
     } else if (wg < n_absorb + a.n_att_wg) {
         // attention item i: page (i % 8) + 8 ((i / 8) / n_q), pages counted in sequence
@@ -594,6 +597,20 @@ __global__ __launch_bounds__(kThreads, 2) void step_persistent_kernel(const Args
 }
 
 // ---------------------------------------------------------------------------
+// mla_absorb_q for at most 8 query rows (B * Sq <= 8) at the DeepSeek-V3 head
+// shapes: the absorb item above, one workgroup per (head, column half), every
+// weight load in flight at once; fp32 sums, one rounding to latent_dtype.
+// ---------------------------------------------------------------------------
+template <bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void absorb_rows_kernel(const mla_params_t p, const uint16_t *__restrict__ q_nope,
+                                                               const uint16_t *__restrict__ W_UK, void *__restrict__ q_abs) {
+    absorb_rows(p, q_nope, W_UK, p.B * p.Sq, blockIdx.x, [&](int64_t i, float v) {
+        if constexpr (kOutBf16) static_cast<uint16_t *>(q_abs)[i] = bf16_bits(v);
+        else static_cast<float *>(q_abs)[i] = v;
+    });
+}
+
+// ---------------------------------------------------------------------------
 // mla_decode_splitkv with fixed splits of one page each (the plan of a small batch
 // of single new tokens): one workgroup per (sequence, page, quarter of 32 heads),
 // the attention item above with plain stores.  A split past the sequence's pages
@@ -631,6 +648,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_page_kernel(const mla_para
 }
 
 }  // namespace
+
+bool absorb_rows_supported(const mla_params_t &p) {
+    return static_cast<int64_t>(p.B) * p.Sq <= kMaxB && p.d_h == kDh && p.d_c == dec::kDc && p.q_dtype == MLA_BF16 &&
+           p.w_dtype == MLA_BF16 && (p.latent_dtype == MLA_BF16 || p.latent_dtype == MLA_F32);
+}
+
+hipError_t launch_absorb_rows(const mla_params_t &p, const void *q_nope, const void *W_UK, void *q_abs,
+                              hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(2 * p.H));
+    const auto qn = static_cast<const uint16_t *>(q_nope);
+    const auto wk = static_cast<const uint16_t *>(W_UK);
+    if (p.latent_dtype == MLA_BF16)
+        hipLaunchKernelGGL((absorb_rows_kernel<true>), grid, dim3(kThreads), 0, stream, p, qn, wk, q_abs);
+    else
+        hipLaunchKernelGGL((absorb_rows_kernel<false>), grid, dim3(kThreads), 0, stream, p, qn, wk, q_abs);
+    return hipGetLastError();
+}
 
 bool decode_page_supported(const mla_params_t &p) {
     return p.Sq == 1 && p.H >= 32 && p.H % 32 == 0 && p.d_c == dec::kDc && p.d_r == dec::kDr &&

@@ -248,6 +248,8 @@ mla_status_t mla_absorb_q(const mla_params_t *p, const void *q_nope, const void 
     if (s != MLA_OK) return s;
     if (!q_nope || !W_UK || !q_abs) return fail(MLA_ERR_NULL, "mla_absorb_q: NULL tensor pointer");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!(p->flags & MLA_FLAG_GENERIC) && mla::absorb_rows_supported(*p))
+        return hip_status(mla::launch_absorb_rows(*p, q_nope, W_UK, q_abs, st), "mla_absorb_q launch");
     if (mla::absorb_mfma_supported(*p))
         return hip_status(mla::launch_absorb_mfma(*p, q_nope, W_UK, q_abs, st), "mla_absorb_q launch");
     return hip_status(mla::launch_absorb_generic(*p, q_nope, W_UK, q_abs, st), "mla_absorb_q launch");

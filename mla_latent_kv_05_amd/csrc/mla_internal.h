@@ -106,6 +106,11 @@ hipError_t take_errors_decode128(uint32_t *bits);
 // workgroup per page and 32 heads, kernels_step_persistent.hip).
 enum class DecodeKernel { k128, k8, kMfma64 };
 bool decode_page_supported(const mla_params_t &p);
+// mla_absorb_q for at most 8 query rows: one workgroup per head and column half,
+// fp32 VALU sums (kernels_step_persistent.hip)
+bool absorb_rows_supported(const mla_params_t &p);
+hipError_t launch_absorb_rows(const mla_params_t &p, const void *q_nope, const void *W_UK, void *q_abs,
+                              hipStream_t stream);
 hipError_t launch_decode_page(const mla_params_t &p, const void *q_abs, const void *q_rope, const void *c_kv,
                               const void *k_pe, const int32_t *block_table, const int32_t *seq_lens, void *o_part,
                               float *lse_part, hipStream_t stream);

@@ -46,7 +46,8 @@ def tol_of(wl):
 # ------------------------------------------------------------------ one entry point at a time
 
 @pytest.mark.parametrize("wl_name,R,flags", [
-    ("v3_b1", 1, 0), ("v3_b64", 64, 0), ("v3_b64", 70, 0), ("v3_sq4_fp8", 9, 0),
+    ("v3_b1", 1, 0), ("v3_b64", 3, 0), ("v3_b64", 8, 0),        # at most 8 rows: one workgroup per head half
+    ("v3_b64", 64, 0), ("v3_b64", 70, 0), ("v3_sq4_fp8", 9, 0),
     ("v3_b64", 70, mla.FLAG_GENERIC), ("tiny", 3, 0),
 ])
 def test_absorb_q(wl_name, R, flags):
@@ -66,6 +67,22 @@ def test_absorb_q(wl_name, R, flags):
     else:
         assert e <= TOL["bf16"]
         assert_bf16_rounding(qa.float().cpu().numpy(), ref)
+
+
+def test_absorb_q_small_batch_fp32_latent():
+    """At most 8 query rows with an fp32 q_abs: the fp32 sums themselves, against
+    the oracle in fp64 (bf16 inputs, 128 products per element)."""
+    wl = I.workload("v3_b64", B=5)
+    case = I.make_case(wl, seq_lens=[64] * wl.B)
+    p = params_for(case)
+    p.latent_dtype = mla.F32
+    note("absorb_q small batch, fp32 q_abs")
+    qa = torch.empty((wl.B, 1, wl.H, wl.d_c), dtype=torch.float32, device="cuda")
+    dc = DeviceCase(case)
+    mla.absorb_q(p, dc.q_nope, dc.W_UK, qa)
+    torch.cuda.synchronize()
+    ref = O.absorb_q(O.dims_of(case), case.q_nope, case.W_UK)
+    assert err_rms(qa.cpu().numpy(), ref) <= 1e-5
 
 
 def run_decode(case, p, ref=None):
