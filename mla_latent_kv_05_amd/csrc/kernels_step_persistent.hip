@@ -260,100 +260,118 @@ struct AttnIo {
     int split_stride;
 };
 
+// Scores of one half of the 576 dims for one head block (16 heads) over the page's
+// 64 tokens: S^T[token, head] = K Q^T in four 16-token blocks, 9 steps of 32 dims
+// (step ks = 9 KH + s: latent chunk group ks < 16, RoPE ks - 16).  The wave loads
+// only its half of the query rows, then waits for them and the page copy.
+template <int KH>
+__device__ __forceinline__ void score_half(const AttnIo &a, uint32_t sm, int64_t qrow, int lane, f32x4 (&sc)[4]) {
+    const int l16 = lane & 15, q4 = lane >> 4;            // 16x16 operand lane: row / column l16, k-group q4
+    // query operand (B): head row qrow, dims 32 ks + 8 q4 .. + 7
+    bf16x8 qreg[9];
+    {
+        const uint16_t *qa = a.q_abs + qrow * dec::kDc + 8 * q4;
+        const uint16_t *qr = a.q_rope + qrow * dec::kDr + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < 9; ++s) {
+            const int ks = 9 * KH + s;
+            qreg[s] = *reinterpret_cast<const bf16x8 *>(ks < 16 ? qa + 32 * ks : qr + 32 * (ks - 16));
+        }
+    }
+    wait_vmcnt<0>();                                      // the query rows and the page
+    __syncthreads();
+    // K operand (A): token row 16 tb + l16, logical chunk 4 ks + q4 (latent, ks = 4 m +
+    // k0: at kx[k0] + 256 m) or 4 (ks - 16) + q4 (RoPE); the swizzles depend on l16 only
+    const int sw = lat_swz(l16);
+    uint32_t kx[4], kp[2];
+#pragma unroll
+    for (int k0 = 0; k0 < 4; ++k0) kx[k0] = sm + l16 * dec::kCkvRow + (((4 * k0 + q4) ^ sw) << 4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) kp[k] = sm + kRopeOff + l16 * dec::kKpeRow + (((4 * k + q4) ^ rope_swz(l16)) << 4);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) sc[tb] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < 9; ++s) {
+        const int ks = 9 * KH + s;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const uint32_t addr = ks < 16 ? kx[ks & 3] + 256 * (ks >> 2) + tb * 16 * dec::kCkvRow
+                                          : kp[ks - 16] + tb * 16 * dec::kKpeRow;
+            sc[tb] = mfma16(as_bf16x8(dec::ld128(addr)), qreg[s], sc[tb]);
+        }
+    }
+}
+
 // q_abs is readable; the page copy may still be in flight.
-//   scores   wave w: head block hb = w % 2 (16 heads) and token half th = w / 2
-//            (32 tokens): S^T[token, head] = K Q^T, 18 steps of 32 dims (16
-//            latent, 2 RoPE), two 16-token blocks
-//   softmax  the two waves of a head block meet in LDS for the maximum and the
-//            sums; the bf16 weights go to LDS as P[head][token]
+//   scores   wave w: head block hb = w % 2 (16 heads) and half kh = w / 2 of the
+//            576 dims (kh = 0: latent 0 .. 287; kh = 1: latent 288 .. 511 and the
+//            RoPE key), all 64 tokens (score_half): each query element is loaded
+//            by one wave of the workgroup
+//   softmax  the kh = 1 wave of a head block passes its partial scores through LDS
+//            (the RoPE rows, dead once every score step is done); the kh = 0 wave
+//            adds them, takes the maximum, weights and sums over the page and writes
+//            the bf16 weights to LDS as P[head][token]
 //   latent   wave w: latent columns 128 w .. 128 w + 127 of all 32 heads:
 //            O^T += V^T P^T, V^T by transposing reads, tokens in natural order
 template <bool kDev>
 __device__ __forceinline__ void attend_quarter(const mla_params_t &p, const AttnIo &a, uint32_t sm, int b, int j,
                                                int n_valid, int hq) {
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hb = w & 1, th = w >> 1;
-    const int l16 = lane & 15, q4 = lane >> 4;            // 16x16 operand lane: row / column l16, k-group q4
+    const int hb = w & 1, kh = w >> 1;
+    const int l16 = lane & 15, q4 = lane >> 4;
     const int h0 = 32 * hq;                               // first head of the quarter
     const int64_t qrow = static_cast<int64_t>(b) * p.H + h0 + 16 * hb + l16;
-    // query operand (B): head 16 hb + l16, dims 32 ks + 8 q4 .. + 7
-    bf16x8 qreg[18];
-    {
-        const uint16_t *qa = a.q_abs + qrow * dec::kDc + 8 * q4;
-        const uint16_t *qr = a.q_rope + qrow * dec::kDr + 8 * q4;
+    f32x4 sc[4];
+    if (kh == 0) score_half<0>(a, sm, qrow, lane, sc);
+    else score_half<1>(a, sm, qrow, lane, sc);
+    // lane holds head 16 hb + l16, tokens 16 tb + 4 q4 + i (partial over its half)
+    __syncthreads();                                      // every score step is done: the RoPE rows are free
+    const uint32_t xs = sm + kRopeOff + hb * 4096 + 16 * lane;
+    if (kh == 1) {
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8 *>(qa + 32 * ks);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qreg[16 + ks] = *reinterpret_cast<const bf16x8 *>(qr + 32 * ks);
+        for (int tb = 0; tb < 4; ++tb) lds_store<f32x4>(xs + 1024 * tb, sc[tb]);
     }
-    wait_vmcnt<0>();                                      // the query rows and the page
     __syncthreads();
-    // K operand (A): token row 32 th + 16 tb + l16, logical chunk 4 ks + q4 (latent,
-    // ks = 4 m + k0: at kx[k0] + 256 m) or 4 (ks - 16) + q4 (RoPE); the swizzles
-    // depend on l16 only
-    const int r0 = 32 * th + l16;
-    const int sw = lat_swz(l16);
-    uint32_t kx[4], kp[2];
-#pragma unroll
-    for (int k0 = 0; k0 < 4; ++k0) kx[k0] = sm + r0 * dec::kCkvRow + (((4 * k0 + q4) ^ sw) << 4);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) kp[k] = sm + kRopeOff + r0 * dec::kKpeRow + (((4 * k + q4) ^ rope_swz(l16)) << 4);
-    f32x4 sc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const uint32_t addr = ks < 16 ? kx[ks & 3] + 256 * (ks >> 2) + tb * 16 * dec::kCkvRow
-                                          : kp[ks - 16] + tb * 16 * dec::kKpeRow;
-            sc[tb] = mfma16(as_bf16x8(dec::ld128(addr)), qreg[ks], sc[tb]);
-        }
-    }
-    // softmax: lane holds head 16 hb + l16, tokens 32 th + 16 tb + 4 q4 + i
-    const float zs = p.scale * dec::kLog2e;
-    float z[2][4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 32 * th + 16 * tb + 4 * q4 + i;
-            z[tb][i] = tok < n_valid ? sc[tb][i] * zs : -INFINITY;
-            m = fmaxf(m, z[tb][i]);
-        }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    // stats: [0, 256) maxima, [256, 512) sums, [512, 768) sums of the rounded weights,
-    // per wave x 16 heads
+    // stats: [512, 768) the sums of the rounded weights per head of the quarter
     const uint32_t st = sm + kStatOff;
-    if (q4 == 0) lds_store<float>(st + 4 * (16 * w + l16), m);
-    __syncthreads();
-    m = fmaxf(m, lds_load<float>(st + 4 * (16 * (w ^ 2) + l16)));   // with the head's other token half
-    // (finite: the page has a valid position, in its first half)
-    float ls = 0.f, lw = 0.f;
-    uint32_t pk[2][2];
+    float m = -INFINITY, ls = 0.f;
+    if (kh == 0) {
+        const float zs = p.scale * dec::kLog2e;
+        float z[4][4];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
+            const f32x4 o1 = lds_load<f32x4>(xs + 1024 * tb);
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-            const float p0 = exp2f(z[tb][i] - m), p1 = exp2f(z[tb][i + 1] - m);
-            ls += p0 + p1;
-            const uint32_t u = cvt_pk_bf16(p0, p1);
-            lw += bf_lo(u) + bf_hi(u);
-            pk[tb][i >> 1] = u;
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * tb + 4 * q4 + i;
+                z[tb][i] = tok < n_valid ? (sc[tb][i] + o1[i]) * zs : -INFINITY;
+                m = fmaxf(m, z[tb][i]);
+            }
         }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));                  // finite: position 0 of the page is valid
+        float lw = 0.f;
+        uint32_t pk[4][2];
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-        ls += __shfl_xor(ls, o);
-        lw += __shfl_xor(lw, o);
-    }
-    if (q4 == 0) {
-        lds_store<float>(st + 256 + 4 * (16 * w + l16), ls);
-        lds_store<float>(st + 512 + 4 * (16 * w + l16), lw);
-    }
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-        lds_store<u32x2>(sm + kPOff + (16 * hb + l16) * kPRow + 2 * (32 * th + 16 * tb + 4 * q4),
-                         u32x2{pk[tb][0], pk[tb][1]});
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = exp2f(z[tb][i] - m), p1 = exp2f(z[tb][i + 1] - m);
+                ls += p0 + p1;
+                const uint32_t u = cvt_pk_bf16(p0, p1);
+                lw += bf_lo(u) + bf_hi(u);
+                pk[tb][i >> 1] = u;
+            }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+            ls += __shfl_xor(ls, o);
+            lw += __shfl_xor(lw, o);
+        }
+        if (q4 == 0) lds_store<float>(st + 512 + 4 * (16 * hb + l16), lw);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+            lds_store<u32x2>(sm + kPOff + (16 * hb + l16) * kPRow + 2 * (16 * tb + 4 * q4), u32x2{pk[tb][0], pk[tb][1]});
+    }
     __syncthreads();
     // latent sum: lane (n, g): head n of the quarter, k = 8 g + e <-> token 16 kk + 8 g
     // + e.  Transposing read hl of lane (q16, i16): row 16 kk + 8 g + 4 hl + i16 / 4,
@@ -383,9 +401,9 @@ __device__ __forceinline__ void attend_quarter(const mla_params_t &p, const Attn
             o[cb] = mfma32(av, bw, o[cb]);
         }
     }
-    // head n's totals (its head block's two token halves)
+    // head n's total of its rounded weights
     const int hbn = n >> 4, ln = n & 15;
-    const float lw_tot = lds_load<float>(st + 512 + 4 * (16 * hbn + ln)) + lds_load<float>(st + 512 + 4 * (16 * (hbn + 2) + ln));
+    const float lw_tot = lds_load<float>(st + 512 + 4 * (16 * hbn + ln));
     const float inv = 1.f / lw_tot;
     const int64_t prow = (static_cast<int64_t>(b) * p.H + h0 + n) * a.split_stride + j;
     uint16_t *dst = a.o_part + prow * dec::kDc + 128 * w;
@@ -411,8 +429,8 @@ __device__ __forceinline__ void attend_quarter(const mla_params_t &p, const Attn
             if constexpr (kDev) store_dev_x4(dst + 32 * cb + 16 * pr + 8 * g, v);
             else *reinterpret_cast<u32x4 *>(dst + 32 * cb + 16 * pr + 8 * g) = v;
         }
-    if (w < 2 && q4 == 0) {                                    // head 16 w + l16: maximum and sum
-        const float l_tot = ls + lds_load<float>(st + 256 + 4 * (16 * (w + 2) + l16));
+    if (kh == 0 && q4 == 0) {                                  // head 16 w + l16: maximum and sum
+        const float l_tot = ls;
         const int64_t prow_h = (static_cast<int64_t>(b) * p.H + h0 + 16 * w + l16) * a.split_stride + j;
         const float lse = (m + __log2f(l_tot)) * dec::kLn2;
         if constexpr (kDev) store_dev_f32(a.lse_part + prow_h, lse);
