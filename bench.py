@@ -217,11 +217,14 @@ def main():
         diff = float((step_e.out - step.out).abs().max() / step.out.pow(2).mean().sqrt())
         assert diff <= 6e-2, f"expanded-cache route differs from the e4m3 route by {diff}"
 
-    # a small batch of single new tokens: also the single-launch step, for reference
-    # (not a headline route: slower on this GPU; equal within rounding, not bit for bit)
+    # a small batch of single new tokens at a short context (where the planner itself
+    # takes one-page splits): also the single-launch step, for reference (not a
+    # headline route: slower on this GPU; equal within rounding, not bit for bit).  Its
+    # attention items are single pages, so at long contexts it is not a route at all.
     ms_single = None
     L = mla.lib()
-    if L.mla_decode_step_persistent_workspace(ctypes.byref(p)) > 0:
+    if (L.mla_decode_step_persistent_workspace(ctypes.byref(p)) > 0
+            and L.mla_decode_kernel_name(ctypes.byref(p)) == b"page_bf16"):
         nws = mla.decode_step_persistent_workspace(p)
         ws1 = [torch.zeros(nws, dtype=torch.uint8, device=dev) for _ in reps]
         out1 = torch.empty_like(step.out)

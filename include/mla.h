@@ -315,7 +315,10 @@ mla_status_t mla_decode_step_noalloc(const mla_params_t *p, const void *q_nope, 
  * part_dtype = BF16.  num_splits, split_pages, num_parts, part_dtype and the flags
  * are ignored.  On an MI355X this one launch is slower than mla_decode_step's
  * three (the waits between its roles cross the compute dies' L2 caches); it is
- * for callers that want a single launch.
+ * for callers that want a single launch.  It suits short contexts only.  Every
+ * page is one attention workgroup and one partial per head, so the work grows
+ * with the pages: 4 sequences of 131,072 positions take about 4.9 ms, against
+ * 0.18 ms for mla_decode_step.
  *
  * Supported (else MLA_ERR_UNSUPPORTED): Sq = 1, 1 <= B <= 8, H a multiple of 32
  * up to 128, d_h = 128, d_c = 512, d_r = 64, q_dtype = w_dtype = kv_dtype =
